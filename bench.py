@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Throughput of the 3-D max-pooling path on one MI355X.
+
+One step runs the whole path once over the five named synthetic workloads:
+the forward (window max + int32 argmax) of all five, then the backward of
+the four that have one, each through the C ABI on the current stream:
+
+  adaptive_f32_divisible  float32 (2,3,8,8,8) -> (4,4,4)      fwd + gather bwd
+  adaptive_bf16_ties      bfloat16 (4,16,10,10,10) -> (8,8,8) fwd + accumulate bwd
+  fixed_bf16_k2s2         bfloat16 (16,64,16,112,112) k2 s2   fwd only
+  fixed_f16_k3s2          float16 (8,128,32,56,56) k3 s2      fwd + accumulate bwd
+  adaptive_f32_large      float32 (32,256,16,32,32) -> (5,7,7) fwd + accumulate bwd
+
+Inputs (x, grad_output) are drawn once on the CPU from fixed seeds and are
+resident in HBM before timing; outputs are preallocated.  The metric is
+effective HBM bandwidth: algorithmic bytes (every input read once, every
+output written once: |x|+|y|+|idx| forward, |gy|+|idx|+|gx| backward) per
+second, over the whole step, and as a fraction of the 8 TB/s peak.
+
+Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one
+GPU (planes shard across GPUs with no communication, so more GPUs are not
+measured here).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0
+METRIC = "effective HBM GB/s (bytes read+written / time) fwd+bwd; % of MI355X HBM peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; stored traffic counters are reported only
+    while it matches the hash they were measured at."""
+    from bwd_max_pool3d_amd import _build
+    h = hashlib.sha256()
+    for path in _build.sources() + [os.path.join(_build.CSRC, f) for f in
+                                    ("geometry.hpp", "dtype.hpp", "kernels.hpp")]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Op:
+    """One C-ABI call of the step, with its inputs and preallocated outputs."""
+
+    def __init__(self, wl, kind, fn, nbytes, elems, note):
+        self.wl, self.kind, self.fn, self.nbytes, self.elems, self.note = (
+            wl, kind, fn, nbytes, elems, note)
+        self.ms = []
+
+    @property
+    def name(self):
+        return "%s.%s" % (self.wl.name, self.kind)
+
+
+def build_ops(torch, mp, workloads):
+    fwd_ops, bwd_ops = [], []
+    for wl in workloads.WORKLOADS:
+        x = wl.make_x().cuda()
+        N, C, D, H, W = wl.shape
+        if wl.adaptive:
+            o3 = tuple(wl.out)
+        else:
+            o3 = tuple(mp.mp3d_out_size(X, k, s) for X, k, s in zip(wl.shape[2:], wl.kernel, wl.stride))
+        oshape = (N, C) + o3
+        y = torch.empty(oshape, dtype=x.dtype, device="cuda")
+        idx = torch.empty(oshape, dtype=torch.int32, device="cuda")
+        es = x.element_size()
+        nin, nout = x.numel(), y.numel()
+        fbytes = nin * es + nout * es + nout * 4
+        if wl.adaptive:
+            f = (lambda x=x, o3=o3, y=y, idx=idx: mp.amp3d_forward(x, o3, out=(y, idx)))
+        else:
+            f = (lambda x=x, wl=wl, y=y, idx=idx: mp.mp3d_forward(x, wl.kernel, wl.stride, out=(y, idx)))
+        fwd_ops.append(Op(wl, "fwd", f, fbytes, nin, "forward"))
+        if wl.backward:
+            gy = wl.make_gy(oshape).cuda()
+            gx = torch.empty(wl.shape, dtype=x.dtype, device="cuda")
+            bbytes = nout * es + nout * 4 + nin * es
+            b = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
+                gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, out=gx))
+            bwd_ops.append(Op(wl, "bwd", b, bbytes, nin, "backward"))
+    return fwd_ops + bwd_ops
+
+
+def cpu_baseline(target_s: float):
+    """The CPU oracle, single-threaded, on the same fraction of every
+    workload's planes (so the byte mix matches the GPU step), sized to
+    about ``target_s`` seconds."""
+    import numpy as np
+    import torch
+    import oracle
+    from bwd_max_pool3d_amd import workloads
+
+    orc = oracle.get()
+    code = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+    def storage(t):
+        t = t.contiguous()
+        if t.dtype == torch.float32:
+            return t.numpy()
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    cache = {}
+
+    def draw(wl, kind, shape=None):
+        if (wl.name, kind) not in cache:
+            cache[(wl.name, kind)] = wl.make_x() if kind == "x" else wl.make_gy(shape)
+        return cache[(wl.name, kind)]
+
+    def run(frac):
+        total_bytes = 0
+        elapsed = 0.0
+        planes_used = []
+        for wl in workloads.WORKLOADS:
+            N, C, D, H, W = wl.shape
+            P = N * C
+            np_ = max(1, int(round(P * frac)))
+            planes_used.append("%s:%d/%d" % (wl.name, np_, P))
+            x = draw(wl, "x").reshape(P, 1, D, H, W)[:np_].contiguous()
+            c = code[x.dtype]
+            if wl.adaptive:
+                o3, k, s = tuple(wl.out), (0, 0, 0), (0, 0, 0)
+            else:
+                k, s = wl.kernel, wl.stride
+                o3 = tuple(orc.fixed_out(X, ka, sa) for X, ka, sa in zip(wl.shape[2:], k, s))
+            es = x.element_size()
+            xs = storage(x)
+            t0 = time.perf_counter()
+            y, idx = orc.forward(xs, c, o3, k, s)
+            elapsed += time.perf_counter() - t0
+            nin, nout = xs.size, y.size
+            total_bytes += nin * es + nout * (es + 4)
+            if wl.backward:
+                gy = draw(wl, "gy", (P, 1) + o3)[:np_].contiguous()
+                gys = storage(gy)
+                t0 = time.perf_counter()
+                orc.backward(gys, idx, c, (np_, 1, D, H, W), side=False)
+                elapsed += time.perf_counter() - t0
+                total_bytes += nout * (es + 4) + nin * es
+        return total_bytes, elapsed, planes_used
+
+    probe = 1.0 / 512
+    b, t, _ = run(probe)
+    frac = min(1.0, probe * target_s / max(t, 1e-3))
+    b, t, used = run(frac)
+    return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "plain C oracle, one thread, forward+backward on %.4f of each "
+                      "workload's planes (%s): %.3g GB of algorithmic bytes in %.1f s"
+                      % (frac, ", ".join(used), b / 1e9, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU-oracle sample size in seconds (0 skips the leg)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the step, run a plain 1 GiB device copy 10 times "
+                         "(reference kernel for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this path runs on one GPU; --gpus %d is not supported "
+              "(planes shard across GPUs with no communication)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bwd_max_pool3d_amd as mp
+    from bwd_max_pool3d_amd import workloads
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": a.numel() * 4, "launches": 10}))
+        return
+
+    print("[bench] building inputs", file=sys.stderr, flush=True)
+    ops = build_ops(torch, mp, workloads)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for op in ops:
+            op.fn()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in ops] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for step in range(args.steps):
+        for op, (e0, e1) in zip(ops, evs[step]):
+            e0.record(stream)
+            op.fn()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for step in range(args.steps):
+        for op, (e0, e1) in zip(ops, evs[step]):
+            op.ms.append(e0.elapsed_time(e1))
+    print("[bench] timed %d steps" % args.steps, file=sys.stderr, flush=True)
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    step_bytes = sum(op.nbytes for op in ops)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    per_op = []
+    for op in ops:
+        avg = sum(op.ms) / len(op.ms)
+        per_op.append({"op": op.name, "ms": round(avg, 5), "bytes": op.nbytes,
+                       "GB_s": round(op.nbytes / (avg * 1e-3) / 1e9, 1),
+                       "elems_per_s": round(op.elems / (avg * 1e-3), 1),
+                       "frac_of_peak": round(op.nbytes / (avg * 1e-3) / 1e9 / PEAK_GBS, 4)})
+    dom = max(per_op, key=lambda r: r["ms"])
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == kernel_source_hash() and dom["op"] in tr.get("ops", {}):
+            traffic = tr["ops"][dom["op"]]["hbm_bytes"]
+    roofline = {"bound": "hbm", "achieved": dom["GB_s"], "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["GB_s"] / PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom["op"], "algorithmic_bytes": dom["bytes"], "avg_ms": dom["ms"]}
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "five 3-D max-pool workloads per step: forward of all five, "
+                               "backward of the four with one (adaptive f32 2x3x8^3->4^3; "
+                               "adaptive bf16 4x16x10^3->8^3; fixed bf16 16x64x16x112x112 "
+                               "k2s2 fwd only; fixed f16 8x128x32x56x56 k3s2; adaptive f32 "
+                               "32x256x16x32x32->5x7x7)",
+                   "step_bytes": step_bytes, "storage_dtypes": "f32, bf16, f16; idx int32",
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "roofline": roofline,
+        "per_op": per_op,
+    }
+    if args.cpu_seconds > 0:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+"""3-D max pooling over NCDHW tensors on AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of libmp3d.so (include/mp3d.h), with the same
+names.  PyTorch supplies device memory and the current stream; every step
+of the computation runs in the library's HIP kernels.  There is no CPU or
+PyTorch fallback: if the library is missing every call raises ImportError.
+
+  mp3d_forward(x, kernel, stride) -> (y, idx)        fixed windows, no padding
+  amp3d_forward(x, out_size) -> (y, idx)             adaptive windows
+  mp3d_backward(gy, idx, in_shape, kernel=None, stride=None, overlap=-1) -> gx
+  mp3d_out_size(X, k, s) -> int
+
+x, y, gy and gx are float32, float16 or bfloat16; idx is int32, flat within
+each D*H*W plane.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import Mp3dError  # noqa: F401
+
+__all__ = ["mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size", "Mp3dError"]
+
+_DTYPE = {torch.float32: _lib.MP3D_F32, torch.float16: _lib.MP3D_F16,
+          torch.bfloat16: _lib.MP3D_BF16}
+
+
+def _triple(v) -> tuple[int, int, int]:
+    if isinstance(v, int):
+        return (v, v, v)
+    v = tuple(int(a) for a in v)
+    if len(v) != 3:
+        raise ValueError("expected 3 values, got %r" % (v,))
+    return v
+
+
+def _code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError("unsupported dtype %s" % t.dtype) from None
+
+
+def _check_tensor(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous NCDHW" % name)
+    if t.dim() != 5:
+        raise ValueError("%s must be 5-D (N, C, D, H, W)" % name)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def mp3d_out_size(X: int, k: int, s: int) -> int:
+    """(X - k) // s + 1, as the library computes it."""
+    out = ctypes.c_int64()
+    _lib.check(_lib.load().mp3d_out_size(X, k, s, ctypes.byref(out)))
+    return out.value
+
+
+def _outputs(x: torch.Tensor, shape, out):
+    if out is None:
+        return (torch.empty(shape, dtype=x.dtype, device=x.device),
+                torch.empty(shape, dtype=torch.int32, device=x.device))
+    y, idx = out
+    _check_tensor(y, "y")
+    _check_tensor(idx, "idx")
+    if (tuple(y.shape) != shape or tuple(idx.shape) != shape or y.dtype != x.dtype
+            or idx.dtype != torch.int32):
+        raise ValueError("out must be (y, idx) of shape %s, dtypes (%s, int32)" % (shape, x.dtype))
+    return y, idx
+
+
+def mp3d_forward(x: torch.Tensor, kernel, stride=None, out=None):
+    """Fixed-window forward: returns (y, idx).  ``out`` may supply a
+    preallocated (y, idx) pair."""
+    lib = _lib.load()
+    _check_tensor(x, "x")
+    k = _triple(kernel)
+    s = _triple(stride if stride is not None else kernel)
+    N, C, D, H, W = x.shape
+    o = tuple(mp3d_out_size(X, ka, sa) for X, ka, sa in zip((D, H, W), k, s))
+    y, idx = _outputs(x, (N, C) + o, out)
+    _lib.check(lib.mp3d_forward(x.data_ptr(), y.data_ptr(), idx.data_ptr(), _code(x),
+                                N, C, D, H, W, *k, *s, _stream(x)))
+    return y, idx
+
+
+def amp3d_forward(x: torch.Tensor, out_size, out=None):
+    """Adaptive-window forward: returns (y, idx).  ``out`` may supply a
+    preallocated (y, idx) pair."""
+    lib = _lib.load()
+    _check_tensor(x, "x")
+    o = _triple(out_size)
+    N, C, D, H, W = x.shape
+    y, idx = _outputs(x, (N, C) + o, out)
+    _lib.check(lib.amp3d_forward(x.data_ptr(), y.data_ptr(), idx.data_ptr(), _code(x),
+                                 N, C, D, H, W, *o, _stream(x)))
+    return y, idx
+
+
+def mp3d_backward(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel=None,
+                  stride=None, overlap: int = -1, out: torch.Tensor | None = None):
+    """Backward: gx of shape ``in_shape``.  ``kernel``/``stride`` None means
+    adaptive windows; ``overlap`` -1 lets the library pick the gather path
+    when the windows tile every axis, 0 forces it, 1 forces accumulation.
+    ``out`` may supply a preallocated gx."""
+    lib = _lib.load()
+    _check_tensor(gy, "gy")
+    _check_tensor(idx, "idx")
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    if idx.shape != gy.shape or idx.device != gy.device:
+        raise ValueError("idx and gy must have the same shape and device")
+    N, C, D, H, W = (int(v) for v in in_shape)
+    if gy.shape[:2] != (N, C):
+        raise ValueError("gy's N, C do not match in_shape")
+    if kernel is None:
+        k = s = (0, 0, 0)
+    else:
+        k = _triple(kernel)
+        s = _triple(stride if stride is not None else kernel)
+    if out is None:
+        out = torch.empty((N, C, D, H, W), dtype=gy.dtype, device=gy.device)
+    else:
+        _check_tensor(out, "out")
+        if out.shape != (N, C, D, H, W) or out.dtype != gy.dtype:
+            raise ValueError("out must be a %s tensor of shape %s" % (gy.dtype, (N, C, D, H, W)))
+    od, oh, ow = gy.shape[2:]
+    _lib.check(lib.mp3d_backward(gy.data_ptr(), idx.data_ptr(), out.data_ptr(), _code(gy),
+                                 N, C, D, H, W, od, oh, ow, *k, *s, int(overlap), _stream(gy)))
+    return out

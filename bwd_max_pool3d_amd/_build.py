@@ -1,0 +1,38 @@
+"""Build libmp3d.so (the HIP kernels and the C ABI) in-tree for gfx950."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIBRARY = os.path.join(HERE, "libmp3d.so")
+SOURCES = ["api.hip", "plan.hip", "forward.hip", "backward.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Wall", "-Wno-unused-result",
+    # keep IEEE subnormals and exact rounding: no fast-math, no FTZ
+    "-fno-fast-math", "-ffp-contract=off",
+    # no packed-FP32 instructions in the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def sources() -> list[str]:
+    return [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build(out: str = LIBRARY, verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *sources()]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,61 @@
+"""ctypes view of libmp3d.so (declared in include/mp3d.h).
+
+Loading fails loudly: there is no fallback implementation anywhere in this
+package, so a missing or unloadable library is an ImportError for every op.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libmp3d.so")
+
+MP3D_OK, MP3D_EINVAL, MP3D_EDTYPE, MP3D_ENOTDIV, MP3D_EOVERFLOW, MP3D_EHIP = range(6)
+MP3D_F32, MP3D_F16, MP3D_BF16 = 0, 1, 2
+
+EXPORTS = ("mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
+           "mp3d_strerror", "mp3d_last_error")
+
+_i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+_lib = None
+
+
+class Mp3dError(RuntimeError):
+    """A libmp3d call returned a non-zero status."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__("%s (status %d)" % (message, code))
+        self.code = code
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """The loaded library (cached).  Raises ImportError if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            "libmp3d.so is not built at %s; run `python -m bwd_max_pool3d_amd._build` "
+            "(or __graft_entry__.build()) first" % path)
+    lib = ctypes.CDLL(path)
+    lib.mp3d_forward.argtypes = [_vp, _vp, _vp, ctypes.c_int] + [_i64] * 5 + [_i32] * 6 + [_vp]
+    lib.amp3d_forward.argtypes = [_vp, _vp, _vp, ctypes.c_int] + [_i64] * 5 + [_i32] * 3 + [_vp]
+    lib.mp3d_backward.argtypes = ([_vp, _vp, _vp, ctypes.c_int] + [_i64] * 5 + [_i32] * 9
+                                  + [ctypes.c_int, _vp])
+    lib.mp3d_out_size.argtypes = [_i64, _i32, _i32, ctypes.POINTER(_i64)]
+    lib.mp3d_strerror.argtypes = [ctypes.c_int]
+    lib.mp3d_strerror.restype = ctypes.c_char_p
+    lib.mp3d_last_error.argtypes = []
+    lib.mp3d_last_error.restype = ctypes.c_char_p
+    for name in ("mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def check(code: int) -> None:
+    if code != MP3D_OK:
+        lib = load()
+        msg = lib.mp3d_last_error().decode() or lib.mp3d_strerror(code).decode()
+        raise Mp3dError(code, msg)

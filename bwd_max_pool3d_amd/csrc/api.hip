@@ -1,0 +1,272 @@
+// api.hip -- the C ABI declared in include/mp3d.h: argument checks, the
+// choice of kernel, launch planning, and error reporting.
+//
+// Every check runs before the first launch, so a failing call writes
+// nothing.  The library allocates no device memory: all buffers belong to
+// the caller, and the only per-process state is the cached LDS limit of
+// each device and the per-thread error message.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "../../include/mp3d.h"
+#include "dtype.hpp"
+#include "kernels.hpp"
+
+namespace mp3d {
+
+namespace {
+
+thread_local char g_msg[256] = "";
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool log_enabled()
+{
+    static int on = -1;
+    if (on < 0) {
+        const char *v = getenv("MP3D_LOG");
+        on = (v && *v && strcmp(v, "0") != 0) ? 1 : 0;
+    }
+    return on == 1;
+}
+
+constexpr int64_t kInt32Max = 2147483647;
+
+// Shared checks of shapes and pointers; fills the per-plane sizes of g.
+int check_common(int dtype, int64_t N, int64_t C, int64_t D, int64_t H, int64_t W)
+{
+    if (dtype != MP3D_F32 && dtype != MP3D_F16 && dtype != MP3D_BF16)
+        return fail(MP3D_EDTYPE, "dtype %d is not MP3D_F32, MP3D_F16 or MP3D_BF16", dtype);
+    if (N < 0 || C < 0)
+        return fail(MP3D_EINVAL, "N=%lld and C=%lld must be >= 0", (long long)N, (long long)C);
+    if (D <= 0 || H <= 0 || W <= 0)
+        return fail(MP3D_EINVAL, "spatial extents must be >= 1 (D=%lld H=%lld W=%lld)",
+                    (long long)D, (long long)H, (long long)W);
+    if (D > kInt32Max || H > kInt32Max || W > kInt32Max || D * H > kInt32Max ||
+        D * H * W > kInt32Max)
+        return fail(MP3D_EOVERFLOW, "D*H*W exceeds the int32 index range");
+    const int64_t plane = D * H * W;
+    if (N > 0 && C > ((int64_t)1 << 62) / N / plane)
+        return fail(MP3D_EOVERFLOW, "N*C*D*H*W exceeds 2^62 elements");
+    return MP3D_OK;
+}
+
+int set_fixed_axis(Axis *a, int64_t X, int32_t k, int32_t s, const char *name)
+{
+    if (k <= 0 || s <= 0)
+        return fail(MP3D_EINVAL, "kernel and stride on %s must be >= 1 (got %d, %d)", name, k, s);
+    if (X < k)
+        return fail(MP3D_EINVAL, "kernel %d exceeds extent %lld on %s", k, (long long)X, name);
+    *a = Axis{(int32_t)X, (int32_t)((X - k) / s + 1), k, s};
+    return MP3D_OK;
+}
+
+int set_adaptive_axis(Axis *a, int64_t X, int32_t O, const char *name)
+{
+    if (O <= 0)
+        return fail(MP3D_EINVAL, "output extent on %s must be >= 1 (got %d)", name, O);
+    *a = Axis{(int32_t)X, O, 0, 0};
+    return MP3D_OK;
+}
+
+int finish_geom(Geom *g, int64_t N, int64_t C)
+{
+    const int64_t out = (int64_t)g->ax[0].O * g->ax[1].O * g->ax[2].O;
+    if ((int64_t)g->ax[0].O * g->ax[1].O > kInt32Max || out > kInt32Max)
+        return fail(MP3D_EOVERFLOW, "OD*OH*OW exceeds the int32 range");
+    g->planes = N * C;
+    g->in_plane = g->ax[0].X * g->ax[1].X * g->ax[2].X;
+    g->out_plane = (int32_t)out;
+    if (g->planes > 0 && g->planes > ((int64_t)1 << 62) / out)
+        return fail(MP3D_EOVERFLOW, "N*C*OD*OH*OW exceeds 2^62 elements");
+    return MP3D_OK;
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return MP3D_OK;
+    return fail(MP3D_EHIP, "%s: %s (hipError %d)", what, hipGetErrorString(e), (int)e);
+}
+
+template <typename T>
+int run_forward(const void *x, void *y, int32_t *idx, const Geom &g, hipStream_t s)
+{
+    FwdPlan p;
+    if (plan_forward(g, (int)sizeof(typename T::raw), &p)) {
+        if (log_enabled())
+            fprintf(stderr, "[mp3d] forward tile dtype=%d tile=(%d,%d,%d) tiles=%lld lds=%u\n",
+                    T::code, p.tod, p.toh, p.tow, (long long)p.ntiles, p.lds_bytes);
+        return hip_status(launch_forward_tile<T>(x, y, idx, p, s), "forward tile launch");
+    }
+    if (log_enabled()) fprintf(stderr, "[mp3d] forward direct dtype=%d\n", T::code);
+    return hip_status(launch_forward_direct<T>(x, y, idx, g, s), "forward direct launch");
+}
+
+int forward(const void *x, void *y, int32_t *idx, int dtype, const Geom &g, hipStream_t s)
+{
+    if (g.planes == 0) return MP3D_OK;
+    if (!x || !y || !idx) return fail(MP3D_EINVAL, "null tensor pointer");
+    switch (dtype) {
+    case MP3D_F32: return run_forward<F32>(x, y, idx, g, s);
+    case MP3D_F16: return run_forward<F16>(x, y, idx, g, s);
+    default: return run_forward<BF16>(x, y, idx, g, s);
+    }
+}
+
+template <typename T>
+int run_backward(const void *gy, const int32_t *idx, void *gx, const Geom &g, bool gather,
+                 hipStream_t s)
+{
+    if (gather) {
+        GatherPlan p{g, g.ax[0].X / g.ax[0].O, g.ax[1].X / g.ax[1].O, g.ax[2].X / g.ax[2].O};
+        if (log_enabled()) fprintf(stderr, "[mp3d] backward gather dtype=%d\n", T::code);
+        return hip_status(launch_backward_gather<T>(gy, idx, gx, p, s), "backward gather launch");
+    }
+    BwdPlan p;
+    plan_backward(g, &p);
+    if (log_enabled())
+        fprintf(stderr, "[mp3d] backward accumulate dtype=%d box=(%d,%d,%d) tiles=%lld lds=%u\n",
+                T::code, p.td, p.th, p.tw, (long long)p.ntiles, p.lds_bytes);
+    return hip_status(launch_backward_tile<T>(gy, idx, gx, p, s), "backward tile launch");
+}
+
+// Windows tile an axis -- each position in exactly one window, the one
+// given by p / (X/O) -- for adaptive windows when O divides X, and for
+// fixed windows when stride == X/O and kernel <= stride.
+bool axis_tiles(const Axis &a)
+{
+    if (a.X % a.O != 0) return false;
+    if (a.k == 0) return true;
+    return a.s == a.X / a.O && a.k <= a.s;
+}
+
+}  // namespace
+
+size_t lds_limit()
+{
+    static std::mutex mu;
+    static size_t cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cache[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            v <= 0)
+            v = 64 * 1024;
+        cache[dev] = (size_t)v;
+    }
+    return cache[dev];
+}
+
+}  // namespace mp3d
+
+using namespace mp3d;
+
+extern "C" {
+
+int mp3d_out_size(int64_t X, int32_t k, int32_t s, int64_t *out)
+{
+    if (!out) return fail(MP3D_EINVAL, "out is NULL");
+    if (k <= 0 || s <= 0) return fail(MP3D_EINVAL, "kernel and stride must be >= 1");
+    if (X < k) return fail(MP3D_EINVAL, "kernel %d exceeds extent %lld", k, (long long)X);
+    *out = (X - k) / s + 1;
+    return MP3D_OK;
+}
+
+int mp3d_forward(const void *x, void *y, int32_t *idx, int dtype, int64_t N, int64_t C,
+                 int64_t D, int64_t H, int64_t W, int32_t kd, int32_t kh, int32_t kw,
+                 int32_t sd, int32_t sh, int32_t sw, void *stream)
+{
+    int rc = check_common(dtype, N, C, D, H, W);
+    if (rc) return rc;
+    Geom g;
+    if ((rc = set_fixed_axis(&g.ax[0], D, kd, sd, "D"))) return rc;
+    if ((rc = set_fixed_axis(&g.ax[1], H, kh, sh, "H"))) return rc;
+    if ((rc = set_fixed_axis(&g.ax[2], W, kw, sw, "W"))) return rc;
+    if ((rc = finish_geom(&g, N, C))) return rc;
+    return forward(x, y, idx, dtype, g, (hipStream_t)stream);
+}
+
+int amp3d_forward(const void *x, void *y, int32_t *idx, int dtype, int64_t N, int64_t C,
+                  int64_t D, int64_t H, int64_t W, int32_t od, int32_t oh, int32_t ow,
+                  void *stream)
+{
+    int rc = check_common(dtype, N, C, D, H, W);
+    if (rc) return rc;
+    Geom g;
+    if ((rc = set_adaptive_axis(&g.ax[0], D, od, "D"))) return rc;
+    if ((rc = set_adaptive_axis(&g.ax[1], H, oh, "H"))) return rc;
+    if ((rc = set_adaptive_axis(&g.ax[2], W, ow, "W"))) return rc;
+    if ((rc = finish_geom(&g, N, C))) return rc;
+    return forward(x, y, idx, dtype, g, (hipStream_t)stream);
+}
+
+int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype, int64_t N,
+                  int64_t C, int64_t D, int64_t H, int64_t W, int32_t od, int32_t oh,
+                  int32_t ow, int32_t kd, int32_t kh, int32_t kw, int32_t sd, int32_t sh,
+                  int32_t sw, int overlap, void *stream)
+{
+    int rc = check_common(dtype, N, C, D, H, W);
+    if (rc) return rc;
+    if (overlap < -1 || overlap > 1)
+        return fail(MP3D_EINVAL, "overlap must be -1, 0 or 1 (got %d)", overlap);
+    const int64_t X[3] = {D, H, W};
+    const int32_t O[3] = {od, oh, ow}, K[3] = {kd, kh, kw}, S[3] = {sd, sh, sw};
+    const char *names[3] = {"D", "H", "W"};
+    Geom g;
+    for (int a = 0; a < 3; ++a) {
+        if (K[a] == 0 && S[a] == 0) {
+            if ((rc = set_adaptive_axis(&g.ax[a], X[a], O[a], names[a]))) return rc;
+        } else {
+            if ((rc = set_fixed_axis(&g.ax[a], X[a], K[a], S[a], names[a]))) return rc;
+            if (g.ax[a].O != O[a])
+                return fail(MP3D_EINVAL,
+                            "output extent %d on %s does not match (X-k)/s+1 = %d", O[a],
+                            names[a], g.ax[a].O);
+        }
+    }
+    if ((rc = finish_geom(&g, N, C))) return rc;
+    const bool tiles = axis_tiles(g.ax[0]) && axis_tiles(g.ax[1]) && axis_tiles(g.ax[2]);
+    if (overlap == 0 && !tiles)
+        return fail(MP3D_ENOTDIV, "overlap=0 needs windows that tile every axis");
+    if (g.planes == 0) return MP3D_OK;
+    if (!gy || !idx || !gx) return fail(MP3D_EINVAL, "null tensor pointer");
+    const bool gather = overlap == 0 || (overlap == -1 && tiles);
+    const hipStream_t s = (hipStream_t)stream;
+    switch (dtype) {
+    case MP3D_F32: return run_backward<F32>(gy, idx, gx, g, gather, s);
+    case MP3D_F16: return run_backward<F16>(gy, idx, gx, g, gather, s);
+    default: return run_backward<BF16>(gy, idx, gx, g, gather, s);
+    }
+}
+
+const char *mp3d_strerror(int code)
+{
+    switch (code) {
+    case MP3D_OK: return "success";
+    case MP3D_EINVAL: return "invalid argument";
+    case MP3D_EDTYPE: return "unsupported dtype";
+    case MP3D_ENOTDIV: return "windows do not tile every axis";
+    case MP3D_EOVERFLOW: return "size exceeds the index range";
+    case MP3D_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *mp3d_last_error(void) { return g_msg; }
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+/*
+ * mp3d.h -- C ABI of libmp3d: 3-D max pooling over NCDHW tensors on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operations:
+ *  - forward, fixed windows: "Struct Maxpool3dForward" (teenygrad API docs),
+ *    the description under the struct: one output per window, no padding,
+ *    and per axis O = (X - K) / STRIDE + 1 with integer division.  Window o
+ *    covers [o*STRIDE, o*STRIDE + K).
+ *  - forward, adaptive windows, and the backward: "[KernelGen][MThreads]
+ *    Add adaptive_max_pool3d_backward Moore Threads specialized operator"
+ *    (FlagGems-Experimental PR #308), Summary.  The backward sends each
+ *    output window's gradient to the input position of that window's
+ *    argmax.  When every spatial axis divides evenly the windows tile the
+ *    input and each input is reached by at most one window (a gather with a
+ *    single write per input); otherwise windows overlap and contributions
+ *    add (a zero-filled accumulator plus an atomic scatter).  The page
+ *    prints no window formula; this library takes window o of O over an
+ *    axis of length X to cover [floor(o*X/O), ceil((o+1)*X/O)).
+ *
+ * Semantics fixed here where the pages are silent:
+ *  - A window is scanned d, then h, then w, ascending.  The argmax is the
+ *    first element in that order that is not smaller than any other: ties
+ *    go to the earlier element, -0 and +0 tie, and NaN counts as larger
+ *    than every number (the first NaN wins).  y holds that element's bits.
+ *  - idx is int32, flat within one plane: (d*H + h)*W + w.
+ *  - The backward accumulates in binary32 from +0 and rounds the sum once,
+ *    to nearest-even, into the storage type.
+ *
+ * Layout and ownership: every tensor is contiguous NCDHW in device memory
+ * owned by the caller; the library never allocates or frees.  x and gx
+ * hold N*C*D*H*W elements; y, idx and gy hold N*C*OD*OH*OW.  Outputs must
+ * not alias inputs, and each pointer is aligned to its element size.
+ * dtype selects the storage type of x, y, gy and gx
+ * (MP3D_F32, MP3D_F16, MP3D_BF16); idx is always int32.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Calls enqueue their kernels and return without synchronising;
+ * device faults surface at the caller's next synchronisation.
+ *
+ * Errors: every call returns MP3D_OK (0) or an error code.  All argument
+ * checks run before the first launch, so a call that fails leaves every
+ * output untouched.  mp3d_last_error() gives a message for the calling
+ * thread's most recent failure.  N*C == 0 is a valid no-op.
+ */
+#ifndef MP3D_H
+#define MP3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mp3d_status {
+    MP3D_OK = 0,
+    MP3D_EINVAL = 1,    /* null pointer with work to do, a size, kernel,
+                           stride or output extent <= 0, a window larger
+                           than its axis, or inconsistent shapes */
+    MP3D_EDTYPE = 2,    /* dtype is not one of MP3D_F32/F16/BF16 */
+    MP3D_ENOTDIV = 3,   /* overlap = 0 asked for, but the windows do not
+                           tile every axis (see mp3d_backward) */
+    MP3D_EOVERFLOW = 4, /* D*H*W > INT32_MAX (int32 idx impossible) or an
+                           element count beyond 2^62 */
+    MP3D_EHIP = 5       /* a HIP launch failed; the message names it */
+};
+
+enum mp3d_dtype { MP3D_F32 = 0, MP3D_F16 = 1, MP3D_BF16 = 2 };
+
+/* Forward with fixed windows (teenygrad "Struct Maxpool3dForward",
+ * description): kernel (kd, kh, kw), stride (sd, sh, sw), no padding.
+ * Output extents are (D-kd)/sd+1, (H-kh)/sh+1, (W-kw)/sw+1; the caller
+ * sizes y and idx from mp3d_out_size.  Writes y (dtype) and idx (int32).
+ * MP3D_EINVAL if any kernel or stride is <= 0 or a kernel exceeds its
+ * axis. */
+int mp3d_forward(const void *x, void *y, int32_t *idx, int dtype,
+                 int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                 int32_t kd, int32_t kh, int32_t kw,
+                 int32_t sd, int32_t sh, int32_t sw, void *stream);
+
+/* Forward with adaptive windows (PR #308, Summary): output extents
+ * (od, oh, ow), each >= 1 (an extent larger than its axis is allowed; the
+ * windows then have width 1 or 2 and overlap).  Writes y and idx. */
+int amp3d_forward(const void *x, void *y, int32_t *idx, int dtype,
+                  int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                  int32_t od, int32_t oh, int32_t ow, void *stream);
+
+/* Backward (PR #308, Summary): gx[p] = sum of gy[o] over the outputs o
+ * whose idx[o] == p, in binary32 from +0, rounded once to dtype; +0 where
+ * no output points.  Every element of gx is written.
+ *
+ * (N, C, D, H, W) is the input shape; (od, oh, ow) the shape of gy and
+ * idx.  The window rule is given per axis so that the library knows which
+ * windows can reach a block of gx: kd/kh/kw and sd/sh/sw > 0 select fixed
+ * windows on that axis (od must then equal (D-kd)/sd+1, and so on); a
+ * kernel and stride of 0 select adaptive windows on that axis.
+ *
+ * overlap selects the path:
+ *   0  gather: one pass over gx, no accumulator, no atomics.  Valid only
+ *      when the windows tile every axis: X % O == 0 and, for fixed windows,
+ *      stride == X / O and kernel <= stride.  Otherwise MP3D_ENOTDIV.
+ *   1  accumulate: zero-filled binary32 accumulator, atomic scatter of gy
+ *      at idx, one rounding store.  Valid for every geometry.
+ *  -1  choose: 0 when valid, else 1.
+ * Each idx[o] must lie inside window o, as the forward produces it; idx
+ * values outside [0, D*H*W) are ignored (never written, never a fault),
+ * and in-range values outside their window give unspecified but
+ * memory-safe results. */
+int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype,
+                  int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                  int32_t od, int32_t oh, int32_t ow,
+                  int32_t kd, int32_t kh, int32_t kw,
+                  int32_t sd, int32_t sh, int32_t sw,
+                  int overlap, void *stream);
+
+/* Fixed-window output extent (X - k)/s + 1 into *out.  MP3D_EINVAL if
+ * k <= 0, s <= 0, X < k or out is NULL. */
+int mp3d_out_size(int64_t X, int32_t k, int32_t s, int64_t *out);
+
+/* Text for a status code (static storage). */
+const char *mp3d_strerror(int code);
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+const char *mp3d_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MP3D_H */

@@ -1,0 +1,105 @@
+"""The C ABI on the host: the library loads, exports every entry point the
+header declares, and rejects bad arguments with the documented codes
+before touching the GPU (none of these calls reaches a HIP API)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bwd_max_pool3d_amd as mp
+from bwd_max_pool3d_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "mp3d.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for want in ("mp3d_forward", "amp3d_forward", "mp3d_backward"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_lib.EXPORTS) == set(declared_functions())
+
+
+def test_out_size():
+    assert mp.mp3d_out_size(16, 2, 2) == 8
+    assert mp.mp3d_out_size(112, 2, 2) == 56
+    assert mp.mp3d_out_size(32, 3, 2) == 15
+    assert mp.mp3d_out_size(56, 3, 2) == 27
+    assert mp.mp3d_out_size(5, 5, 1) == 1
+    for X, k, s in [(2, 3, 1), (5, 0, 1), (5, 2, 0), (5, -1, 1)]:
+        with pytest.raises(mp.Mp3dError) as e:
+            mp.mp3d_out_size(X, k, s)
+        assert e.value.code == _lib.MP3D_EINVAL
+    assert _lib.load().mp3d_out_size(5, 2, 2, None) == _lib.MP3D_EINVAL
+
+
+FAKE = 0x1000   # never dereferenced: every call below fails validation
+
+
+def fwd(*, x=FAKE, y=FAKE, idx=FAKE, dtype=0, shape=(1, 1, 4, 4, 4), k=(2, 2, 2), s=(2, 2, 2)):
+    return _lib.load().mp3d_forward(x, y, idx, dtype, *shape, *k, *s, None)
+
+
+def afwd(*, x=FAKE, dtype=0, shape=(1, 1, 4, 4, 4), out=(2, 2, 2)):
+    return _lib.load().amp3d_forward(x, FAKE, FAKE, dtype, *shape, *out, None)
+
+
+def bwd(*, gy=FAKE, dtype=0, shape=(1, 1, 4, 4, 4), out=(2, 2, 2), k=(0, 0, 0), s=(0, 0, 0),
+        overlap=-1):
+    return _lib.load().mp3d_backward(gy, FAKE, FAKE, dtype, *shape, *out, *k, *s, overlap, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: fwd(dtype=3), _lib.MP3D_EDTYPE),
+    (lambda: fwd(dtype=-1), _lib.MP3D_EDTYPE),
+    (lambda: fwd(x=None), _lib.MP3D_EINVAL),
+    (lambda: fwd(idx=None), _lib.MP3D_EINVAL),
+    (lambda: fwd(k=(0, 2, 2)), _lib.MP3D_EINVAL),
+    (lambda: fwd(s=(2, 2, -1)), _lib.MP3D_EINVAL),
+    (lambda: fwd(k=(5, 2, 2)), _lib.MP3D_EINVAL),
+    (lambda: fwd(shape=(1, 1, 0, 4, 4)), _lib.MP3D_EINVAL),
+    (lambda: fwd(shape=(-1, 1, 4, 4, 4)), _lib.MP3D_EINVAL),
+    (lambda: fwd(shape=(1, 1, 2048, 1024, 1024)), _lib.MP3D_EOVERFLOW),
+    (lambda: fwd(shape=(1 << 40, 1 << 20, 4, 4, 4)), _lib.MP3D_EOVERFLOW),
+    (lambda: afwd(out=(0, 2, 2)), _lib.MP3D_EINVAL),
+    (lambda: afwd(x=None), _lib.MP3D_EINVAL),
+    (lambda: afwd(out=(65536, 65536, 2)), _lib.MP3D_EOVERFLOW),
+    (lambda: bwd(overlap=2), _lib.MP3D_EINVAL),
+    (lambda: bwd(gy=None), _lib.MP3D_EINVAL),
+    (lambda: bwd(shape=(1, 1, 5, 5, 5), overlap=0), _lib.MP3D_ENOTDIV),
+    (lambda: bwd(shape=(1, 1, 8, 8, 8), out=(2, 2, 2), k=(3, 3, 3), s=(3, 3, 3), overlap=0),
+     _lib.MP3D_ENOTDIV),  # 8 % 2 == 0 but the windows [0,3), [3,6) do not tile
+    (lambda: bwd(shape=(1, 1, 6, 6, 6), out=(3, 2, 2), k=(3, 3, 3), s=(3, 3, 3)), _lib.MP3D_EINVAL),
+    (lambda: bwd(k=(2, 0, 2), s=(2, 2, 2)), _lib.MP3D_EINVAL),
+    (lambda: bwd(dtype=5), _lib.MP3D_EDTYPE),
+])
+def test_validation_codes(call, code):
+    assert call() == code
+    assert _lib.load().mp3d_last_error().decode() != ""
+
+
+def test_empty_batch_is_a_no_op():
+    # N*C == 0: nothing to do, even with null pointers
+    assert fwd(x=None, y=None, idx=None, shape=(0, 3, 4, 4, 4)) == _lib.MP3D_OK
+    assert afwd(x=None, shape=(2, 0, 4, 4, 4)) == _lib.MP3D_OK
+    assert bwd(gy=None, shape=(0, 0, 4, 4, 4)) == _lib.MP3D_OK
+
+
+def test_strerror_covers_every_code():
+    lib = _lib.load()
+    texts = {lib.mp3d_strerror(c).decode() for c in range(6)}
+    assert len(texts) == 6
+    assert lib.mp3d_strerror(99).decode() == "unknown status"

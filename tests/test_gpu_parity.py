@@ -1,0 +1,317 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases are compared element by element over the whole tensor; the
+large workloads are run at full size in the launch configuration the
+benchmark times and compared on sampled planes, plus properties checked on
+every element.  See tests/_gpu.py for the bar each output must meet.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import _golden
+import _gpu
+import _pins
+import bwd_max_pool3d_amd as mp
+from bwd_max_pool3d_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [torch.float32, torch.float16, torch.bfloat16]
+DT_ID = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
+# (shape, adaptive out or None, kernel, stride)
+CASES = [
+    ((2, 3, 8, 8, 8), (4, 4, 4), None, None),
+    ((1, 2, 10, 10, 10), (8, 8, 8), None, None),
+    ((1, 1, 7, 7, 7), (8, 8, 8), None, None),             # output larger than input
+    ((2, 2, 5, 6, 7), (3, 4, 2), None, None),
+    ((1, 2, 16, 32, 32), (5, 7, 7), None, None),
+    ((3, 1, 1, 1, 1), (1, 1, 1), None, None),
+    ((1, 2, 1, 1, 9), (1, 1, 4), None, None),
+    ((1, 1, 4, 3, 5), (1, 1, 1), None, None),             # one global window
+    ((1, 1, 9, 1, 1), (4, 1, 1), None, None),
+    ((2, 1, 6, 6, 6), (6, 6, 6), None, None),             # identity
+    ((1, 1, 64, 64, 64), (1, 1, 1), None, None),          # window too big for LDS
+    ((2, 3, 8, 8, 8), None, (2, 2, 2), (2, 2, 2)),
+    ((1, 2, 9, 8, 7), None, (3, 3, 3), (2, 2, 2)),
+    ((2, 1, 9, 5, 11), None, (2, 3, 2), (3, 1, 2)),       # gaps between windows
+    ((1, 1, 6, 6, 6), None, (1, 1, 1), (1, 1, 1)),
+    ((1, 1, 8, 4, 6), None, (1, 1, 1), (2, 2, 2)),        # tiles with k < s
+    ((1, 2, 32, 56, 56), None, (3, 3, 3), (2, 2, 2)),
+    ((1, 1, 16, 112, 112), None, (2, 2, 2), (2, 2, 2)),
+    ((1, 1, 5, 5, 5), None, (5, 5, 5), (1, 1, 1)),
+    ((1, 1, 7, 300, 300), None, (2, 3, 3), (2, 2, 2)),    # slices larger than LDS
+    ((1, 1, 2, 1, 70000), None, (1, 1, 5), (1, 1, 3)),    # rows larger than LDS
+    ((2, 1, 3, 5000, 1), (2, 777, 1), None, None),
+]
+
+
+def _case_id(c):
+    shape, out, k, s = c
+    geo = "a%s" % "x".join(map(str, out)) if out else "k%ss%s" % (
+        "".join(map(str, k)), "".join(map(str, s)))
+    return "%s-%s" % ("x".join(map(str, shape)), geo)
+
+
+def _tiles(shape, out, k, s, orc):
+    o3 = _gpu.out_shape(orc, shape, out, k, s)
+    for a in range(3):
+        X, O = shape[2 + a], o3[a]
+        if X % O:
+            return False
+        if k is not None and not (s[a] == X // O and k[a] <= s[a]):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_small_forward_backward(orc, case, dtype):
+    shape, out, k, s = case
+    code = _gpu.CODE[dtype]
+    base = abs(hash((shape, out, k, s))) % 10000
+    for j, kind in enumerate(("normal", "ties", "special")):
+        x = _pins.from_storage(_pins.draw(shape, code, kind, base + j), code)
+        y, idx = _gpu.gpu_forward(x, out, k, s)
+        yo, io = _gpu.oracle_forward(orc, x, out, k, s)
+        _gpu.assert_forward_match(y, idx, yo, io, "%s fwd %s" % (_case_id(case), kind))
+    # backward on the last forward's idx
+    gy = _pins.from_storage(_pins.draw(tuple(y.shape), code, "normal", base + 7), code)
+    tiles = _tiles(shape, out, k, s, orc)
+    gx = _gpu.gpu_backward(gy, idx.cpu(), shape, k, s, overlap=-1)
+    _gpu.check_backward(orc, gy, idx.cpu(), shape, gx, exact=tiles, what=_case_id(case))
+    if tiles:
+        # the accumulate path must also be exact here: one contribution per cell
+        gx1 = _gpu.gpu_backward(gy, idx.cpu(), shape, k, s, overlap=1)
+        _gpu.check_backward(orc, gy, idx.cpu(), shape, gx1, exact=True, what="forced accumulate")
+
+
+@pytest.mark.parametrize("case", _golden.pr308_cases(), ids=lambda c: "%s-%s-%s" % (
+    c[1], "x".join(map(str, c[2])), "x".join(map(str, c[3]))))
+def test_pr308_shapes(orc, case):
+    """Every shape printed on the PR #308 page (tests/golden/pr308_shapes.txt)."""
+    kind, dt, shape, out = case
+    dtype = workloads.DTYPES[dt]
+    code = _gpu.CODE[dtype]
+    x = _pins.from_storage(_pins.draw(shape, code, "ties", 11), code)
+    y, idx = _gpu.gpu_forward(x, out)
+    yo, io = _gpu.oracle_forward(orc, x, out)
+    _gpu.assert_forward_match(y, idx, yo, io, "pr308 fwd")
+    gy = _pins.from_storage(_pins.draw(tuple(y.shape), code, "normal", 12), code)
+    gx = _gpu.gpu_backward(gy, idx.cpu(), shape)
+    exact = all(X % O == 0 for X, O in zip(shape[2:], out))
+    _gpu.check_backward(orc, gy, idx.cpu(), shape, gx, exact=exact, what="pr308 bwd")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+def test_misaligned_pointers(orc, dtype):
+    """Tensors starting one element past a 16-byte boundary."""
+    code = _gpu.CODE[dtype]
+    shape = (2, 3, 10, 9, 7)
+    n = int(np.prod(shape))
+    x0 = _pins.from_storage(_pins.draw(shape, code, "normal", 3), code)
+    buf = torch.empty(n + 1, dtype=dtype, device="cuda")
+    xd = buf[1:].view(shape)
+    xd.copy_(x0.cuda())
+    assert xd.data_ptr() % 16 != 0
+    for out, k, s in [((4, 4, 3), None, None), (None, (3, 2, 3), (2, 2, 2))]:
+        y, idx = _gpu.gpu_forward(xd, out, k, s)
+        yo, io = _gpu.oracle_forward(orc, x0, out, k, s)
+        _gpu.assert_forward_match(y, idx, yo, io, "misaligned fwd")
+        gy0 = _pins.from_storage(_pins.draw(tuple(y.shape), code, "normal", 4), code)
+        gbuf = torch.empty(gy0.numel() + 1, dtype=dtype, device="cuda")
+        gyd = gbuf[1:].view(gy0.shape)
+        gyd.copy_(gy0.cuda())
+        xbuf = torch.full((n + 1,), float("nan"), dtype=dtype, device="cuda")
+        gxd = xbuf[1:].view(shape)
+        mp.mp3d_backward(gyd, idx, shape, kernel=k, stride=s, out=gxd)
+        _gpu.check_backward(orc, gy0, idx.cpu(), shape, gxd, exact=False, what="misaligned bwd")
+
+
+def test_many_small_planes(orc):
+    shape = (256, 256, 2, 2, 2)
+    x = _pins.from_storage(_pins.draw(shape, 1, "ties", 5), 1)
+    for out, k, s in [((1, 1, 1), None, None), (None, (2, 2, 2), (2, 2, 2)),
+                      ((2, 1, 2), None, None)]:
+        y, idx = _gpu.gpu_forward(x, out, k, s)
+        yo, io = _gpu.oracle_forward(orc, x, out, k, s)
+        _gpu.assert_forward_match(y, idx, yo, io, "many planes")
+        gy = _pins.from_storage(_pins.draw(tuple(y.shape), 1, "normal", 6), 1)
+        gx = _gpu.gpu_backward(gy, idx.cpu(), shape, k, s)
+        _gpu.check_backward(orc, gy, idx.cpu(), shape, gx, exact=True, what="many planes")
+
+
+def test_subnormal_gradients(orc):
+    """float32 subnormal contributions are accumulated exactly (no flush)."""
+    shape = (2, 2, 10, 10, 10)
+    x = _pins.from_storage(_pins.draw(shape, 0, "ties", 8), 0)
+    y, idx = _gpu.gpu_forward(x, (8, 8, 8))
+    g = torch.randn(y.shape, generator=torch.Generator().manual_seed(9)) * 1e-39
+    gx = _gpu.gpu_backward(g, idx.cpu(), shape)
+    _gpu.check_backward(orc, g, idx.cpu(), shape, gx, exact=False, what="subnormal")
+
+
+def test_out_of_range_idx_ignored(orc):
+    shape = (1, 2, 6, 6, 6)
+    g = torch.Generator().manual_seed(3)
+    # small integers: every sum is exact in any order, so runs compare bitwise
+    gy = torch.randint(-3, 4, (1, 2, 4, 4, 4), generator=g).float()
+    idx = torch.randint(0, 216, (1, 2, 4, 4, 4), generator=g, dtype=torch.int32)
+    idx.view(-1)[::5] = -1
+    idx.view(-1)[1::7] = 216
+    idx.view(-1)[2::11] = 2**31 - 1
+    # adaptive windows 6 -> 4 overlap, so the accumulate path runs; idx here
+    # is arbitrary in-plane data, which that path handles as the oracle does
+    # only for entries inside their windows -- so restrict to the window-free
+    # property: out-of-range entries change nothing.
+    gx_all = _gpu.gpu_backward(gy, idx, shape, overlap=1)
+    keep = (idx >= 0) & (idx < 216)
+    gy2 = gy.clone()
+    gy2[~keep] = 0
+    gx_kept = _gpu.gpu_backward(gy2, idx, shape, overlap=1)
+    assert torch.equal(gx_all.cpu(), gx_kept.cpu())
+
+
+def test_side_stream(orc):
+    """Work is enqueued on the caller's current stream."""
+    shape = (4, 8, 16, 16, 16)
+    x = _pins.from_storage(_pins.draw(shape, 2, "normal", 21), 2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xd = x.cuda(non_blocking=False)
+        y, idx = mp.amp3d_forward(xd, (5, 7, 7))
+        gy = torch.ones_like(y)
+        gx = mp.mp3d_backward(gy, idx, shape)
+    s.synchronize()
+    yo, io = _gpu.oracle_forward(orc, x, (5, 7, 7))
+    _gpu.assert_forward_match(y, idx, yo, io, "side stream")
+    _gpu.check_backward(orc, gy.cpu(), idx.cpu(), shape, gx, exact=False, what="side stream")
+
+
+def test_repeatable(orc):
+    """Forward and gather results are bit-identical across runs."""
+    shape = (2, 16, 16, 32, 32)
+    x = _pins.from_storage(_pins.draw(shape, 0, "ties", 31), 0).cuda()
+    ref = mp.amp3d_forward(x, (5, 7, 7))
+    g1 = mp.mp3d_backward(torch.ones_like(ref[0]), ref[1], shape)
+    for _ in range(5):
+        y, idx = mp.amp3d_forward(x, (5, 7, 7))
+        assert torch.equal(y.view(torch.int32), ref[0].view(torch.int32))
+        assert torch.equal(idx, ref[1])
+    yd, idd = mp.amp3d_forward(x, (8, 16, 16))
+    gd = mp.mp3d_backward(yd, idd, shape)
+    for _ in range(5):
+        assert torch.equal(mp.mp3d_backward(yd, idd, shape).view(torch.int32), gd.view(torch.int32))
+    assert g1.shape == shape
+
+
+def test_errors_leave_outputs_untouched():
+    x = torch.randn(1, 1, 4, 4, 4, device="cuda")
+    y = torch.full((1, 1, 2, 2, 2), 5.0, device="cuda")
+    idx = torch.full((1, 1, 2, 2, 2), 9, dtype=torch.int32, device="cuda")
+    with pytest.raises(mp.Mp3dError) as e:
+        mp.mp3d_forward(x, (5, 2, 2), (1, 1, 1))          # kernel larger than D
+    assert e.value.code == 1
+    lib = mp._lib.load()
+    rc = lib.mp3d_forward(x.data_ptr(), y.data_ptr(), idx.data_ptr(), 9, 1, 1, 4, 4, 4,
+                          2, 2, 2, 2, 2, 2, None)
+    assert rc == 2
+    rc = lib.mp3d_backward(y.data_ptr(), idx.data_ptr(), x.data_ptr(), 0, 1, 1, 5, 5, 5,
+                           2, 2, 2, 0, 0, 0, 0, 0, 0, 0, None)
+    assert rc == 3                                         # 5 -> 2 does not tile
+    torch.cuda.synchronize()
+    assert (y == 5).all() and (idx == 9).all()
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size
+# ---------------------------------------------------------------------------
+
+def _sample_planes(P: int, n: int = 10, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    picks = {0, P - 1} | set(int(v) for v in rng.integers(0, P, size=n))
+    return sorted(picks)
+
+
+def _windows(orc, X, O, k, s):
+    lo = [orc.window(X, O, k, s, o)[0] for o in range(O)]
+    hi = [orc.window(X, O, k, s, o)[1] for o in range(O)]
+    return torch.tensor(lo, device="cuda"), torch.tensor(hi, device="cuda")
+
+
+def _full_properties(orc, wl, x, y, idx):
+    """On every output: y has the bits of x at idx, and idx lies inside
+    the output's own window."""
+    N, C, D, H, W = wl.shape
+    bits = torch.int16 if x.element_size() == 2 else torch.int32
+    ix = torch.gather(x.reshape(N * C, -1), 1, idx.reshape(N * C, -1).long())
+    assert torch.equal(ix.view(bits), y.reshape(N * C, -1).view(bits))
+    OD, OH, OW = y.shape[2:]
+    k = wl.kernel or (0, 0, 0)
+    s = wl.stride or (0, 0, 0)
+    i5 = idx.long()
+    comps = (i5 // (H * W), (i5 // W) % H, i5 % W)
+    for a, (X, O) in enumerate(zip((D, H, W), (OD, OH, OW))):
+        lo, hi = _windows(orc, X, O, k[a], s[a])
+        shape = [1, 1, 1, 1, 1]
+        shape[2 + a] = O
+        c = comps[a]
+        assert bool(((c >= lo.view(shape)) & (c < hi.view(shape))).all())
+
+
+def _full_backward_property(gy, idx, gx, in_shape):
+    """On every gx element: within the float32-summation bound (plus half a
+    unit in the last place of the storage type) of the exact sum."""
+    N, C, D, H, W = in_shape
+    P, n = N * C, D * H * W
+    ii = idx.view(P, -1).long()
+    g64 = gy.view(P, -1).double()
+    ref = torch.zeros(P, n, dtype=torch.float64, device="cuda").scatter_add_(1, ii, g64)
+    ab = torch.zeros(P, n, dtype=torch.float64, device="cuda").scatter_add_(1, ii, g64.abs())
+    cnt = torch.zeros(P, n, dtype=torch.float64, device="cuda").scatter_add_(
+        1, ii, torch.ones_like(g64))
+    half_ulp = {torch.float32: 0.0, torch.float16: 2.0**-11, torch.bfloat16: 2.0**-8}[gy.dtype]
+    tiny = {torch.float32: 0.0, torch.float16: 2.0**-25, torch.bfloat16: 2.0**-134}[gy.dtype]
+    bound = (cnt - 1).clamp(min=0) * 2.0**-24 * ab * 1.0001 + half_ulp * ref.abs() * 1.0001 + tiny
+    err = (gx.view(P, -1).double() - ref).abs()
+    assert bool((err <= bound).all()), "max excess %g" % float((err - bound).max())
+    assert bool((gx.view(P, -1)[cnt == 0] == 0).all())
+
+
+@pytest.mark.parametrize("wl", workloads.WORKLOADS, ids=lambda w: w.name)
+def test_workload_full_size(orc, wl):
+    N, C, D, H, W = wl.shape
+    P = N * C
+    x = wl.make_x()
+    xd = x.cuda()
+    out = wl.out
+    k, s = wl.kernel, wl.stride
+    y, idx = _gpu.gpu_forward(xd, out, k, s)
+    torch.cuda.synchronize()
+    small = P * D * H * W <= 1 << 20
+    planes = range(P) if small else _sample_planes(P)
+    for p in planes:
+        n_, c_ = divmod(p, C)
+        xp = x[n_:n_ + 1, c_:c_ + 1].contiguous()
+        yo, io = _gpu.oracle_forward(orc, xp, out, k, s)
+        _gpu.assert_forward_match(y[n_:n_ + 1, c_:c_ + 1], idx[n_:n_ + 1, c_:c_ + 1], yo, io,
+                                  "%s plane %d" % (wl.name, p))
+    _full_properties(orc, wl, xd, y, idx)
+    if not wl.backward:
+        return
+    gy = wl.make_gy(tuple(y.shape))
+    gyd = gy.cuda()
+    gx = _gpu.gpu_backward(gyd, idx, wl.shape, k, s)
+    torch.cuda.synchronize()
+    exact = all(X % O == 0 for X, O in zip(wl.shape[2:], y.shape[2:])) and (
+        k is None or all(ka == sa for ka, sa in zip(k, s)))
+    for p in planes:
+        n_, c_ = divmod(p, C)
+        sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
+        _gpu.check_backward(orc, gy[sl].contiguous(), idx[sl].cpu().contiguous(),
+                            (1, 1, D, H, W), gx[sl], exact=exact,
+                            what="%s plane %d" % (wl.name, p))
+    _full_backward_property(gyd, idx, gx, wl.shape)
