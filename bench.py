@@ -167,6 +167,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-oracle sample size in seconds (0 skips the leg)")
+    ap.add_argument("--only", default=None,
+                    help="time only the ops whose name contains this text (profiling aid; "
+                         "the JSON then covers that subset)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the step, run a plain 1 GiB device copy 10 times "
                          "(reference kernel for the HBM byte counters)")
@@ -189,8 +192,28 @@ def main():
         print(json.dumps({"copy_bytes_each_way": a.numel() * 4, "launches": 10}))
         return
 
+    # practical peak: a plain 1 GiB device-to-device copy (read + write)
+    ca = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    cb = torch.empty_like(ca)
+    for _ in range(3):
+        cb.copy_(ca)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        cb.copy_(ca)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * ca.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del ca, cb
+    torch.cuda.empty_cache()
+
     print("[bench] building inputs", file=sys.stderr, flush=True)
     ops = build_ops(torch, mp, workloads)
+    if args.only:
+        # forward ops must still run once so their idx feeds the backward
+        for op in ops:
+            op.fn()
+        ops = [op for op in ops if args.only in op.name]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
@@ -248,6 +271,7 @@ def main():
                    "step_bytes": step_bytes, "storage_dtypes": "f32, bf16, f16; idx int32",
                    "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "copy_GB_s": round(copy_gbs, 1),
         "roofline": roofline,
         "per_op": per_op,
     }

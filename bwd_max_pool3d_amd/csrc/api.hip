@@ -104,6 +104,20 @@ int hip_status(hipError_t e, const char *what)
 template <typename T>
 int run_forward(const void *x, void *y, int32_t *idx, const Geom &g, hipStream_t s)
 {
+    FixedPlan fp;
+    if (plan_fixed(g, (int)sizeof(typename T::raw), x, y, idx, &fp)) {
+        if (log_enabled())
+            fprintf(stderr, "[mp3d] forward fixed dtype=%d k=%d s=%d threads=%u vec_store=%d\n",
+                    T::code, g.ax[0].k, g.ax[0].s, fp.nthreads, fp.vec_store);
+        return hip_status(launch_forward_fixed<T>(x, y, idx, fp, s), "forward fixed launch");
+    }
+    ColPlan cp;
+    if (plan_col(g, (int)sizeof(typename T::raw), x, &cp)) {
+        if (log_enabled())
+            fprintf(stderr, "[mp3d] forward column dtype=%d tod=%d tiles=%u maxkd=%d lds=%u\n",
+                    T::code, cp.tod, cp.ntiles, cp.maxkd, cp.lds_bytes);
+        return hip_status(launch_forward_col<T>(x, y, idx, cp, s), "forward column launch");
+    }
     FwdPlan p;
     if (plan_forward(g, (int)sizeof(typename T::raw), &p)) {
         if (log_enabled())
@@ -154,6 +168,23 @@ bool axis_tiles(const Axis &a)
 }
 
 }  // namespace
+
+int device_cus()
+{
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cache[dev]) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cache[dev] = v;
+    }
+    return cache[dev];
+}
 
 size_t lds_limit()
 {

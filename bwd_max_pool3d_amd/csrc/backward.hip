@@ -17,6 +17,9 @@
 //    happen on-chip, so HBM sees gy and idx read and gx written once.
 // Accumulation is binary32 from +0 (so -0 contributions give +0) and the
 // sum is rounded once to the storage type.
+#include <algorithm>
+#include <climits>
+
 #include "dtype.hpp"
 #include "kernels.hpp"
 
@@ -24,66 +27,157 @@ namespace mp3d {
 
 namespace {
 
+// Blocks are dealt to the 8 XCDs round-robin by block id; renumber them so
+// that each XCD walks one contiguous run of tiles (tiles of one plane re-read
+// the windows on their borders through that XCD's L2).
+__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks)
+{
+    if (nblocks % 8u) return b;
+    return (b % 8u) * (nblocks / 8u) + b / 8u;
+}
+
+// Pack VE rounded accumulator values into one 16-byte store.
+template <typename T>
+__device__ __forceinline__ u32x4 pack16(const float *a)
+{
+    if constexpr (sizeof(typename T::raw) == 4) {
+        return *reinterpret_cast<const u32x4 *>(a);
+    } else {
+        const float4 u = *reinterpret_cast<const float4 *>(a);
+        const float4 v = *reinterpret_cast<const float4 *>(a + 4);
+        auto two = [](float lo, float hi) {
+            return (uint32_t)T::narrow(lo) | ((uint32_t)T::narrow(hi) << 16);
+        };
+        return u32x4{two(u.x, u.y), two(u.z, u.w), two(v.x, v.y), two(v.z, v.w)};
+    }
+}
+
+constexpr int kRound = 8;   // windows per thread fetched per round
+
+// An input box of one plane and the windows that can reach it.
+struct BTile {
+    int64_t plane;
+    int32_t d0, d1, h0, h1, w0, w1;        // input box
+    int32_t od0, oh0, ow0, cd, ch, cw;      // reaching windows: [od0, od0+cd) x ...
+    int32_t n, nw;                          // box elements, reaching windows
+    bool full;                              // whole rows and slices: one span
+};
+
+__device__ __forceinline__ BTile btile_at(const BwdPlan &p, int64_t t)
+{
+    const Axis &A = p.g.ax[0], &B = p.g.ax[1], &Cw = p.g.ax[2];
+    BTile b;
+    int64_t q = t;
+    const int32_t tw = (int32_t)(q % p.ntw); q /= p.ntw;
+    const int32_t th = (int32_t)(q % p.nth); q /= p.nth;
+    const int32_t td = (int32_t)(q % p.ntd);
+    b.plane = q / p.ntd;
+    b.d0 = td * p.td; b.d1 = min(b.d0 + p.td, A.X);
+    b.h0 = th * p.th; b.h1 = min(b.h0 + p.th, B.X);
+    b.w0 = tw * p.tw; b.w1 = min(b.w0 + p.tw, Cw.X);
+    b.n = (b.d1 - b.d0) * (b.h1 - b.h0) * (b.w1 - b.w0);
+    b.full = (b.h1 - b.h0 == B.X) && (b.w1 - b.w0 == Cw.X);
+    b.od0 = A.first_reaching(b.d0);
+    b.oh0 = B.first_reaching(b.h0);
+    b.ow0 = Cw.first_reaching(b.w0);
+    b.cd = max(A.last_starting(b.d1 - 1) + 1 - b.od0, 0);
+    b.ch = max(B.last_starting(b.h1 - 1) + 1 - b.oh0, 0);
+    b.cw = max(Cw.last_starting(b.w1 - 1) + 1 - b.ow0, 0);
+    b.nw = b.cd * b.ch * b.cw;
+    return b;
+}
+
+// Issue the loads of one round of (idx, gy) pairs of tile b; i = INT_MIN
+// marks an empty slot.  Decoding waits until the values are needed.
+template <typename T>
+__device__ __forceinline__ void fetch_round(const BwdPlan &p, const BTile &b, int32_t round,
+                                            const typename T::raw *__restrict__ gy,
+                                            const int32_t *__restrict__ idx,
+                                            int32_t (&ri)[kRound], typename T::raw (&rg)[kRound])
+{
+    const int64_t obase = b.plane * (int64_t)p.g.out_plane;
+    const int32_t OH = p.g.ax[1].O, OW = p.g.ax[2].O;
+#pragma unroll
+    for (int k = 0; k < kRound; ++k) {
+        const int32_t e = (round * kRound + k) * kBlock + (int32_t)threadIdx.x;
+        ri[k] = INT32_MIN;
+        if (e < b.nw) {
+            const int32_t owl = e % b.cw, r = e / b.cw, ohl = r % b.ch, odl = r / b.ch;
+            const int64_t o = obase + ((b.od0 + odl) * OH + b.oh0 + ohl) * OW + b.ow0 + owl;
+            ri[k] = idx[o];
+            rg[k] = gy[o];
+        }
+    }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(kBlock)
 bwd_tile_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
                 typename T::raw *__restrict__ gx, BwdPlan p)
 {
+    using R = typename T::raw;
+    constexpr int VE = 16 / (int)sizeof(R);   // gx elements per 16-byte store
     extern __shared__ __align__(16) float acc[];
-    const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
-    const int32_t D = A.X, H = B.X, W = Cw.X;
-    for (int64_t t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
-        int64_t q = t;
-        const int32_t tw = (int32_t)(q % p.ntw); q /= p.ntw;
-        const int32_t th = (int32_t)(q % p.nth); q /= p.nth;
-        const int32_t td = (int32_t)(q % p.ntd);
-        const int64_t plane = q / p.ntd;
-        const int32_t d0 = td * p.td, d1 = min(d0 + p.td, D);
-        const int32_t h0 = th * p.th, h1 = min(h0 + p.th, H);
-        const int32_t w0 = tw * p.tw, w1 = min(w0 + p.tw, W);
-        const int32_t ld = d1 - d0, lh = h1 - h0, lw = w1 - w0;
-        const int32_t n = ld * lh * lw;
-        const bool full = (lh == H && lw == W);
+    const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X;
+    const int32_t tid = threadIdx.x;
+    const int64_t first = xcd_local_block(blockIdx.x, gridDim.x);
 
-        for (int32_t e = threadIdx.x; e < n; e += kBlock) acc[e] = 0.0f;
+    // The workgroup is persistent: round 0 of the next tile's (idx, gy)
+    // loads is issued before this tile's store phase.
+    int32_t ri[kRound];
+    R rg[kRound];
+    if (first < p.ntiles) fetch_round<T>(p, btile_at(p, first), 0, gy, idx, ri, rg);
+
+    for (int64_t t = first; t < p.ntiles; t += gridDim.x) {
+        const BTile b = btile_at(p, t);
+        const int32_t lh = b.h1 - b.h0, lw = b.w1 - b.w0;
+        R *gp = gx + b.plane * (int64_t)p.g.in_plane;
+        R *dst = gp + b.d0 * H * W;                 // the box, when rows are whole
+
+        // the accumulator is shifted so that its element e and dst[e] share
+        // their alignment: whole 16-byte gx vectors map to aligned LDS reads
+        const int32_t mis = (int32_t)(((uintptr_t)dst / sizeof(R)) % VE);
+        const int32_t head = b.full ? min((VE - mis) % VE, b.n) : 0;
+        const int32_t shift = (4 - head % 4) % 4;
+        float *a = acc + shift;
+        const int32_t ibase = b.d0 * H * W;
+
+        for (int32_t e = tid; e < b.n + shift; e += kBlock) acc[e] = 0.0f;   // zero fill
         __syncthreads();
-
-        // windows that can reach the box along each axis
-        const int32_t od0 = A.first_reaching(d0), od1 = A.last_starting(d1 - 1) + 1;
-        const int32_t oh0 = B.first_reaching(h0), oh1 = B.last_starting(h1 - 1) + 1;
-        const int32_t ow0 = Cw.first_reaching(w0), ow1 = Cw.last_starting(w1 - 1) + 1;
-        if (od0 < od1 && oh0 < oh1 && ow0 < ow1) {
-            const int32_t cd = od1 - od0, ch = oh1 - oh0, cw = ow1 - ow0;
-            const int32_t nw = cd * ch * cw;
-            const int64_t obase = plane * (int64_t)p.g.out_plane;
-            const int32_t ibase = d0 * H * W;
-            for (int32_t e = threadIdx.x; e < nw; e += kBlock) {
-                const int32_t owl = e % cw, r = e / cw, ohl = r % ch, odl = r / ch;
-                const int64_t o = obase + ((od0 + odl) * B.O + oh0 + ohl) * Cw.O + ow0 + owl;
-                const int32_t i = idx[o];
+        for (int32_t round = 0;; ++round) {
+#pragma unroll
+            for (int k = 0; k < kRound; ++k) {
+                const int32_t i = ri[k];
                 int32_t loc = -1;
-                if (full) {
-                    const int32_t l = i - ibase;
-                    if ((uint32_t)l < (uint32_t)n) loc = l;
+                if (b.full) {
+                    const uint32_t l = (uint32_t)i - (uint32_t)ibase;
+                    if (i != INT32_MIN && l < (uint32_t)b.n) loc = (int32_t)l;
                 } else if ((uint32_t)i < (uint32_t)p.g.in_plane) {
                     const int32_t d = i / (H * W), rem = i - d * H * W;
                     const int32_t h = rem / W, w = rem - h * W;
-                    if (d >= d0 && d < d1 && h >= h0 && h < h1 && w >= w0 && w < w1)
-                        loc = ((d - d0) * lh + (h - h0)) * lw + (w - w0);
+                    if (d >= b.d0 && d < b.d1 && h >= b.h0 && h < b.h1 && w >= b.w0 && w < b.w1)
+                        loc = ((d - b.d0) * lh + (h - b.h0)) * lw + (w - b.w0);
                 }
-                if (loc >= 0) atomicAdd(&acc[loc], T::widen(gy[o]));
+                if (loc >= 0) atomicAdd(&a[loc], T::widen(rg[k]));   // ds_add_f32 scatter
             }
+            if ((round + 1) * kRound * kBlock >= b.nw) break;
+            fetch_round<T>(p, b, round + 1, gy, idx, ri, rg);
         }
         __syncthreads();
+        if (t + gridDim.x < p.ntiles) fetch_round<T>(p, btile_at(p, t + gridDim.x), 0, gy, idx, ri, rg);
 
-        typename T::raw *gp = gx + plane * (int64_t)p.g.in_plane;
-        if (full) {
-            typename T::raw *dst = gp + d0 * H * W;
-            for (int32_t e = threadIdx.x; e < n; e += kBlock) dst[e] = T::narrow(acc[e]);
+        // one rounding store per gx element
+        if (b.full) {
+            const int32_t nvec = (b.n - head) / VE;
+            const int32_t tail0 = head + nvec * VE;
+            if (tid < head) dst[tid] = T::narrow(a[tid]);
+            u32x4 *vd = reinterpret_cast<u32x4 *>(dst + head);
+            for (int32_t i = tid; i < nvec; i += kBlock) vd[i] = pack16<T>(a + head + i * VE);
+            if (tid < b.n - tail0) dst[tail0 + tid] = T::narrow(a[tail0 + tid]);
         } else {
-            for (int32_t e = threadIdx.x; e < n; e += kBlock) {
+            for (int32_t e = tid; e < b.n; e += kBlock) {
                 const int32_t w = e % lw, r = e / lw, h = r % lh, d = r / lh;
-                gp[((d0 + d) * H + h0 + h) * W + w0 + w] = T::narrow(acc[e]);
+                gp[((b.d0 + d) * H + b.h0 + h) * W + b.w0 + w] = T::narrow(a[e]);
             }
         }
         __syncthreads();   // LDS is reused by the next tile
@@ -118,7 +212,13 @@ hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
                                 const BwdPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
-    const int64_t grid = p.ntiles < (1 << 24) ? p.ntiles : (1 << 24);
+    // persistent: as many workgroups as can be resident at once
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_tile_kernel<T>, kBlock,
+                                                     p.lds_bytes) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)per_cu * device_cus());
+    if (grid >= 64) grid &= ~(int64_t)7;    // a multiple of 8 lets blocks map per XCD
     hipLaunchKernelGGL(bwd_tile_kernel<T>, dim3((uint32_t)grid), dim3(kBlock),
                        p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
     return hipGetLastError();

@@ -13,11 +13,26 @@
 
 namespace mp3d {
 
+// A 16-byte vector as a native LLVM vector (keeps loaded data in registers;
+// the HIP uint4 struct is copied through memory when assigned under a branch)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 struct F32 {
     using raw = float;
     static constexpr int code = 0;
+    // narrowing a widened value gives back its exact bits, NaN included
+    static constexpr bool exact_nan = true;
     __device__ static inline float widen(float r) { return r; }
     __device__ static inline float narrow(float f) { return f; }
+    __device__ static inline float back(float f) { return f; }
+    // the four elements of a 16-byte vector
+    // (elements are copied out before the bit cast: this clang reads lane 0
+    // for __builtin_bit_cast applied directly to an ext_vector element)
+    __device__ static inline void unpack(u32x4 q, float *v) {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(float, w[i]);
+    }
 };
 
 struct F16 {
@@ -31,6 +46,19 @@ struct F16 {
         if (f != f)
             return (uint16_t)(((u >> 16) & 0x8000u) | 0x7e00u | ((u & 0x7fffffu) >> 13));
         return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32, RNE
+    }
+    // exact for every widened value except NaN, whose payload may change
+    static constexpr bool exact_nan = false;
+    __device__ static inline uint16_t back(float f) {
+        return __builtin_bit_cast(uint16_t, (_Float16)f);
+    }
+    __device__ static inline void unpack(u32x4 q, float *v) {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = widen((uint16_t)(w[i] & 0xffffu));
+            v[2 * i + 1] = widen((uint16_t)(w[i] >> 16));
+        }
     }
 };
 
@@ -47,6 +75,19 @@ struct BF16 {
         // add half an ulp of the result, minus one unless the kept lsb is 1
         u += 0x7fffu + ((u >> 16) & 1u);
         return (uint16_t)(u >> 16);
+    }
+    // widening is a shift, so the top half is the original pattern
+    static constexpr bool exact_nan = true;
+    __device__ static inline uint16_t back(float f) {
+        return (uint16_t)(__builtin_bit_cast(uint32_t, f) >> 16);
+    }
+    __device__ static inline void unpack(u32x4 q, float *v) {
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+            v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        }
     }
 };
 

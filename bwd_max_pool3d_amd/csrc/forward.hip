@@ -15,6 +15,8 @@
 //
 // fwd_direct: one thread per output reading its window straight from
 // global memory; used only when no single window's box fits in LDS.
+#include <algorithm>
+
 #include "dtype.hpp"
 #include "kernels.hpp"
 
@@ -22,38 +24,192 @@ namespace mp3d {
 
 namespace {
 
-__device__ inline bool better(float v, float best) {
+// Blocks are dealt to the 8 XCDs round-robin by block id; renumber them so
+// that each XCD walks one contiguous run of tiles (neighbouring tiles share
+// halo rows through that XCD's L2).
+__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks)
+{
+    if (nblocks % 8u) return b;
+    return (b % 8u) * (nblocks / 8u) + b / 8u;
+}
+
+__device__ __forceinline__ bool better(float v, float best) {
     return v > best || (v != v && best == best);
 }
 
-// Copy `count` elements from global `src` to LDS `dst`, where dst and src
-// agree modulo 16 bytes: the unaligned head and tail go element by
-// element, the body in 16-byte vectors with four loads in flight per
-// thread before their LDS stores.
+constexpr int kPrefetch = 16;   // 16-byte vectors per thread carried between tiles
+
+// A tile: a block of outputs of one plane and the input box under it.
+struct Tile {
+    int64_t plane;
+    int32_t od0, od1, oh0, oh1, ow0, ow1;   // outputs [od0, od1) x ...
+    int32_t bd0, bd1, bh0, bh1, bw0, bw1;   // input box [bd0, bd1) x ...
+};
+
+__device__ __forceinline__ Tile tile_at(const FwdPlan &p, int64_t t)
+{
+    const Axis &A = p.g.ax[0], &B = p.g.ax[1], &Cw = p.g.ax[2];
+    Tile r;
+    int64_t q = t;
+    const int32_t tw = (int32_t)(q % p.ntw); q /= p.ntw;
+    const int32_t th = (int32_t)(q % p.nth); q /= p.nth;
+    const int32_t td = (int32_t)(q % p.ntd);
+    r.plane = q / p.ntd;
+    r.od0 = td * p.tod; r.od1 = min(r.od0 + p.tod, A.O);
+    r.oh0 = th * p.toh; r.oh1 = min(r.oh0 + p.toh, B.O);
+    r.ow0 = tw * p.tow; r.ow1 = min(r.ow0 + p.tow, Cw.O);
+    r.bd0 = A.start(r.od0); r.bd1 = A.end(r.od1 - 1);
+    r.bh0 = p.full_h ? 0 : B.start(r.oh0); r.bh1 = p.full_h ? B.X : B.end(r.oh1 - 1);
+    r.bw0 = p.full_w ? 0 : Cw.start(r.ow0); r.bw1 = p.full_w ? Cw.X : Cw.end(r.ow1 - 1);
+    return r;
+}
+
+// A contiguous span of x split into an unaligned head, whole 16-byte
+// vectors, and a tail.  The LDS copy starts at the same address modulo 16,
+// so the vectors land aligned.
+struct SpanShape {
+    int32_t head, nvec, tail0, count;
+};
+
 template <typename R>
-__device__ inline void copy_span(R *dst, const R *__restrict__ src, int32_t count) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ SpanShape span_shape(const R *src, int32_t count)
+{
+    SpanShape s;
     const uintptr_t a = (uintptr_t)src;
-    int32_t head = (int32_t)(((16u - (a & 15u)) & 15u) / sizeof(R));
-    if (head > count) head = count;
-    const int32_t nvec = (int32_t)(((int64_t)(count - head) * (int32_t)sizeof(R)) / 16);
-    const int32_t tail0 = head + nvec * (int32_t)(16 / sizeof(R));
-    if (tid < head) dst[tid] = src[tid];
-    const uint4 *vs = reinterpret_cast<const uint4 *>(src + head);
-    uint4 *vd = reinterpret_cast<uint4 *>(dst + head);
-    int32_t i = tid;
-    for (; i + 3 * kBlock < nvec; i += 4 * kBlock) {
-        uint4 a0 = vs[i];
-        uint4 a1 = vs[i + kBlock];
-        uint4 a2 = vs[i + 2 * kBlock];
-        uint4 a3 = vs[i + 3 * kBlock];
-        vd[i] = a0;
-        vd[i + kBlock] = a1;
-        vd[i + 2 * kBlock] = a2;
-        vd[i + 3 * kBlock] = a3;
+    s.head = min((int32_t)(((16u - (a & 15u)) & 15u) / sizeof(R)), count);
+    s.nvec = (int32_t)(((int64_t)(count - s.head) * (int32_t)sizeof(R)) / 16);
+    s.tail0 = s.head + s.nvec * (int32_t)(16 / sizeof(R));
+    s.count = count;
+    return s;
+}
+
+// Registers holding one tile's span between its load and its LDS store.
+template <typename R>
+struct SpanRegs {
+    u32x4 v[kPrefetch];
+    R head, tail;
+};
+
+template <typename R>
+__device__ __forceinline__ void span_fetch(SpanRegs<R> &r, const R *__restrict__ src, const SpanShape &s)
+{
+    const int tid = threadIdx.x;
+    const u32x4 *vs = reinterpret_cast<const u32x4 *>(src + s.head);
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+        const int32_t i = k * kBlock + tid;
+        if (i < s.nvec) r.v[k] = vs[i];
     }
-    for (; i < nvec; i += kBlock) vd[i] = vs[i];
-    if (tid < count - tail0) dst[tail0 + tid] = src[tail0 + tid];
+    if (tid < s.head) r.head = src[tid];
+    if (tid < s.count - s.tail0) r.tail = src[s.tail0 + tid];
+}
+
+template <typename R>
+__device__ __forceinline__ void span_put(const SpanRegs<R> &r, R *dst, const SpanShape &s)
+{
+    const int tid = threadIdx.x;
+    u32x4 *vd = reinterpret_cast<u32x4 *>(dst + s.head);
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+        const int32_t i = k * kBlock + tid;
+        if (i < s.nvec) vd[i] = r.v[k];
+    }
+    if (tid < s.head) dst[tid] = r.head;
+    if (tid < s.count - s.tail0) dst[s.tail0 + tid] = r.tail;
+}
+
+// Window bounds of the tile's outputs, per axis, into the LDS table.
+__device__ __forceinline__ void write_table(int2 *tab, const FwdPlan &p, const Tile &tl)
+{
+    const Axis &A = p.g.ax[0], &B = p.g.ax[1], &Cw = p.g.ax[2];
+    const int32_t ntab = p.tod + p.toh + p.tow;
+    for (int32_t j = threadIdx.x; j < ntab; j += kBlock) {
+        int2 v = make_int2(0, 0);
+        if (j < p.tod) {
+            const int32_t o = tl.od0 + j;
+            if (o < tl.od1) v = make_int2(A.start(o), A.end(o));
+        } else if (j < p.tod + p.toh) {
+            const int32_t o = tl.oh0 + j - p.tod;
+            if (o < tl.oh1) v = make_int2(B.start(o), B.end(o));
+        } else {
+            const int32_t o = tl.ow0 + j - p.tod - p.toh;
+            if (o < tl.ow1) v = make_int2(Cw.start(o), Cw.end(o));
+        }
+        tab[j] = v;
+    }
+}
+
+// Reduce every window of the tile out of its LDS box.
+//  stage B: for every box row and output column, the first maximum of the
+//           row over that column's window (value, column) -> LDS;
+//  stage C: every output combines the row partials of its window's (d, h)
+//           rows in ascending order, then stores y (the element's own
+//           bits, read back from the box) and idx.
+template <typename T>
+__device__ __forceinline__ void reduce_tile(const FwdPlan &p, const Tile &tl, const int2 *tab,
+                                   const typename T::raw *box, float *pv, int32_t *pw,
+                                   typename T::raw *__restrict__ y, int32_t *__restrict__ idx)
+{
+    const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X, OH = p.g.ax[1].O, OW = p.g.ax[2].O;
+    const int32_t tid = threadIdx.x;
+    const int32_t lh = tl.bh1 - tl.bh0, lw = tl.bw1 - tl.bw0;
+    const int32_t cd = tl.od1 - tl.od0, ch = tl.oh1 - tl.oh0, cw = tl.ow1 - tl.ow0;
+    const int32_t nrow = (tl.bd1 - tl.bd0) * lh;
+
+    for (int32_t ob = 0; ob < cw; ob += kBlock) {
+        const int32_t cwb = min(cw - ob, kBlock);
+        const int32_t owl = ob + tid % cwb, rstep = kBlock / cwb;
+        if (tid < rstep * cwb) {
+            const int2 ww = tab[p.tod + p.toh + owl];
+            for (int32_t r = tid / cwb; r < nrow; r += rstep) {
+                const int32_t rb = r * lw - tl.bw0;
+                float best = T::widen(box[rb + ww.x]);
+                int32_t bw = ww.x;
+#pragma unroll 4
+                for (int32_t w = ww.x + 1; w < ww.y; ++w) {
+                    const float v = T::widen(box[rb + w]);
+                    if (better(v, best)) {
+                        best = v;
+                        bw = w;
+                    }
+                }
+                pv[r * cw + owl] = best;
+                pw[r * cw + owl] = bw;
+            }
+        }
+    }
+    __syncthreads();
+
+    const int64_t obase = tl.plane * (int64_t)p.g.out_plane;
+    for (int32_t ob = 0; ob < cw; ob += kBlock) {
+        const int32_t cwb = min(cw - ob, kBlock);
+        const int32_t owl = ob + tid % cwb, qstep = kBlock / cwb;
+        if (tid < qstep * cwb) {
+            for (int32_t qq = tid / cwb; qq < cd * ch; qq += qstep) {
+                const int32_t odl = qq / ch, ohl = qq - odl * ch;
+                const int2 wd = tab[odl], wh = tab[p.tod + ohl];
+                float best = pv[((wd.x - tl.bd0) * lh + (wh.x - tl.bh0)) * cw + owl];
+                int32_t bd = wd.x, bh = wh.x;
+                for (int32_t d = wd.x; d < wd.y; ++d) {
+                    const int32_t r0 = (d - tl.bd0) * lh - tl.bh0;
+#pragma unroll 4
+                    for (int32_t h = wh.x; h < wh.y; ++h) {
+                        const float v = pv[(r0 + h) * cw + owl];
+                        if (better(v, best)) {
+                            best = v;
+                            bd = d;
+                            bh = h;
+                        }
+                    }
+                }
+                const int32_t rr = (bd - tl.bd0) * lh + (bh - tl.bh0);
+                const int32_t bw = pw[rr * cw + owl];
+                const int64_t o = obase + ((tl.od0 + odl) * OH + tl.oh0 + ohl) * OW + tl.ow0 + owl;
+                y[o] = box[rr * lw + bw - tl.bw0];
+                idx[o] = (bd * H + bh) * W + bw;
+            }
+        }
+    }
 }
 
 template <typename T>
@@ -63,88 +219,55 @@ fwd_tile_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restri
 {
     using R = typename T::raw;
     extern __shared__ __align__(16) unsigned char smem[];
-    const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
-    const int32_t H = B.X, W = Cw.X;
-    const int32_t ntab = p.tod + p.toh + p.tow;
+    const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X;
+    // LDS: window table | row partials (value, column) | input box
     int2 *tab = reinterpret_cast<int2 *>(smem);
-    unsigned char *boxbase = smem + ((ntab * (int)sizeof(int2) + 15) & ~15);
+    float *pv = reinterpret_cast<float *>(smem + p.tab_bytes);
+    int32_t *pw = reinterpret_cast<int32_t *>(smem + p.tab_bytes + p.part_bytes);
+    unsigned char *boxbase = smem + p.tab_bytes + 2 * p.part_bytes;
+    const int64_t first = xcd_local_block(blockIdx.x, gridDim.x);
 
-    for (int64_t t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
-        int64_t q = t;
-        const int32_t tw = (int32_t)(q % p.ntw); q /= p.ntw;
-        const int32_t th = (int32_t)(q % p.nth); q /= p.nth;
-        const int32_t td = (int32_t)(q % p.ntd);
-        const int64_t plane = q / p.ntd;
-        const int32_t od0 = td * p.tod, od1 = min(od0 + p.tod, A.O);
-        const int32_t oh0 = th * p.toh, oh1 = min(oh0 + p.toh, B.O);
-        const int32_t ow0 = tw * p.tow, ow1 = min(ow0 + p.tow, Cw.O);
-        const int32_t bd0 = A.start(od0), bd1 = A.end(od1 - 1);
-        const int32_t bh0 = p.full_h ? 0 : B.start(oh0);
-        const int32_t bh1 = p.full_h ? H : B.end(oh1 - 1);
-        const int32_t bw0 = p.full_w ? 0 : Cw.start(ow0);
-        const int32_t bw1 = p.full_w ? W : Cw.end(ow1 - 1);
-        const int32_t ld = bd1 - bd0, lh = bh1 - bh0, lw = bw1 - bw0;
-        const R *xp = x + plane * (int64_t)p.g.in_plane;
-
-        R *box;
-        if (p.full_h && p.full_w) {
-            const R *src = xp + bd0 * H * W;
-            box = reinterpret_cast<R *>(boxbase + ((uintptr_t)src & 15u));
-            copy_span(box, src, ld * H * W);
-        } else {
-            box = reinterpret_cast<R *>(boxbase);
-            const int32_t n = ld * lh * lw;
+    if (p.full_h && p.full_w) {
+        // Boxes are whole slices, one contiguous span of the plane.  The
+        // workgroup is persistent and pipelined: the next tile's span is
+        // in flight in registers while the current tile is reduced.
+        SpanRegs<R> regs;
+        if (first < p.ntiles) {
+            const Tile tl = tile_at(p, first);
+            const R *src = x + tl.plane * (int64_t)p.g.in_plane + tl.bd0 * H * W;
+            span_fetch(regs, src, span_shape(src, (tl.bd1 - tl.bd0) * H * W));
+        }
+        for (int64_t t = first; t < p.ntiles; t += gridDim.x) {
+            const Tile tl = tile_at(p, t);
+            const R *src = x + tl.plane * (int64_t)p.g.in_plane + tl.bd0 * H * W;
+            R *box = reinterpret_cast<R *>(boxbase + ((uintptr_t)src & 15u));
+            span_put(regs, box, span_shape(src, (tl.bd1 - tl.bd0) * H * W));
+            write_table(tab, p, tl);
+            __syncthreads();
+            if (t + gridDim.x < p.ntiles) {
+                const Tile nx = tile_at(p, t + gridDim.x);
+                const R *ns = x + nx.plane * (int64_t)p.g.in_plane + nx.bd0 * H * W;
+                span_fetch(regs, ns, span_shape(ns, (nx.bd1 - nx.bd0) * H * W));
+            }
+            reduce_tile<T>(p, tl, tab, box, pv, pw, y, idx);
+            __syncthreads();   // LDS is reused by the next tile
+        }
+    } else {
+        for (int64_t t = first; t < p.ntiles; t += gridDim.x) {
+            const Tile tl = tile_at(p, t);
+            const R *xp = x + tl.plane * (int64_t)p.g.in_plane;
+            R *box = reinterpret_cast<R *>(boxbase);
+            const int32_t lh = tl.bh1 - tl.bh0, lw = tl.bw1 - tl.bw0;
+            const int32_t n = (tl.bd1 - tl.bd0) * lh * lw;
             for (int32_t e = threadIdx.x; e < n; e += kBlock) {
                 const int32_t w = e % lw, r = e / lw, h = r % lh, d = r / lh;
-                box[e] = xp[((bd0 + d) * H + bh0 + h) * W + bw0 + w];
+                box[e] = xp[((tl.bd0 + d) * H + tl.bh0 + h) * W + tl.bw0 + w];
             }
+            write_table(tab, p, tl);
+            __syncthreads();
+            reduce_tile<T>(p, tl, tab, box, pv, pw, y, idx);
+            __syncthreads();
         }
-        for (int32_t j = threadIdx.x; j < ntab; j += kBlock) {
-            int2 v = make_int2(0, 0);
-            if (j < p.tod) {
-                const int32_t o = od0 + j;
-                if (o < od1) v = make_int2(A.start(o), A.end(o));
-            } else if (j < p.tod + p.toh) {
-                const int32_t o = oh0 + j - p.tod;
-                if (o < oh1) v = make_int2(B.start(o), B.end(o));
-            } else {
-                const int32_t o = ow0 + j - p.tod - p.toh;
-                if (o < ow1) v = make_int2(Cw.start(o), Cw.end(o));
-            }
-            tab[j] = v;
-        }
-        __syncthreads();
-
-        const int32_t cd = od1 - od0, ch = oh1 - oh0, cw = ow1 - ow0;
-        const int32_t nout = cd * ch * cw;
-        const int64_t obase = plane * (int64_t)p.g.out_plane;
-        for (int32_t e = threadIdx.x; e < nout; e += kBlock) {
-            const int32_t owl = e % cw, r = e / cw, ohl = r % ch, odl = r / ch;
-            const int2 wd = tab[odl], wh = tab[p.tod + ohl], ww = tab[p.tod + p.toh + owl];
-            int32_t rb = ((wd.x - bd0) * lh + (wh.x - bh0)) * lw - bw0;
-            R rbest = box[rb + ww.x];
-            float best = T::widen(rbest);
-            int32_t pbest = (wd.x * H + wh.x) * W + ww.x;
-            for (int32_t d = wd.x; d < wd.y; ++d) {
-                for (int32_t h = wh.x; h < wh.y; ++h) {
-                    const int32_t rowl = ((d - bd0) * lh + (h - bh0)) * lw - bw0;
-                    const int32_t rowp = (d * H + h) * W;
-                    for (int32_t w = ww.x; w < ww.y; ++w) {
-                        const R rv = box[rowl + w];
-                        const float v = T::widen(rv);
-                        if (better(v, best)) {
-                            best = v;
-                            rbest = rv;
-                            pbest = rowp + w;
-                        }
-                    }
-                }
-            }
-            const int64_t o = obase + ((od0 + odl) * B.O + oh0 + ohl) * Cw.O + ow0 + owl;
-            y[o] = rbest;
-            idx[o] = pbest;
-        }
-        __syncthreads();   // LDS is reused by the next tile
     }
 }
 
@@ -194,7 +317,13 @@ hipError_t launch_forward_tile(const void *x, void *y, int32_t *idx,
                                const FwdPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
-    const int64_t grid = p.ntiles < (1 << 24) ? p.ntiles : (1 << 24);
+    // persistent: as many workgroups as can be resident at once
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd_tile_kernel<T>, kBlock,
+                                                     p.lds_bytes) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)per_cu * device_cus());
+    if (grid >= 64) grid &= ~(int64_t)7;    // a multiple of 8 lets blocks map per XCD
     hipLaunchKernelGGL(fwd_tile_kernel<T>, dim3((uint32_t)grid), dim3(kBlock),
                        p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();

@@ -21,6 +21,8 @@ struct FwdPlan {
     int32_t ntd, nth, ntw;     // tiles per axis
     int32_t full_h, full_w;    // box spans whole rows / whole slices
     int64_t ntiles;            // planes * ntd * nth * ntw
+    uint32_t tab_bytes;        // LDS: window table, 16-byte aligned
+    uint32_t part_bytes;       // LDS: each of the two row-partial arrays
     uint32_t lds_bytes;        // dynamic LDS per workgroup
 };
 
@@ -42,14 +44,49 @@ struct GatherPlan {
     int32_t qd, qh, qw;
 };
 
+// Forward with compile-time window shape: one thread per V consecutive
+// outputs of a row, input rows loaded straight into registers.
+struct FixedPlan {
+    static constexpr int V = 4;
+    Geom g;
+    FastDiv groups, oh, od;    // divide by G, OH, OD
+    int32_t G;                 // thread groups per output row: ceil(OW / V)
+    uint32_t nthreads;         // planes * OD * OH * G
+    int32_t vec_store;         // outputs may be stored as 4-wide vectors
+};
+
+// Forward by axis: D-reduce in registers from coalesced column loads, then
+// an H*W reduce out of LDS.  One workgroup per (plane, run of tod output
+// slices).
+struct ColPlan {
+    Geom g;
+    int32_t tod, ntd;          // output slices per tile, tiles per plane
+    FastDiv ntd_div, ow_div, oh_div;
+    uint32_t ntiles;           // planes * ntd
+    int32_t maxkd;             // widest window along D
+    uint32_t tab_bytes, pv_bytes, lds_bytes;
+};
+
 size_t lds_limit();
+int device_cus();      // compute units of the current device
+
+bool fixed_shape_supported(const Geom &g);
+bool plan_fixed(const Geom &g, int elem_bytes, const void *x, const void *y,
+                const void *idx, FixedPlan *p);
 
 bool plan_forward(const Geom &g, int elem_bytes, FwdPlan *p);
+bool plan_col(const Geom &g, int elem_bytes, const void *x, ColPlan *p);
 bool plan_backward(const Geom &g, BwdPlan *p);
 
 template <typename T>
 hipError_t launch_forward_tile(const void *x, void *y, int32_t *idx,
                                const FwdPlan &p, hipStream_t s);
+template <typename T>
+hipError_t launch_forward_fixed(const void *x, void *y, int32_t *idx,
+                                const FixedPlan &p, hipStream_t s);
+template <typename T>
+hipError_t launch_forward_col(const void *x, void *y, int32_t *idx,
+                              const ColPlan &p, hipStream_t s);
 template <typename T>
 hipError_t launch_forward_direct(const void *x, void *y, int32_t *idx,
                                  const Geom &g, hipStream_t s);

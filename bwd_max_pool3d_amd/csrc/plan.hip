@@ -16,8 +16,8 @@ namespace mp3d {
 
 namespace {
 
-constexpr int64_t kLdsCap = 64 * 1024;     // LDS per workgroup, all uses
-constexpr int64_t kBoxBudget = 60 * 1024;   // of which the forward's input box
+constexpr int64_t kLdsCap = 64 * 1024;     // forward LDS per workgroup, all uses
+constexpr int64_t kAccBudget = 40 * 1024;   // backward accumulator per workgroup
 constexpr int64_t kWantTiles = 1024;        // >= 4 workgroups per CU
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -38,53 +38,68 @@ int64_t box_extent(const Axis &a, int32_t t)
     return m;
 }
 
-// Largest t (1..O) with box_extent(a, t) * unit <= budget, or 0.
-int32_t fit_tile(const Axis &a, int64_t unit, int64_t budget)
-{
-    int32_t best = 0;
-    const int32_t cap = std::min<int32_t>(a.O, 4096);
-    for (int32_t t = 1; t <= cap; ++t) {
-        if (box_extent(a, t) * unit <= budget) best = t;
-        else break;
-    }
-    return best;
-}
-
 // Even out tiles: the smallest tile size giving the same tile count.
 int32_t balance(int32_t O, int32_t t) { return (int32_t)cdiv(O, cdiv(O, t)); }
 
 }  // namespace
 
+// LDS bytes of a forward tile of tod x toh x tow outputs: window table,
+// two row-partial arrays (value, column) and the input box plus 16 bytes of
+// alignment slack.
+static int64_t fwd_lds(const Geom &g, int es, int32_t tod, int32_t toh, int32_t tow,
+                       bool full_h, bool full_w, int64_t *tab, int64_t *part)
+{
+    const Axis &A = g.ax[0], &B = g.ax[1], &Cw = g.ax[2];
+    const int64_t ld = box_extent(A, tod);
+    const int64_t lh = full_h ? B.X : box_extent(B, toh);
+    const int64_t lw = full_w ? Cw.X : box_extent(Cw, tow);
+    *tab = ((int64_t)(tod + toh + tow) * 8 + 15) & ~(int64_t)15;
+    *part = ((ld * lh * tow * 4) + 15) & ~(int64_t)15;
+    return *tab + 2 * *part + 16 + ld * lh * lw * es;
+}
+
 bool plan_forward(const Geom &g, int es, FwdPlan *p)
 {
     const Axis &A = g.ax[0], &B = g.ax[1], &Cw = g.ax[2];
-    const int64_t H = B.X, W = Cw.X;
     const int64_t cap = std::min<int64_t>(kLdsCap, (int64_t)lds_limit());
-    const int64_t budget = std::min<int64_t>(kBoxBudget, cap - 4096);
+    int64_t tab = 0, part = 0;
     p->g = g;
     int32_t tod = 0, toh = B.O, tow = Cw.O;
-    int full_h = 1, full_w = 1;
-    int32_t t = fit_tile(A, H * W * es, budget);
-    if (t > 0) {
+    bool full_h = true, full_w = true;
+    // largest whole-slice tile that fits
+    for (int32_t t = 1; t <= std::min<int32_t>(A.O, 4096); ++t) {
+        if (fwd_lds(g, es, t, toh, tow, true, true, &tab, &part) <= cap) tod = t;
+        else break;
+    }
+    if (tod > 0) {
         // enough tiles to spread over the chip when there are few planes
         const int64_t per_plane = cdiv(kWantTiles, std::max<int64_t>(g.planes, 1));
         const int32_t tpar = (int32_t)std::max<int64_t>(1, A.O / per_plane);
-        tod = balance(A.O, std::min(t, tpar));
+        tod = balance(A.O, std::min(tod, tpar));
     } else {
         tod = 1;
-        full_h = 0;
-        const int64_t dext = box_extent(A, 1);
-        toh = fit_tile(B, dext * W * es, budget);
+        full_h = false;
+        toh = 0;
+        for (int32_t t = 1; t <= std::min<int32_t>(B.O, 4096); ++t) {
+            if (fwd_lds(g, es, 1, t, tow, false, true, &tab, &part) <= cap) toh = t;
+            else break;
+        }
         if (toh > 0) {
             toh = balance(B.O, toh);
         } else {
             toh = 1;
-            full_w = 0;
-            tow = fit_tile(Cw, dext * box_extent(B, 1) * es, budget);
+            full_w = false;
+            tow = 0;
+            for (int32_t t = 1; t <= std::min<int32_t>(Cw.O, 4096); ++t) {
+                if (fwd_lds(g, es, 1, 1, t, false, false, &tab, &part) <= cap) tow = t;
+                else break;
+            }
             if (tow == 0) return false;
             tow = balance(Cw.O, tow);
         }
     }
+    const int64_t lds = fwd_lds(g, es, tod, toh, tow, full_h, full_w, &tab, &part);
+    if (lds > cap) return false;
     p->tod = tod;
     p->toh = toh;
     p->tow = tow;
@@ -94,19 +109,78 @@ bool plan_forward(const Geom &g, int es, FwdPlan *p)
     p->full_h = full_h;
     p->full_w = full_w;
     p->ntiles = g.planes * p->ntd * p->nth * p->ntw;
-    const int64_t lh = full_h ? H : box_extent(B, toh);
-    const int64_t lw = full_w ? W : box_extent(Cw, tow);
-    const int64_t box = box_extent(A, tod) * lh * lw * es;
-    const int64_t tab = ((int64_t)(tod + toh + tow) * 8 + 15) & ~(int64_t)15;
-    if (tab + 16 + box > cap) return false;   // e.g. O far above X: huge tables
-    p->lds_bytes = (uint32_t)(tab + 16 + box);
+    p->tab_bytes = (uint32_t)tab;
+    p->part_bytes = (uint32_t)part;
+    p->lds_bytes = (uint32_t)lds;
+    return true;
+}
+
+bool plan_fixed(const Geom &g, int es, const void *x, const void *y, const void *idx,
+                FixedPlan *p)
+{
+    if (!fixed_shape_supported(g)) return false;
+    const Axis &c = g.ax[2];
+    const int64_t W = c.X, V = FixedPlan::V;
+    const int64_t ve = 16 / es;                     // elements per 16-byte vector
+    const int64_t span = (V - 1) * c.s + c.k;       // input columns per thread
+    const int64_t G = cdiv(c.O, V);
+    if ((W * es) % 16 || (uintptr_t)x % 16 || (V * c.s * es) % 16) return false;
+    if ((G - 1) * V * c.s + (span / ve) * ve > W) return false;   // vectors stay in the row
+    const int64_t n = g.planes * g.ax[0].O * g.ax[1].O * G;
+    if (n >= ((int64_t)1 << 31)) return false;
+    p->g = g;
+    p->G = (int32_t)G;
+    p->groups = FastDiv((uint32_t)G);
+    p->oh = FastDiv((uint32_t)g.ax[1].O);
+    p->od = FastDiv((uint32_t)g.ax[0].O);
+    p->nthreads = (uint32_t)n;
+    p->vec_store = (c.O % V == 0) && ((uintptr_t)y % (V * es) == 0) && ((uintptr_t)idx % 16 == 0);
+    return true;
+}
+
+bool plan_col(const Geom &g, int es, const void *x, ColPlan *p)
+{
+    const Axis &A = g.ax[0], &B = g.ax[1], &Cw = g.ax[2];
+    const int64_t HW = (int64_t)B.X * Cw.X;
+    if ((HW * es) % 16 || (uintptr_t)x % 16) return false;
+    // widest window along D (all windows of a fixed axis have width k)
+    int64_t maxkd = A.k;
+    if (!A.k) {
+        if (A.O > 4096) return false;
+        for (int32_t o = 0; o < A.O; ++o) maxkd = std::max<int64_t>(maxkd, A.end(o) - A.start(o));
+    }
+    if (maxkd > 8) return false;
+    const int64_t cap = std::min<int64_t>(kLdsCap, (int64_t)lds_limit());
+    const int64_t tab = ((int64_t)(B.O + Cw.O) * 8 + 15) & ~(int64_t)15;
+    if (tab > 16 * 1024) return false;
+    const int64_t per_slice = ((HW * 4 + 15) & ~(int64_t)15) + HW;   // value + offset
+    int32_t tod = (int32_t)std::min<int64_t>(A.O, (cap - tab - 16) / per_slice);
+    if (tod < 1) return false;
+    const int64_t per_plane = cdiv(kWantTiles, std::max<int64_t>(g.planes, 1));
+    tod = std::min<int32_t>(tod, (int32_t)std::max<int64_t>(1, A.O / per_plane));
+    tod = balance(A.O, tod);
+    const int64_t ntd = cdiv(A.O, tod);
+    const int64_t ntiles = g.planes * ntd;
+    if (ntiles >= ((int64_t)1 << 31) || (int64_t)tod * B.O * Cw.O >= ((int64_t)1 << 31))
+        return false;
+    p->g = g;
+    p->tod = tod;
+    p->ntd = (int32_t)ntd;
+    p->ntd_div = FastDiv((uint32_t)ntd);
+    p->ow_div = FastDiv((uint32_t)Cw.O);
+    p->oh_div = FastDiv((uint32_t)B.O);
+    p->ntiles = (uint32_t)ntiles;
+    p->maxkd = (int32_t)maxkd;
+    p->tab_bytes = (uint32_t)tab;
+    p->pv_bytes = (uint32_t)(((int64_t)tod * HW * 4 + 15) & ~(int64_t)15);
+    p->lds_bytes = (uint32_t)(tab + p->pv_bytes + (int64_t)tod * HW);
     return true;
 }
 
 bool plan_backward(const Geom &g, BwdPlan *p)
 {
     const int32_t D = g.ax[0].X, H = g.ax[1].X, W = g.ax[2].X;
-    const int64_t budget = std::min<int64_t>(kLdsCap, (int64_t)lds_limit());
+    const int64_t budget = std::min<int64_t>(kAccBudget, (int64_t)lds_limit() - 64);
     const int64_t slice = (int64_t)H * W * 4;
     p->g = g;
     if (slice <= budget) {
@@ -131,7 +205,7 @@ bool plan_backward(const Geom &g, BwdPlan *p)
     p->nth = (int32_t)cdiv(H, p->th);
     p->ntw = (int32_t)cdiv(W, p->tw);
     p->ntiles = g.planes * p->ntd * p->nth * p->ntw;
-    p->lds_bytes = (uint32_t)((int64_t)p->td * p->th * p->tw * 4);
+    p->lds_bytes = (uint32_t)(((int64_t)p->td * p->th * p->tw + 4) * 4);   // + alignment shift
     return true;
 }
 

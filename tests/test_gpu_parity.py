@@ -43,6 +43,9 @@ CASES = [
     ((1, 2, 32, 56, 56), None, (3, 3, 3), (2, 2, 2)),
     ((1, 1, 16, 112, 112), None, (2, 2, 2), (2, 2, 2)),
     ((1, 1, 5, 5, 5), None, (5, 5, 5), (1, 1, 1)),
+    ((2, 3, 7, 9, 24), None, (3, 3, 3), (2, 2, 2)),       # partial last thread group
+    ((1, 2, 6, 6, 40), None, (2, 2, 2), (2, 2, 2)),
+    ((1, 1, 4, 4, 36), None, (2, 2, 2), (2, 2, 2)),       # rows not a multiple of 4 outputs
     ((1, 1, 7, 300, 300), None, (2, 3, 3), (2, 2, 2)),    # slices larger than LDS
     ((1, 1, 2, 1, 70000), None, (1, 1, 5), (1, 1, 3)),    # rows larger than LDS
     ((2, 1, 3, 5000, 1), (2, 777, 1), None, None),
