@@ -29,11 +29,15 @@ class Mp3dError(RuntimeError):
         self.code = code
 
 
-def load(path: str = LIBRARY) -> ctypes.CDLL:
-    """The loaded library (cached).  Raises ImportError if it is missing."""
+def load(path: str | None = None) -> ctypes.CDLL:
+    """The loaded library (cached).  Raises ImportError if it is missing.
+    ``MP3D_LIBRARY`` in the environment names another build of the same
+    library (for comparing builds); the default is the in-tree one."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = os.environ.get("MP3D_LIBRARY") or LIBRARY
     if not os.path.exists(path):
         raise ImportError(
             "libmp3d.so is not built at %s; run `python -m bwd_max_pool3d_amd._build` "

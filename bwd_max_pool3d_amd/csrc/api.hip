@@ -70,7 +70,7 @@ int set_fixed_axis(Axis *a, int64_t X, int32_t k, int32_t s, const char *name)
         return fail(MP3D_EINVAL, "kernel and stride on %s must be >= 1 (got %d, %d)", name, k, s);
     if (X < k)
         return fail(MP3D_EINVAL, "kernel %d exceeds extent %lld on %s", k, (long long)X, name);
-    *a = Axis{(int32_t)X, (int32_t)((X - k) / s + 1), k, s};
+    *a = Axis::make((int32_t)X, (int32_t)((X - k) / s + 1), k, s);
     return MP3D_OK;
 }
 
@@ -78,7 +78,7 @@ int set_adaptive_axis(Axis *a, int64_t X, int32_t O, const char *name)
 {
     if (O <= 0)
         return fail(MP3D_EINVAL, "output extent on %s must be >= 1 (got %d)", name, O);
-    *a = Axis{(int32_t)X, O, 0, 0};
+    *a = Axis::make((int32_t)X, O, 0, 0);
     return MP3D_OK;
 }
 

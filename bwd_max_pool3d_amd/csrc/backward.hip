@@ -67,11 +67,8 @@ __device__ __forceinline__ BTile btile_at(const BwdPlan &p, int64_t t)
 {
     const Axis &A = p.g.ax[0], &B = p.g.ax[1], &Cw = p.g.ax[2];
     BTile b;
-    int64_t q = t;
-    const int32_t tw = (int32_t)(q % p.ntw); q /= p.ntw;
-    const int32_t th = (int32_t)(q % p.nth); q /= p.nth;
-    const int32_t td = (int32_t)(q % p.ntd);
-    b.plane = q / p.ntd;
+    int32_t td, th, tw;
+    p.split.split(t, &b.plane, &td, &th, &tw);
     b.d0 = td * p.td; b.d1 = min(b.d0 + p.td, A.X);
     b.h0 = th * p.th; b.h1 = min(b.h0 + p.th, B.X);
     b.w0 = tw * p.tw; b.w1 = min(b.w0 + p.tw, Cw.X);
@@ -102,7 +99,18 @@ __device__ __forceinline__ void fetch_round(const BwdPlan &p, const BTile &b, in
         const int32_t e = (round * kRound + k) * kBlock + (int32_t)threadIdx.x;
         ri[k] = INT32_MIN;
         if (e < b.nw) {
-            const int32_t owl = e % b.cw, r = e / b.cw, ohl = r % b.ch, odl = r / b.ch;
+            int32_t owl, ohl, odl;
+            if (b.full) {       // cw == OW and ch == OH: divide by launch constants
+                const uint32_t r = p.ow_div.div((uint32_t)e);
+                owl = e - (int32_t)r * OW;
+                odl = (int32_t)p.oh_div.div(r);
+                ohl = (int32_t)r - odl * OH;
+            } else {
+                owl = e % b.cw;
+                const int32_t r = e / b.cw;
+                ohl = r % b.ch;
+                odl = r / b.ch;
+            }
             const int64_t o = obase + ((b.od0 + odl) * OH + b.oh0 + ohl) * OW + b.ow0 + owl;
             ri[k] = idx[o];
             rg[k] = gy[o];
@@ -142,7 +150,9 @@ bwd_tile_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
         float *a = acc + shift;
         const int32_t ibase = b.d0 * H * W;
 
-        for (int32_t e = tid; e < b.n + shift; e += kBlock) acc[e] = 0.0f;   // zero fill
+        // zero fill, 16 bytes at a time
+        for (int32_t e = tid; e < (b.n + shift + 3) / 4; e += kBlock)
+            reinterpret_cast<u32x4 *>(acc)[e] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
         for (int32_t round = 0;; ++round) {
 #pragma unroll
@@ -172,7 +182,18 @@ bwd_tile_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
             const int32_t tail0 = head + nvec * VE;
             if (tid < head) dst[tid] = T::narrow(a[tid]);
             u32x4 *vd = reinterpret_cast<u32x4 *>(dst + head);
-            for (int32_t i = tid; i < nvec; i += kBlock) vd[i] = pack16<T>(a + head + i * VE);
+            int32_t i = tid;
+            for (; i + 3 * kBlock < nvec; i += 4 * kBlock) {     // four LDS reads in flight
+                const u32x4 v0 = pack16<T>(a + head + i * VE);
+                const u32x4 v1 = pack16<T>(a + head + (i + kBlock) * VE);
+                const u32x4 v2 = pack16<T>(a + head + (i + 2 * kBlock) * VE);
+                const u32x4 v3 = pack16<T>(a + head + (i + 3 * kBlock) * VE);
+                st_stream(vd + i, v0);
+                st_stream(vd + i + kBlock, v1);
+                st_stream(vd + i + 2 * kBlock, v2);
+                st_stream(vd + i + 3 * kBlock, v3);
+            }
+            for (; i < nvec; i += kBlock) st_stream(vd + i, pack16<T>(a + head + i * VE));
             if (tid < b.n - tail0) dst[tail0 + tid] = T::narrow(a[tail0 + tid]);
         } else {
             for (int32_t e = tid; e < b.n; e += kBlock) {
@@ -212,12 +233,9 @@ hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
                                 const BwdPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
-    // persistent: as many workgroups as can be resident at once
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_tile_kernel<T>, kBlock,
-                                                     p.lds_bytes) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)per_cu * device_cus());
+    // one workgroup per tile (measured faster than a persistent grid here:
+    // the store phases of many resident workgroups overlap)
+    int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)1 << 24);
     if (grid >= 64) grid &= ~(int64_t)7;    // a multiple of 8 lets blocks map per XCD
     hipLaunchKernelGGL(bwd_tile_kernel<T>, dim3((uint32_t)grid), dim3(kBlock),
                        p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);

@@ -2,10 +2,9 @@
 // to and from binary32 on the device.
 //
 // float32 is stored as float; float16 and bfloat16 as their raw 16-bit
-// patterns.  Widening to binary32 is exact for all three.  Narrowing rounds
-// to nearest, ties to even (IEEE 754 default), keeps subnormals, overflows
-// to infinity, and turns NaN into a quiet NaN that keeps its sign and top
-// fraction bits.
+// patterns.  Widening to binary32 is exact for all three.  Narrowing uses
+// gfx950's conversion instructions: round to nearest, ties to even (IEEE
+// 754 default), subnormals kept, overflow to infinity; NaN stays a NaN.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,6 +15,15 @@ namespace mp3d {
 // A 16-byte vector as a native LLVM vector (keeps loaded data in registers;
 // the HIP uint4 struct is copied through memory when assigned under a branch)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) stores and loads: data written or read once is
+// not kept in the caches.  Output streams measured markedly faster this way.
+template <typename V>
+__device__ __forceinline__ void st_stream(V *p, V v) { __builtin_nontemporal_store(v, p); }
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V *p) { return __builtin_nontemporal_load(p); }
 
 struct F32 {
     using raw = float;
@@ -42,9 +50,6 @@ struct F16 {
         return (float)__builtin_bit_cast(_Float16, r);   // v_cvt_f32_f16, exact
     }
     __device__ static inline uint16_t narrow(float f) {
-        uint32_t u = __builtin_bit_cast(uint32_t, f);
-        if (f != f)
-            return (uint16_t)(((u >> 16) & 0x8000u) | 0x7e00u | ((u & 0x7fffffu) >> 13));
         return __builtin_bit_cast(uint16_t, (_Float16)f);  // v_cvt_f16_f32, RNE
     }
     // exact for every widened value except NaN, whose payload may change
@@ -69,12 +74,7 @@ struct BF16 {
         return __builtin_bit_cast(float, (uint32_t)r << 16);
     }
     __device__ static inline uint16_t narrow(float f) {
-        uint32_t u = __builtin_bit_cast(uint32_t, f);
-        if (f != f)
-            return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u | ((u & 0x7fffffu) >> 16));
-        // add half an ulp of the result, minus one unless the kept lsb is 1
-        u += 0x7fffu + ((u >> 16) & 1u);
-        return (uint16_t)(u >> 16);
+        return __builtin_bit_cast(uint16_t, (__bf16)f);    // v_cvt_pk_bf16_f32, RNE
     }
     // widening is a shift, so the top half is the original pattern
     static constexpr bool exact_nan = true;

@@ -50,11 +50,8 @@ __device__ __forceinline__ Tile tile_at(const FwdPlan &p, int64_t t)
 {
     const Axis &A = p.g.ax[0], &B = p.g.ax[1], &Cw = p.g.ax[2];
     Tile r;
-    int64_t q = t;
-    const int32_t tw = (int32_t)(q % p.ntw); q /= p.ntw;
-    const int32_t th = (int32_t)(q % p.nth); q /= p.nth;
-    const int32_t td = (int32_t)(q % p.ntd);
-    r.plane = q / p.ntd;
+    int32_t td, th, tw;
+    p.split.split(t, &r.plane, &td, &th, &tw);
     r.od0 = td * p.tod; r.od1 = min(r.od0 + p.tod, A.O);
     r.oh0 = th * p.toh; r.oh1 = min(r.oh0 + p.toh, B.O);
     r.ow0 = tw * p.tow; r.ow1 = min(r.ow0 + p.tow, Cw.O);

@@ -38,7 +38,7 @@ __device__ __forceinline__ void col_load(ColWin<MAXKD> &w, const R *__restrict__
 {
 #pragma unroll
     for (int j = 0; j < MAXKD; ++j)
-        if (j < n) w.q[j] = *reinterpret_cast<const u32x4 *>(col + (int64_t)j * hw);
+        if (j < n) w.q[j] = ld_stream(reinterpret_cast<const u32x4 *>(col + (int64_t)j * hw));
 }
 
 // Element-wise first maximum over the n loaded slices; writes the values
@@ -167,8 +167,8 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
             raw = T::back(best);
         else
             raw = xp[pos];            // NaN: copy the element's own bits
-        y[obase + e] = raw;
-        idx[obase + e] = pos;
+        st_stream(y + obase + e, raw);
+        st_stream(idx + obase + e, pos);
     }
 }
 

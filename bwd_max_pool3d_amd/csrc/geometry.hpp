@@ -14,31 +14,6 @@
 
 namespace mp3d {
 
-// One spatial axis: extent X split into O windows; k > 0 selects fixed
-// windows of width k and stride s, k == 0 adaptive windows.
-struct Axis {
-    int32_t X, O, k, s;
-
-    __host__ __device__ inline int32_t start(int32_t o) const {
-        return k ? o * s : (int32_t)(((int64_t)o * X) / O);
-    }
-    __host__ __device__ inline int32_t end(int32_t o) const {
-        return k ? o * s + k : (int32_t)((((int64_t)o + 1) * X + O - 1) / O);
-    }
-    // First window whose end lies beyond position p (windows before it
-    // cannot contain p or anything after it).
-    __host__ __device__ inline int32_t first_reaching(int32_t p) const {
-        if (k) return p < k ? 0 : (p - k) / s + 1;
-        return (int32_t)(((int64_t)p * O) / X);
-    }
-    // Last window that starts at or before position p, clamped to O-1.
-    __host__ __device__ inline int32_t last_starting(int32_t p) const {
-        int64_t o = k ? (int64_t)(p / s)
-                      : ((((int64_t)p + 1) * O) - 1) / X;
-        return o < O - 1 ? (int32_t)o : O - 1;
-    }
-};
-
 // Unsigned division by a runtime constant through a multiply-high
 // (Granlund & Montgomery, "Division by invariant integers using
 // multiplication", 1994): for n < 2^31 and 1 <= d < 2^31,
@@ -60,6 +35,87 @@ struct FastDiv {
         uint32_t t = (uint32_t)(((uint64_t)n * m) >> 32);
 #endif
         return (t + n) >> l;
+    }
+};
+
+// One spatial axis: extent X split into O windows; k > 0 selects fixed
+// windows of width k and stride s, k == 0 adaptive windows.  When every
+// numerator below fits 31 bits (`fast`), the divisions by O, X and s use
+// precomputed multiply-high constants instead of 64-bit division.
+struct Axis {
+    int32_t X, O, k, s;
+    FastDiv dO, dX, dS;
+    int32_t fast;
+
+    __host__ static Axis make(int32_t X, int32_t O, int32_t k, int32_t s) {
+        Axis a;
+        a.X = X; a.O = O; a.k = k; a.s = s;
+        a.dO = FastDiv((uint32_t)O);
+        a.dX = FastDiv((uint32_t)X);
+        a.dS = FastDiv((uint32_t)(s > 0 ? s : 1));
+        const int64_t lim = (int64_t)1 << 31;
+        a.fast = ((int64_t)O + 1) * X + O < lim && ((int64_t)X + 1) * O + X < lim;
+        return a;
+    }
+
+    __host__ __device__ inline int32_t start(int32_t o) const {
+        if (k) return o * s;
+        if (fast) return (int32_t)dO.div((uint32_t)(o * X));
+        return (int32_t)(((int64_t)o * X) / O);
+    }
+    __host__ __device__ inline int32_t end(int32_t o) const {
+        if (k) return o * s + k;
+        if (fast) return (int32_t)dO.div((uint32_t)((o + 1) * X + O - 1));
+        return (int32_t)((((int64_t)o + 1) * X + O - 1) / O);
+    }
+    // First window whose end lies beyond position p (windows before it
+    // cannot contain p or anything after it).
+    __host__ __device__ inline int32_t first_reaching(int32_t p) const {
+        if (k) return p < k ? 0 : (int32_t)dS.div((uint32_t)(p - k)) + 1;
+        if (fast) return (int32_t)dX.div((uint32_t)(p * O));
+        return (int32_t)(((int64_t)p * O) / X);
+    }
+    // Last window that starts at or before position p, clamped to O-1.
+    __host__ __device__ inline int32_t last_starting(int32_t p) const {
+        int32_t o;
+        if (k) o = (int32_t)dS.div((uint32_t)p);
+        else if (fast) o = (int32_t)dX.div((uint32_t)((p + 1) * O - 1));
+        else o = (int32_t)(((((int64_t)p + 1) * O) - 1) / X);
+        return o < O - 1 ? o : O - 1;
+    }
+};
+
+// Splits a linear tile number into (plane, i0, i1, i2) for tiles counted
+// plane-major with n0 x n1 x n2 tiles per plane (i2 fastest).
+struct TileSplit {
+    FastDiv d2, d1, d0;
+    int32_t n0, n1, n2;
+    int32_t fast;              // tile numbers fit 31 bits
+
+    __host__ static TileSplit make(int64_t planes, int32_t n0, int32_t n1, int32_t n2) {
+        TileSplit t;
+        t.n0 = n0; t.n1 = n1; t.n2 = n2;
+        t.d0 = FastDiv((uint32_t)n0);
+        t.d1 = FastDiv((uint32_t)n1);
+        t.d2 = FastDiv((uint32_t)n2);
+        t.fast = planes * n0 * n1 * n2 < ((int64_t)1 << 31);
+        return t;
+    }
+    __host__ __device__ inline void split(int64_t t, int64_t *plane, int32_t *i0, int32_t *i1,
+                                          int32_t *i2) const {
+        if (fast) {
+            uint32_t q = (uint32_t)t;
+            uint32_t r = d2.div(q); *i2 = (int32_t)(q - r * (uint32_t)n2); q = r;
+            r = d1.div(q); *i1 = (int32_t)(q - r * (uint32_t)n1); q = r;
+            r = d0.div(q); *i0 = (int32_t)(q - r * (uint32_t)n0);
+            *plane = r;
+        } else {
+            int64_t q = t;
+            *i2 = (int32_t)(q % n2); q /= n2;
+            *i1 = (int32_t)(q % n1); q /= n1;
+            *i0 = (int32_t)(q % n0);
+            *plane = q / n0;
+        }
     }
 };
 

@@ -21,6 +21,7 @@ struct FwdPlan {
     int32_t ntd, nth, ntw;     // tiles per axis
     int32_t full_h, full_w;    // box spans whole rows / whole slices
     int64_t ntiles;            // planes * ntd * nth * ntw
+    TileSplit split;           // tile number -> (plane, td, th, tw)
     uint32_t tab_bytes;        // LDS: window table, 16-byte aligned
     uint32_t part_bytes;       // LDS: each of the two row-partial arrays
     uint32_t lds_bytes;        // dynamic LDS per workgroup
@@ -35,6 +36,8 @@ struct BwdPlan {
     int32_t td, th, tw;        // input tile extents
     int32_t ntd, nth, ntw;
     int64_t ntiles;
+    TileSplit split;           // tile number -> (plane, td, th, tw)
+    FastDiv ow_div, oh_div;    // for boxes of whole slices (all OH x OW reach them)
     uint32_t lds_bytes;
 };
 

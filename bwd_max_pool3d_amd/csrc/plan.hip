@@ -109,6 +109,7 @@ bool plan_forward(const Geom &g, int es, FwdPlan *p)
     p->full_h = full_h;
     p->full_w = full_w;
     p->ntiles = g.planes * p->ntd * p->nth * p->ntw;
+    p->split = TileSplit::make(g.planes, p->ntd, p->nth, p->ntw);
     p->tab_bytes = (uint32_t)tab;
     p->part_bytes = (uint32_t)part;
     p->lds_bytes = (uint32_t)lds;
@@ -205,7 +206,11 @@ bool plan_backward(const Geom &g, BwdPlan *p)
     p->nth = (int32_t)cdiv(H, p->th);
     p->ntw = (int32_t)cdiv(W, p->tw);
     p->ntiles = g.planes * p->ntd * p->nth * p->ntw;
-    p->lds_bytes = (uint32_t)(((int64_t)p->td * p->th * p->tw + 4) * 4);   // + alignment shift
+    p->split = TileSplit::make(g.planes, p->ntd, p->nth, p->ntw);
+    p->ow_div = FastDiv((uint32_t)g.ax[2].O);
+    p->oh_div = FastDiv((uint32_t)g.ax[1].O);
+    // + alignment shift and the rounding of the zero fill to 16 bytes
+    p->lds_bytes = (uint32_t)(((int64_t)p->td * p->th * p->tw + 8) * 4);
     return true;
 }
 

@@ -147,12 +147,17 @@ def test_many_small_planes(orc):
         _gpu.check_backward(orc, gy, idx.cpu(), shape, gx, exact=True, what="many planes")
 
 
-def test_subnormal_gradients(orc):
-    """float32 subnormal contributions are accumulated exactly (no flush)."""
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+def test_subnormal_gradients(orc, dtype):
+    """Gradients in the storage type's subnormal range are accumulated and
+    rounded without flushing to zero."""
     shape = (2, 2, 10, 10, 10)
-    x = _pins.from_storage(_pins.draw(shape, 0, "ties", 8), 0)
+    code = _gpu.CODE[dtype]
+    x = _pins.from_storage(_pins.draw(shape, code, "ties", 8), code)
     y, idx = _gpu.gpu_forward(x, (8, 8, 8))
-    g = torch.randn(y.shape, generator=torch.Generator().manual_seed(9)) * 1e-39
+    scale = {torch.float32: 1e-39, torch.float16: 1e-6, torch.bfloat16: 1e-39}[dtype]
+    g = (torch.randn(y.shape, generator=torch.Generator().manual_seed(9)) * scale).to(dtype)
+    assert (g != 0).float().mean() > 0.5
     gx = _gpu.gpu_backward(g, idx.cpu(), shape)
     _gpu.check_backward(orc, g, idx.cpu(), shape, gx, exact=False, what="subnormal")
 
