@@ -52,154 +52,198 @@ __device__ __forceinline__ u32x4 pack16(const float *a)
     }
 }
 
-constexpr int kRound = 8;   // windows per thread fetched per round
+constexpr int kRound = 8;        // windows per thread fetched per round
+constexpr int kSlabBlock = kSlabThreads;  // threads per slab workgroup
 
-// An input box of one plane and the windows that can reach it.
-struct BTile {
-    int64_t plane;
-    int32_t d0, d1, h0, h1, w0, w1;        // input box
-    int32_t od0, oh0, ow0, cd, ch, cw;      // reaching windows: [od0, od0+cd) x ...
-    int32_t n, nw;                          // box elements, reaching windows
-    bool full;                              // whole rows and slices: one span
-};
-
-__device__ __forceinline__ BTile btile_at(const BwdPlan &p, int64_t t)
+// Round the accumulator a[0, n) into dst[0, n): 16-byte streaming stores for
+// the aligned body (four LDS reads in flight per thread), element stores
+// for the unaligned head and tail.  a[e] and dst[e] share their alignment
+// modulo one 16-byte vector.
+template <typename T, int NT>
+__device__ __forceinline__ void store_span(typename T::raw *dst, const float *a, int32_t n,
+                                           int32_t head)
 {
-    const Axis &A = p.g.ax[0], &B = p.g.ax[1], &Cw = p.g.ax[2];
-    BTile b;
-    int32_t td, th, tw;
-    p.split.split(t, &b.plane, &td, &th, &tw);
-    b.d0 = td * p.td; b.d1 = min(b.d0 + p.td, A.X);
-    b.h0 = th * p.th; b.h1 = min(b.h0 + p.th, B.X);
-    b.w0 = tw * p.tw; b.w1 = min(b.w0 + p.tw, Cw.X);
-    b.n = (b.d1 - b.d0) * (b.h1 - b.h0) * (b.w1 - b.w0);
-    b.full = (b.h1 - b.h0 == B.X) && (b.w1 - b.w0 == Cw.X);
-    b.od0 = A.first_reaching(b.d0);
-    b.oh0 = B.first_reaching(b.h0);
-    b.ow0 = Cw.first_reaching(b.w0);
-    b.cd = max(A.last_starting(b.d1 - 1) + 1 - b.od0, 0);
-    b.ch = max(B.last_starting(b.h1 - 1) + 1 - b.oh0, 0);
-    b.cw = max(Cw.last_starting(b.w1 - 1) + 1 - b.ow0, 0);
-    b.nw = b.cd * b.ch * b.cw;
-    return b;
-}
-
-// Issue the loads of one round of (idx, gy) pairs of tile b; i = INT_MIN
-// marks an empty slot.  Decoding waits until the values are needed.
-template <typename T>
-__device__ __forceinline__ void fetch_round(const BwdPlan &p, const BTile &b, int32_t round,
-                                            const typename T::raw *__restrict__ gy,
-                                            const int32_t *__restrict__ idx,
-                                            int32_t (&ri)[kRound], typename T::raw (&rg)[kRound])
-{
-    const int64_t obase = b.plane * (int64_t)p.g.out_plane;
-    const int32_t OH = p.g.ax[1].O, OW = p.g.ax[2].O;
-#pragma unroll
-    for (int k = 0; k < kRound; ++k) {
-        const int32_t e = (round * kRound + k) * kBlock + (int32_t)threadIdx.x;
-        ri[k] = INT32_MIN;
-        if (e < b.nw) {
-            int32_t owl, ohl, odl;
-            if (b.full) {       // cw == OW and ch == OH: divide by launch constants
-                const uint32_t r = p.ow_div.div((uint32_t)e);
-                owl = e - (int32_t)r * OW;
-                odl = (int32_t)p.oh_div.div(r);
-                ohl = (int32_t)r - odl * OH;
-            } else {
-                owl = e % b.cw;
-                const int32_t r = e / b.cw;
-                ohl = r % b.ch;
-                odl = r / b.ch;
-            }
-            const int64_t o = obase + ((b.od0 + odl) * OH + b.oh0 + ohl) * OW + b.ow0 + owl;
-            ri[k] = idx[o];
-            rg[k] = gy[o];
-        }
+    constexpr int VE = 16 / (int)sizeof(typename T::raw);
+    const int32_t tid = threadIdx.x;
+    const int32_t nvec = (n - head) / VE;
+    const int32_t tail0 = head + nvec * VE;
+    if (tid < head) dst[tid] = T::narrow(a[tid]);
+    u32x4 *vd = reinterpret_cast<u32x4 *>(dst + head);
+    int32_t i = tid;
+    for (; i + 3 * NT < nvec; i += 4 * NT) {
+        const u32x4 v0 = pack16<T>(a + head + i * VE);
+        const u32x4 v1 = pack16<T>(a + head + (i + NT) * VE);
+        const u32x4 v2 = pack16<T>(a + head + (i + 2 * NT) * VE);
+        const u32x4 v3 = pack16<T>(a + head + (i + 3 * NT) * VE);
+        st_stream(vd + i, v0);
+        st_stream(vd + i + NT, v1);
+        st_stream(vd + i + 2 * NT, v2);
+        st_stream(vd + i + 3 * NT, v3);
     }
+    for (; i < nvec; i += NT) st_stream(vd + i, pack16<T>(a + head + i * VE));
+    if (tid < n - tail0) dst[tail0 + tid] = T::narrow(a[tail0 + tid]);
 }
 
-template <typename T>
-__global__ void __launch_bounds__(kBlock)
-bwd_tile_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
+// Slabs of whole H*W slices [d0, d1) of one plane.  The slab is one
+// contiguous run of gx; the windows that can reach it are those of the
+// output slices [od0, od1).
+//
+// CLS (the usual case): windows are split into classes by (od mod cd,
+// oh mod ch, ow mod cw), where c is the smallest window distance along an
+// axis at which windows no longer overlap.  Two windows of one class are
+// disjoint, so their argmax cells differ, and each class adds with plain
+// LDS read-modify-writes; a barrier separates classes.  (LDS float atomics
+// measured about 30 times slower than plain read-modify-writes here.)  The
+// order of the adds is fixed, so results repeat bit for bit.
+// !CLS: all windows in order, with LDS float atomics.
+template <typename T, int NT, bool CLS>
+__global__ void __launch_bounds__(NT)
+bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
                 typename T::raw *__restrict__ gx, BwdPlan p)
 {
     using R = typename T::raw;
-    constexpr int VE = 16 / (int)sizeof(R);   // gx elements per 16-byte store
+    constexpr int VE = 16 / (int)sizeof(R);
     extern __shared__ __align__(16) float acc[];
-    const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X;
+    const Axis A = p.g.ax[0];
+    const int32_t OH = p.g.ax[1].O, OW = p.g.ax[2].O;
+    const int32_t HW = p.g.ax[1].X * p.g.ax[2].X;
+    const int32_t OHW = OH * OW;
     const int32_t tid = threadIdx.x;
-    const int64_t first = xcd_local_block(blockIdx.x, gridDim.x);
 
-    // The workgroup is persistent: round 0 of the next tile's (idx, gy)
-    // loads is issued before this tile's store phase.
+    const uint32_t t = xcd_local_block(blockIdx.x, gridDim.x);
+    if (t >= p.ntiles) return;                   // whole workgroup: no barrier skipped
+    int64_t plane;
+    int32_t td, th, tw;
+    p.split.split(t, &plane, &td, &th, &tw);
+    const int32_t d0 = td * p.td, d1 = min(d0 + p.td, A.X);
+    const int32_t n = (d1 - d0) * HW;
+    const int32_t od0 = A.first_reaching(d0);
+    const int32_t od1 = A.last_starting(d1 - 1) + 1;
+    const int64_t obase = plane * (int64_t)p.g.out_plane;
+    const int32_t ibase = d0 * HW;
+    R *dst = gx + plane * (int64_t)p.g.in_plane + ibase;
+
+    // the accumulator is shifted so that a[e] and dst[e] share alignment
+    const int32_t mis = (int32_t)(((uintptr_t)dst / sizeof(R)) % VE);
+    const int32_t head = min((VE - mis) % VE, n);
+    const int32_t shift = (4 - head % 4) % 4;
+    float *a = acc + shift;
+
     int32_t ri[kRound];
     R rg[kRound];
-    if (first < p.ntiles) fetch_round<T>(p, btile_at(p, first), 0, gy, idx, ri, rg);
-
-    for (int64_t t = first; t < p.ntiles; t += gridDim.x) {
-        const BTile b = btile_at(p, t);
-        const int32_t lh = b.h1 - b.h0, lw = b.w1 - b.w0;
-        R *gp = gx + b.plane * (int64_t)p.g.in_plane;
-        R *dst = gp + b.d0 * H * W;                 // the box, when rows are whole
-
-        // the accumulator is shifted so that its element e and dst[e] share
-        // their alignment: whole 16-byte gx vectors map to aligned LDS reads
-        const int32_t mis = (int32_t)(((uintptr_t)dst / sizeof(R)) % VE);
-        const int32_t head = b.full ? min((VE - mis) % VE, b.n) : 0;
-        const int32_t shift = (4 - head % 4) % 4;
-        float *a = acc + shift;
-        const int32_t ibase = b.d0 * H * W;
-
-        // zero fill, 16 bytes at a time
-        for (int32_t e = tid; e < (b.n + shift + 3) / 4; e += kBlock)
+    if constexpr (CLS) {
+        // slot k holds this thread's window of class k (one round: every
+        // class has at most NT windows reaching a slab).  Class counts per
+        // axis are 1 or 2 (lc = log2), so the class arithmetic is shifts and
+        // masks (uniform, on the scalar unit).
+        const int32_t lcd = p.cls[0] - 1, lch = p.cls[1] - 1, lcw = p.cls[2] - 1;
+#pragma unroll
+        for (int k = 0; k < kRound; ++k) {
+            ri[k] = -1;
+            if (k < p.nclasses) {
+                const int32_t pw = k & lcw, pr = k >> lcw, ph = pr & lch, pd = pr >> lch;
+                const int32_t odf = od0 + ((pd - od0) & lcd);
+                const int32_t nd = odf < od1 ? (od1 - odf + lcd) >> lcd : 0;
+                const int32_t nh = p.cls_n[1][ph], nwc = p.cls_n[2][pw];
+                if (tid < nd * nh * nwc) {
+                    const uint32_t q = p.cls_div[2][pw].div((uint32_t)tid);
+                    const int32_t iw = tid - (int32_t)q * nwc;
+                    const uint32_t id = p.cls_div[1][ph].div(q);
+                    const int32_t ih = (int32_t)q - (int32_t)id * nh;
+                    const int64_t o = obase + (((odf + ((int32_t)id << lcd)) * OH + ph + (ih << lch)) *
+                                               OW + pw + (iw << lcw));
+                    ri[k] = idx[o];
+                    rg[k] = gy[o];
+                }
+            }
+        }
+        for (int32_t e = tid; e < (n + shift + 3) / 4; e += NT)          // zero fill
+            reinterpret_cast<u32x4 *>(acc)[e] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kRound; ++k) {
+            if (k < p.nclasses) {                    // uniform
+                const uint32_t l = (uint32_t)ri[k] - (uint32_t)ibase;
+                if (ri[k] >= 0 && l < (uint32_t)n) a[l] = a[l] + T::widen(rg[k]);
+                __syncthreads();
+            }
+        }
+    } else {
+        const int32_t nw = max(od1 - od0, 0) * OHW;
+        const int64_t wbase = obase + (int64_t)od0 * OHW;
+        auto fetch = [&](int32_t round) {
+#pragma unroll
+            for (int k = 0; k < kRound; ++k) {
+                const int32_t e = (round * kRound + k) * NT + tid;
+                ri[k] = -1;
+                if (e < nw) {
+                    ri[k] = idx[wbase + e];
+                    rg[k] = gy[wbase + e];
+                }
+            }
+        };
+        fetch(0);                                   // in flight during the zero fill
+        for (int32_t e = tid; e < (n + shift + 3) / 4; e += NT)
             reinterpret_cast<u32x4 *>(acc)[e] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
         for (int32_t round = 0;; ++round) {
 #pragma unroll
             for (int k = 0; k < kRound; ++k) {
-                const int32_t i = ri[k];
-                int32_t loc = -1;
-                if (b.full) {
-                    const uint32_t l = (uint32_t)i - (uint32_t)ibase;
-                    if (i != INT32_MIN && l < (uint32_t)b.n) loc = (int32_t)l;
-                } else if ((uint32_t)i < (uint32_t)p.g.in_plane) {
-                    const int32_t d = i / (H * W), rem = i - d * H * W;
-                    const int32_t h = rem / W, w = rem - h * W;
-                    if (d >= b.d0 && d < b.d1 && h >= b.h0 && h < b.h1 && w >= b.w0 && w < b.w1)
-                        loc = ((d - b.d0) * lh + (h - b.h0)) * lw + (w - b.w0);
-                }
-                if (loc >= 0) atomicAdd(&a[loc], T::widen(rg[k]));   // ds_add_f32 scatter
+                const uint32_t l = (uint32_t)ri[k] - (uint32_t)ibase;
+                if (ri[k] >= 0 && l < (uint32_t)n) atomicAdd(&a[l], T::widen(rg[k]));  // ds_add_f32
             }
-            if ((round + 1) * kRound * kBlock >= b.nw) break;
-            fetch_round<T>(p, b, round + 1, gy, idx, ri, rg);
+            if ((round + 1) * kRound * NT >= nw) break;
+            fetch(round + 1);
         }
         __syncthreads();
-        if (t + gridDim.x < p.ntiles) fetch_round<T>(p, btile_at(p, t + gridDim.x), 0, gy, idx, ri, rg);
+    }
+    store_span<T, NT>(dst, a, n, head);
+}
 
-        // one rounding store per gx element
-        if (b.full) {
-            const int32_t nvec = (b.n - head) / VE;
-            const int32_t tail0 = head + nvec * VE;
-            if (tid < head) dst[tid] = T::narrow(a[tid]);
-            u32x4 *vd = reinterpret_cast<u32x4 *>(dst + head);
-            int32_t i = tid;
-            for (; i + 3 * kBlock < nvec; i += 4 * kBlock) {     // four LDS reads in flight
-                const u32x4 v0 = pack16<T>(a + head + i * VE);
-                const u32x4 v1 = pack16<T>(a + head + (i + kBlock) * VE);
-                const u32x4 v2 = pack16<T>(a + head + (i + 2 * kBlock) * VE);
-                const u32x4 v3 = pack16<T>(a + head + (i + 3 * kBlock) * VE);
-                st_stream(vd + i, v0);
-                st_stream(vd + i + kBlock, v1);
-                st_stream(vd + i + 2 * kBlock, v2);
-                st_stream(vd + i + 3 * kBlock, v3);
+// General boxes [d0,d1) x [h0,h1) x [w0,w1) (a slice does not fit in LDS).
+template <typename T>
+__global__ void __launch_bounds__(kBlock)
+bwd_box_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
+               typename T::raw *__restrict__ gx, BwdPlan p)
+{
+    using R = typename T::raw;
+    extern __shared__ __align__(16) float acc[];
+    const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
+    const int32_t H = B.X, W = Cw.X;
+    const int32_t tid = threadIdx.x;
+    for (int64_t t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
+        int64_t plane;
+        int32_t td, th, tw;
+        p.split.split(t, &plane, &td, &th, &tw);
+        const int32_t d0 = td * p.td, d1 = min(d0 + p.td, A.X);
+        const int32_t h0 = th * p.th, h1 = min(h0 + p.th, H);
+        const int32_t w0 = tw * p.tw, w1 = min(w0 + p.tw, W);
+        const int32_t lh = h1 - h0, lw = w1 - w0, n = (d1 - d0) * lh * lw;
+        const int32_t od0 = A.first_reaching(d0), oh0 = B.first_reaching(h0);
+        const int32_t ow0 = Cw.first_reaching(w0);
+        const int32_t cd = max(A.last_starting(d1 - 1) + 1 - od0, 0);
+        const int32_t ch = max(B.last_starting(h1 - 1) + 1 - oh0, 0);
+        const int32_t cw = max(Cw.last_starting(w1 - 1) + 1 - ow0, 0);
+        const int64_t obase = plane * (int64_t)p.g.out_plane;
+
+        for (int32_t e = tid; e < n; e += kBlock) acc[e] = 0.0f;
+        __syncthreads();
+        for (int32_t e = tid; e < cd * ch * cw; e += kBlock) {
+            const int32_t owl = e % cw, r = e / cw, ohl = r % ch, odl = r / ch;
+            const int64_t o = obase + ((od0 + odl) * B.O + oh0 + ohl) * Cw.O + ow0 + owl;
+            const int32_t i = idx[o];
+            if ((uint32_t)i < (uint32_t)p.g.in_plane) {
+                const int32_t d = i / (H * W), rem = i - d * H * W;
+                const int32_t h = rem / W, w = rem - h * W;
+                if (d >= d0 && d < d1 && h >= h0 && h < h1 && w >= w0 && w < w1)
+                    atomicAdd(&acc[((d - d0) * lh + (h - h0)) * lw + (w - w0)], T::widen(gy[o]));
             }
-            for (; i < nvec; i += kBlock) st_stream(vd + i, pack16<T>(a + head + i * VE));
-            if (tid < b.n - tail0) dst[tail0 + tid] = T::narrow(a[tail0 + tid]);
-        } else {
-            for (int32_t e = tid; e < b.n; e += kBlock) {
-                const int32_t w = e % lw, r = e / lw, h = r % lh, d = r / lh;
-                gp[((b.d0 + d) * H + b.h0 + h) * W + b.w0 + w] = T::narrow(a[e]);
-            }
+        }
+        __syncthreads();
+        R *gp = gx + plane * (int64_t)p.g.in_plane;
+        for (int32_t e = tid; e < n; e += kBlock) {
+            const int32_t w = e % lw, r = e / lw, h = r % lh, d = r / lh;
+            gp[((d0 + d) * H + h0 + h) * W + w0 + w] = T::narrow(acc[e]);
         }
         __syncthreads();   // LDS is reused by the next tile
     }
@@ -233,12 +277,21 @@ hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
                                 const BwdPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
-    // one workgroup per tile (measured faster than a persistent grid here:
-    // the store phases of many resident workgroups overlap)
     int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)1 << 24);
-    if (grid >= 64) grid &= ~(int64_t)7;    // a multiple of 8 lets blocks map per XCD
-    hipLaunchKernelGGL(bwd_tile_kernel<T>, dim3((uint32_t)grid), dim3(kBlock),
-                       p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
+    if (p.slab) {
+        // one workgroup per slab; a multiple of 8 lets blocks map per XCD
+        // (the surplus blocks exit at once)
+        if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
+        if (p.nclasses > 0)
+            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, true>), dim3((uint32_t)grid),
+                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
+        else
+            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, false>), dim3((uint32_t)grid),
+                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
+    } else {
+        hipLaunchKernelGGL(bwd_box_kernel<T>, dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
+                           (const R *)gy, idx, (R *)gx, p);
+    }
     return hipGetLastError();
 }
 

@@ -11,6 +11,8 @@
 namespace mp3d {
 
 constexpr int kBlock = 256;            // threads per workgroup (4 waves)
+constexpr int kSlabThreads = 512;      // threads per backward slab workgroup
+constexpr int kMaxCls = 4;             // window classes per axis, at most
 
 // Forward through LDS: each workgroup owns an output tile
 // [od0,od0+tod) x [oh0,oh0+toh) x [ow0,ow0+tow) of one plane, stages the
@@ -37,7 +39,13 @@ struct BwdPlan {
     int32_t ntd, nth, ntw;
     int64_t ntiles;
     TileSplit split;           // tile number -> (plane, td, th, tw)
-    FastDiv ow_div, oh_div;    // for boxes of whole slices (all OH x OW reach them)
+    int32_t slab;              // boxes are whole H*W slices
+    // window classes (slabs only): windows cls[a] apart along axis a are
+    // disjoint; nclasses = product, 0 when the class path is not used.
+    // cls_n[a][r] = number of windows o on axis a with o % cls[a] == r.
+    int32_t cls[3], nclasses;
+    int32_t cls_n[3][kMaxCls];
+    FastDiv cls_div[3][kMaxCls];
     uint32_t lds_bytes;
 };
 
@@ -55,6 +63,9 @@ struct FixedPlan {
     FastDiv groups, oh, od;    // divide by G, OH, OD
     int32_t G;                 // thread groups per output row: ceil(OW / V)
     uint32_t nthreads;         // planes * OD * OH * G
+    uint32_t nrows;            // output rows: planes * OD * OH
+    int32_t rpw;               // whole rows per wave (0: rows may straddle waves)
+    int32_t spill_load;        // some group loads its spill columns itself
     int32_t vec_store;         // outputs may be stored as 4-wide vectors
 };
 

@@ -46,6 +46,7 @@ CASES = [
     ((2, 3, 7, 9, 24), None, (3, 3, 3), (2, 2, 2)),       # partial last thread group
     ((1, 2, 6, 6, 40), None, (2, 2, 2), (2, 2, 2)),
     ((1, 1, 4, 4, 36), None, (2, 2, 2), (2, 2, 2)),       # rows not a multiple of 4 outputs
+    ((2, 1, 3, 5, 1032), None, (3, 3, 3), (2, 2, 2)),     # rows wider than a wave
     ((1, 1, 7, 300, 300), None, (2, 3, 3), (2, 2, 2)),    # slices larger than LDS
     ((1, 1, 2, 1, 70000), None, (1, 1, 5), (1, 1, 3)),    # rows larger than LDS
     ((2, 1, 3, 5000, 1), (2, 777, 1), None, None),
