@@ -84,19 +84,16 @@ __device__ __forceinline__ void store_span(typename T::raw *dst, const float *a,
     if (tid < n - tail0) dst[tail0 + tid] = T::narrow(a[tail0 + tid]);
 }
 
-// Slabs of whole H*W slices [d0, d1) of one plane.  The slab is one
-// contiguous run of gx; the windows that can reach it are those of the
-// output slices [od0, od1).
+// Slabs of whole H*W slices [d0, d1) of one plane.  Every window of the
+// output slices [od0, od1) that can reach the slab is one contiguous run of
+// gy and idx, and the slab is one contiguous run of gx.
 //
-// CLS (the usual case): windows are split into classes by (od mod cd,
-// oh mod ch, ow mod cw), where c is the smallest window distance along an
-// axis at which windows no longer overlap.  Two windows of one class are
-// disjoint, so their argmax cells differ, and each class adds with plain
-// LDS read-modify-writes; a barrier separates classes.  (LDS float atomics
-// measured about 30 times slower than plain read-modify-writes here.)  The
-// order of the adds is fixed, so results repeat bit for bit.
-// !CLS: all windows in order, with LDS float atomics.
-template <typename T, int NT, bool CLS>
+// The scatter uses LDS float atomics (ds_add_f32).  They measured about 30
+// times slower per instruction than plain LDS read-modify-writes, and an
+// atomic-free variant (windows split into 2x2x2 disjoint classes, one
+// barrier per class) was faster alone but slower inside the whole
+// forward+backward step, so the atomics stay.
+template <typename T, int NT>
 __global__ void __launch_bounds__(NT)
 bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
                 typename T::raw *__restrict__ gx, BwdPlan p)
@@ -105,9 +102,8 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
     constexpr int VE = 16 / (int)sizeof(R);
     extern __shared__ __align__(16) float acc[];
     const Axis A = p.g.ax[0];
-    const int32_t OH = p.g.ax[1].O, OW = p.g.ax[2].O;
     const int32_t HW = p.g.ax[1].X * p.g.ax[2].X;
-    const int32_t OHW = OH * OW;
+    const int32_t OHW = p.g.ax[1].O * p.g.ax[2].O;
     const int32_t tid = threadIdx.x;
 
     const uint32_t t = xcd_local_block(blockIdx.x, gridDim.x);
@@ -118,8 +114,8 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
     const int32_t d0 = td * p.td, d1 = min(d0 + p.td, A.X);
     const int32_t n = (d1 - d0) * HW;
     const int32_t od0 = A.first_reaching(d0);
-    const int32_t od1 = A.last_starting(d1 - 1) + 1;
-    const int64_t obase = plane * (int64_t)p.g.out_plane;
+    const int32_t nw = max(A.last_starting(d1 - 1) + 1 - od0, 0) * OHW;
+    const int64_t wbase = plane * (int64_t)p.g.out_plane + (int64_t)od0 * OHW;
     const int32_t ibase = d0 * HW;
     R *dst = gx + plane * (int64_t)p.g.in_plane + ibase;
 
@@ -131,72 +127,31 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
 
     int32_t ri[kRound];
     R rg[kRound];
-    if constexpr (CLS) {
-        // slot k holds this thread's window of class k (one round: every
-        // class has at most NT windows reaching a slab).  Class counts per
-        // axis are 1 or 2 (lc = log2), so the class arithmetic is shifts and
-        // masks (uniform, on the scalar unit).
-        const int32_t lcd = p.cls[0] - 1, lch = p.cls[1] - 1, lcw = p.cls[2] - 1;
+    auto fetch = [&](int32_t round) {
 #pragma unroll
         for (int k = 0; k < kRound; ++k) {
+            const int32_t e = (round * kRound + k) * NT + tid;
             ri[k] = -1;
-            if (k < p.nclasses) {
-                const int32_t pw = k & lcw, pr = k >> lcw, ph = pr & lch, pd = pr >> lch;
-                const int32_t odf = od0 + ((pd - od0) & lcd);
-                const int32_t nd = odf < od1 ? (od1 - odf + lcd) >> lcd : 0;
-                const int32_t nh = p.cls_n[1][ph], nwc = p.cls_n[2][pw];
-                if (tid < nd * nh * nwc) {
-                    const uint32_t q = p.cls_div[2][pw].div((uint32_t)tid);
-                    const int32_t iw = tid - (int32_t)q * nwc;
-                    const uint32_t id = p.cls_div[1][ph].div(q);
-                    const int32_t ih = (int32_t)q - (int32_t)id * nh;
-                    const int64_t o = obase + (((odf + ((int32_t)id << lcd)) * OH + ph + (ih << lch)) *
-                                               OW + pw + (iw << lcw));
-                    ri[k] = idx[o];
-                    rg[k] = gy[o];
-                }
+            if (e < nw) {
+                ri[k] = idx[wbase + e];
+                rg[k] = gy[wbase + e];
             }
         }
-        for (int32_t e = tid; e < (n + shift + 3) / 4; e += NT)          // zero fill
-            reinterpret_cast<u32x4 *>(acc)[e] = u32x4{0u, 0u, 0u, 0u};
-        __syncthreads();
+    };
+    fetch(0);                                   // in flight during the zero fill
+    for (int32_t e = tid; e < (n + shift + 3) / 4; e += NT)
+        reinterpret_cast<u32x4 *>(acc)[e] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    for (int32_t round = 0;; ++round) {
 #pragma unroll
         for (int k = 0; k < kRound; ++k) {
-            if (k < p.nclasses) {                    // uniform
-                const uint32_t l = (uint32_t)ri[k] - (uint32_t)ibase;
-                if (ri[k] >= 0 && l < (uint32_t)n) a[l] = a[l] + T::widen(rg[k]);
-                __syncthreads();
-            }
+            const uint32_t l = (uint32_t)ri[k] - (uint32_t)ibase;
+            if (ri[k] >= 0 && l < (uint32_t)n) atomicAdd(&a[l], T::widen(rg[k]));  // ds_add_f32
         }
-    } else {
-        const int32_t nw = max(od1 - od0, 0) * OHW;
-        const int64_t wbase = obase + (int64_t)od0 * OHW;
-        auto fetch = [&](int32_t round) {
-#pragma unroll
-            for (int k = 0; k < kRound; ++k) {
-                const int32_t e = (round * kRound + k) * NT + tid;
-                ri[k] = -1;
-                if (e < nw) {
-                    ri[k] = idx[wbase + e];
-                    rg[k] = gy[wbase + e];
-                }
-            }
-        };
-        fetch(0);                                   // in flight during the zero fill
-        for (int32_t e = tid; e < (n + shift + 3) / 4; e += NT)
-            reinterpret_cast<u32x4 *>(acc)[e] = u32x4{0u, 0u, 0u, 0u};
-        __syncthreads();
-        for (int32_t round = 0;; ++round) {
-#pragma unroll
-            for (int k = 0; k < kRound; ++k) {
-                const uint32_t l = (uint32_t)ri[k] - (uint32_t)ibase;
-                if (ri[k] >= 0 && l < (uint32_t)n) atomicAdd(&a[l], T::widen(rg[k]));  // ds_add_f32
-            }
-            if ((round + 1) * kRound * NT >= nw) break;
-            fetch(round + 1);
-        }
-        __syncthreads();
+        if ((round + 1) * kRound * NT >= nw) break;
+        fetch(round + 1);
     }
+    __syncthreads();
     store_span<T, NT>(dst, a, n, head);
 }
 
@@ -282,12 +237,8 @@ hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
         // one workgroup per slab; a multiple of 8 lets blocks map per XCD
         // (the surplus blocks exit at once)
         if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
-        if (p.nclasses > 0)
-            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, true>), dim3((uint32_t)grid),
-                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
-        else
-            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, false>), dim3((uint32_t)grid),
-                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
+        hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock>), dim3((uint32_t)grid),
+                           dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
     } else {
         hipLaunchKernelGGL(bwd_box_kernel<T>, dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
                            (const R *)gy, idx, (R *)gx, p);

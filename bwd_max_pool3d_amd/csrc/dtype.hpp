@@ -18,12 +18,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Streaming (non-temporal) stores and loads: data written or read once is
-// not kept in the caches.  Output streams measured markedly faster this way.
+// Streaming (non-temporal) stores: data written once is not kept in the
+// caches.  Output streams measured markedly faster this way.
 template <typename V>
 __device__ __forceinline__ void st_stream(V *p, V v) { __builtin_nontemporal_store(v, p); }
-template <typename V>
-__device__ __forceinline__ V ld_stream(const V *p) { return __builtin_nontemporal_load(p); }
 
 struct F32 {
     using raw = float;

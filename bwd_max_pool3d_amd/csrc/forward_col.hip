@@ -26,7 +26,9 @@ namespace mp3d {
 namespace {
 
 // Loads of one window's slices of one column group: slot j holds slice
-// ds + j while j < n.
+// ds + j while j < n.  Plain (cached) loads: a slice shared by two
+// neighbouring windows is then served from L2 the second time; streaming
+// loads bypass L2 and read it from HBM again.
 template <int MAXKD>
 struct ColWin {
     u32x4 q[MAXKD];
@@ -38,7 +40,7 @@ __device__ __forceinline__ void col_load(ColWin<MAXKD> &w, const R *__restrict__
 {
 #pragma unroll
     for (int j = 0; j < MAXKD; ++j)
-        if (j < n) w.q[j] = ld_stream(reinterpret_cast<const u32x4 *>(col + (int64_t)j * hw));
+        if (j < n) w.q[j] = *reinterpret_cast<const u32x4 *>(col + (int64_t)j * hw);
 }
 
 // Element-wise first maximum over the n loaded slices; writes the values

@@ -12,7 +12,6 @@ namespace mp3d {
 
 constexpr int kBlock = 256;            // threads per workgroup (4 waves)
 constexpr int kSlabThreads = 512;      // threads per backward slab workgroup
-constexpr int kMaxCls = 4;             // window classes per axis, at most
 
 // Forward through LDS: each workgroup owns an output tile
 // [od0,od0+tod) x [oh0,oh0+toh) x [ow0,ow0+tow) of one plane, stages the
@@ -40,12 +39,6 @@ struct BwdPlan {
     int64_t ntiles;
     TileSplit split;           // tile number -> (plane, td, th, tw)
     int32_t slab;              // boxes are whole H*W slices
-    // window classes (slabs only): windows cls[a] apart along axis a are
-    // disjoint; nclasses = product, 0 when the class path is not used.
-    // cls_n[a][r] = number of windows o on axis a with o % cls[a] == r.
-    int32_t cls[3], nclasses;
-    int32_t cls_n[3][kMaxCls];
-    FastDiv cls_div[3][kMaxCls];
     uint32_t lds_bytes;
 };
 

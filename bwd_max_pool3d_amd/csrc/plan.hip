@@ -219,43 +219,6 @@ bool plan_backward(const Geom &g, BwdPlan *p)
     p->ntiles = g.planes * p->ntd * p->nth * p->ntw;
     p->split = TileSplit::make(g.planes, p->ntd, p->nth, p->ntw);
     p->slab = p->th == H && p->tw == W;
-    // window classes: along each axis, the smallest distance c at which
-    // windows o and o + c never overlap
-    p->nclasses = 0;
-    bool ok = p->slab;
-    for (int a = 0; a < 3 && ok; ++a) {
-        const Axis &ax = g.ax[a];
-        int32_t c = 1;
-        if (ax.k) {
-            c = (int32_t)cdiv(ax.k, ax.s);
-        } else if (ax.O <= 65536) {
-            for (int32_t o = 0; o + c < ax.O; ++o)
-                while (o + c < ax.O && ax.start(o + c) < ax.end(o)) ++c;
-        } else {
-            ok = false;
-        }
-        if (c > 2) ok = false;        // class arithmetic uses shifts: 1 or 2 per axis
-        if (!ok) break;
-        p->cls[a] = c;
-        for (int32_t r = 0; r < kMaxCls; ++r) {
-            const int32_t cnt = r < c ? (int32_t)cdiv(ax.O - r, c) : 1;
-            p->cls_n[a][r] = cnt > 0 ? cnt : 1;
-            p->cls_div[a][r] = FastDiv((uint32_t)p->cls_n[a][r]);
-        }
-    }
-    if (ok) {
-        const int32_t ncls = p->cls[0] * p->cls[1] * p->cls[2];
-        // largest class reaching one slab: od slices reaching it, per class
-        int64_t odmax = 0;
-        for (int32_t td = 0; td < p->ntd; ++td) {
-            const int32_t d0 = td * p->td, d1 = std::min(d0 + p->td, D);
-            odmax = std::max<int64_t>(odmax, g.ax[0].last_starting(d1 - 1) + 1 -
-                                                 g.ax[0].first_reaching(d0));
-        }
-        const int64_t big = cdiv(odmax, p->cls[0]) * cdiv(g.ax[1].O, p->cls[1]) *
-                            cdiv(g.ax[2].O, p->cls[2]);
-        if (ncls <= 8 && big <= kSlabThreads && p->ntd <= 65536) p->nclasses = ncls;
-    }
     // + alignment shift and the rounding of the zero fill to 16 bytes
     p->lds_bytes = (uint32_t)(((int64_t)p->td * p->th * p->tw + 8) * 4);
     return true;
