@@ -26,13 +26,81 @@ __device__ inline uint32_t xcd_local_block(uint32_t b, uint32_t nblocks)
     return (b % 8u) * (nblocks / 8u) + b / 8u;
 }
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// Binary16 windows without NaN, in two passes over the registers: each
+// window's maximum first, then the first element equal to it, found by
+// scanning from the last element back to the first.  The maxima use the
+// packed IEEE 754-2019 maximum (NaN when an operand is NaN) on the loaded
+// dwords as they are, two columns per instruction; the compares read either
+// half of a dword directly.  The scan carries the code dd << 4 | hh << 2 |
+// ww, small enough to be an inline constant of the select.  Returns false,
+// computing nothing, when a window holds a NaN.
+template <int KD, int KH, int KW, int SW, int SPAN, int V, int NQ, typename Rel>
+__device__ __forceinline__ bool f16_first_max(const uint32_t (&q)[KD][KH][NQ], Rel rel,
+                                              const uint16_t *__restrict__ xp, int32_t at0,
+                                              bool active, int32_t (&io)[V], uint16_t (&yo)[V])
+{
+    static_assert(KD <= 4 && KH <= 4 && KW <= 4, "window code fields are 2 bits");
+    constexpr int KN = KD * KH * KW;
+    constexpr int LAST = ((KD - 1) << 4) | ((KH - 1) << 2) | (KW - 1);
+    constexpr int NC = (SPAN + 1) / 2;            // dwords holding the SPAN columns
+    static_assert(NC <= NQ, "columns beyond the loaded dwords");
+    auto h2 = [&](int dd, int hh, int i) { return __builtin_bit_cast(half2_t, q[dd][hh][i]); };
+    auto hv = [&](int dd, int hh, int j) { return h2(dd, hh, j / 2)[j % 2]; };
+
+    // column maxima over the KD*KH rows, then each window's KW columns
+    half2_t cm[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        half2_t m = h2(0, 0, i);
+#pragma unroll
+        for (int r = 1; r < KD * KH; ++r) m = __builtin_elementwise_maximum(m, h2(r / KH, r % KH, i));
+        cm[i] = m;
+    }
+    _Float16 mx[V];
+    bool nan = false;
+#pragma unroll
+    for (int o = 0; o < V; ++o) {
+        _Float16 m = cm[(o * SW) / 2][(o * SW) % 2];
+#pragma unroll
+        for (int ww = 1; ww < KW; ++ww) {
+            const int j = o * SW + ww;
+            m = __builtin_elementwise_maximum(m, cm[j / 2][j % 2]);
+        }
+        mx[o] = m;
+        nan |= m != m;
+    }
+    if (nan) return false;
+
+    int32_t c4[V];
+#pragma unroll
+    for (int o = 0; o < V; ++o) c4[o] = LAST;
+#pragma unroll
+    for (int k = KN - 2; k >= 0; --k) {
+        const int dd = k / (KH * KW), hh = (k / KW) % KH, ww = k % KW;
+#pragma unroll
+        for (int o = 0; o < V; ++o)
+            c4[o] = hv(dd, hh, o * SW + ww) == mx[o] ? ((dd << 4) | (hh << 2) | ww) : c4[o];
+    }
+#pragma unroll
+    for (int o = 0; o < V; ++o) {
+        io[o] = at0 + o * SW + rel(c4[o] >> 4, (c4[o] >> 2) & 3, c4[o] & 3);
+        yo[o] = __builtin_bit_cast(uint16_t, mx[o]);
+        // -0 and +0 compare equal, so c4 names the first zero; its sign comes
+        // from the element itself (an L1/L2 hit)
+        if (mx[o] == (_Float16)0 && active) yo[o] = xp[io[o]];
+    }
+    return true;
+}
+
 // Scan the window of output o (0 <= o < V) over the thread's registers:
 // first maximum in d, h, w order, NaN ranking above every number.  Returns
 // the value and the window-relative code (dd * KH + hh) * KW + ww.
-template <int KD, int KH, int KW, int SW, int SPAN>
-__device__ __forceinline__ float scan_window(const float (&v)[KD][KH][SPAN], int o, int &code)
+template <typename T, int KD, int KH, int KW, int SW, typename El>
+__device__ __forceinline__ float scan_window(El el, int o, int &code)
 {
-    float best = v[0][0][o * SW];
+    float best = T::widen(el(0, 0, o * SW));
     code = 0;
 #pragma unroll
     for (int dd = 0; dd < KD; ++dd)
@@ -41,7 +109,7 @@ __device__ __forceinline__ float scan_window(const float (&v)[KD][KH][SPAN], int
 #pragma unroll
             for (int ww = 0; ww < KW; ++ww) {
                 if (dd == 0 && hh == 0 && ww == 0) continue;
-                const float c = v[dd][hh][o * SW + ww];
+                const float c = T::widen(el(dd, hh, o * SW + ww));
                 // strictly greater, or NaN over a non-NaN best
                 const bool take = (best == best) && !(c <= best);
                 best = take ? c : best;
@@ -95,55 +163,80 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
     const R *xp = x + (int64_t)plane * p.g.in_plane;
     const R *base = xp + (d0 * H + h0) * W + w0;
 
-    float v[KD][KH][SPAN];
+    // The thread's input rows as raw dwords, NQ per row; with NX > 0 the
+    // last dword of a row holds the spill columns.
+    constexpr int EPD = 4 / (int)sizeof(R);      // elements per dword
+    constexpr int NQ = NV * 4 + (NX > 0 ? 1 : 0);
+    uint32_t q[KD][KH][NQ];
 #pragma unroll
     for (int dd = 0; dd < KD; ++dd) {
 #pragma unroll
         for (int hh = 0; hh < KH; ++hh) {
             const R *row_p = base + (dd * H + hh) * W;
-            u32x4 q[NV];
+            u32x4 vq[NV];
 #pragma unroll
-            for (int j = 0; j < NV; ++j) q[j] = u32x4{0u, 0u, 0u, 0u};
+            for (int j = 0; j < NV; ++j) vq[j] = u32x4{0u, 0u, 0u, 0u};
             if (active) {                 // idle lanes load nothing and scan zeros
 #pragma unroll
-                for (int j = 0; j < NV; ++j) q[j] = *reinterpret_cast<const u32x4 *>(row_p + j * VE);
+                for (int j = 0; j < NV; ++j) vq[j] = *reinterpret_cast<const u32x4 *>(row_p + j * VE);
             }
 #pragma unroll
-            for (int j = 0; j < NV; ++j) T::unpack(q[j], &v[dd][hh][j * VE]);
-            const u32x4 q0 = q[0];
+            for (int j = 0; j < NV; ++j) {
+                const u32x4 t = vq[j];
+                q[dd][hh][4 * j] = t.x;
+                q[dd][hh][4 * j + 1] = t.y;
+                q[dd][hh][4 * j + 2] = t.z;
+                q[dd][hh][4 * j + 3] = t.w;
+            }
             if constexpr (NX > 0) {
                 // the next group's first columns, across lanes (ds_bpermute)
-                const uint32_t nb = __shfl_down((uint32_t)q0.x, 1);
+                const uint32_t nb = __shfl_down(q[dd][hh][0], 1);
                 const bool in_wave = p.rpw > 0 || lane != 63;
+                uint32_t sp = 0;
+                if (g + 1 < G && in_wave) {
+                    sp = nb;
+                } else if (p.spill_load && active) {
+                    // row end, or the wave's last lane
 #pragma unroll
-                for (int j = 0; j < NX; ++j) {
-                    float f = 0.0f;
-                    if (g + 1 < G && in_wave) {
-                        if constexpr (sizeof(R) == 4)
-                            f = __builtin_bit_cast(float, nb);
-                        else
-                            f = T::widen((R)(j == 0 ? (nb & 0xffffu) : (nb >> 16)));
-                    } else if (p.spill_load && active && w0 + NV * VE + j < W) {
-                        f = T::widen(row_p[NV * VE + j]);   // row end, or the wave's last lane
+                    for (int j = 0; j < NX; ++j) {
+                        if (w0 + NV * VE + j < W) {
+                            const R r = row_p[NV * VE + j];
+                            uint32_t b;
+                            if constexpr (EPD == 1) b = __builtin_bit_cast(uint32_t, r);
+                            else b = (uint32_t)r;
+                            sp |= b << (16 * j);
+                        }
                     }
-                    v[dd][hh][NV * VE + j] = f;
                 }
+                q[dd][hh][NV * 4] = sp;
             }
         }
     }
+    // element j of row (dd, hh)
+    auto el = [&](int dd, int hh, int j) -> R {
+        if constexpr (EPD == 1) return __builtin_bit_cast(float, q[dd][hh][j]);
+        else return (R)(q[dd][hh][j / 2] >> (16 * (j % 2)));
+    };
+
+    // offset of window element (dd, hh, ww) from the window's first element
+    auto rel = [&](int dd, int hh, int ww) { return (dd * H + hh) * W + ww; };
+    const int32_t at0 = (d0 * H + h0) * W + w0;
 
     R yo[V];
     int32_t io[V];
+    bool done = false;
+    if constexpr (T::code == F16::code) done = f16_first_max<KD, KH, KW, SW, SPAN, V, NQ>(q, rel, xp, at0, active, io, yo);
+    if (!done) {
 #pragma unroll
-    for (int o = 0; o < V; ++o) {
-        int code;
-        const float best = scan_window<KD, KH, KW, SW, SPAN>(v, o, code);
-        const int dd = code / (KH * KW), hh = (code / KW) % KH, ww = code % KW;
-        io[o] = ((d0 + dd) * H + h0 + hh) * W + w0 + o * SW + ww;
-        if (T::exact_nan || best == best || !active)
-            yo[o] = T::back(best);
-        else
-            yo[o] = xp[io[o]];            // NaN: copy the element's own bits
+        for (int o = 0; o < V; ++o) {
+            int code;
+            const float best = scan_window<T, KD, KH, KW, SW>(el, o, code);
+            io[o] = at0 + o * SW + rel(code / (KH * KW), (code / KW) % KH, code % KW);
+            if (T::exact_nan || best == best || !active)
+                yo[o] = T::back(best);
+            else
+                yo[o] = xp[io[o]];            // NaN: copy the element's own bits
+        }
     }
 
     const int64_t obase = (int64_t)row * OW + ow0;    // rows are consecutive in y / idx

@@ -69,6 +69,16 @@ def draw(shape, dtype: int, kind: str, seed: int) -> np.ndarray:
     elif kind == "distinct":
         # a random permutation of 0..n-1: no two elements equal
         t = torch.randperm(n, generator=g).float() - n / 2
+    elif kind == "zeros":
+        # signed zeros among negatives: many windows whose maximum is a zero
+        t = torch.tensor([-2.0, -1.0, -0.0, 0.0])[torch.randint(0, 4, (n,), generator=g)]
+    elif kind == "sparse_nan":
+        # few NaN and infinities: most windows hold none
+        t = torch.randn(n, generator=g)
+        u = torch.rand(n, generator=g)
+        t[u < 2e-3] = float("inf")
+        t[(u >= 2e-3) & (u < 4e-3)] = -float("inf")
+        t[u > 1 - 5e-4] = float("nan")
     elif kind == "special":
         t = torch.randn(n, generator=g)
         pick = torch.randint(0, 12, (n,), generator=g)

@@ -77,7 +77,7 @@ def test_small_forward_backward(orc, case, dtype):
     shape, out, k, s = case
     code = _gpu.CODE[dtype]
     base = abs(hash((shape, out, k, s))) % 10000
-    for j, kind in enumerate(("normal", "ties", "special")):
+    for j, kind in enumerate(("normal", "ties", "zeros", "sparse_nan", "special")):
         x = _pins.from_storage(_pins.draw(shape, code, kind, base + j), code)
         y, idx = _gpu.gpu_forward(x, out, k, s)
         yo, io = _gpu.oracle_forward(orc, x, out, k, s)
