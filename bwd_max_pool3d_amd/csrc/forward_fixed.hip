@@ -168,35 +168,51 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
     constexpr int EPD = 4 / (int)sizeof(R);      // elements per dword
     constexpr int NQ = NV * 4 + (NX > 0 ? 1 : 0);
     uint32_t q[KD][KH][NQ];
+    // every row's vector loads first, so that all of them are in flight
+    // together (the spill handling below waits for them)
+    u32x4 vq[KD][KH][NV];
+#pragma unroll
+    for (int dd = 0; dd < KD; ++dd)
+#pragma unroll
+        for (int hh = 0; hh < KH; ++hh)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) vq[dd][hh][j] = u32x4{0u, 0u, 0u, 0u};
+    if (active) {                         // idle lanes load nothing and scan zeros
+#pragma unroll
+        for (int dd = 0; dd < KD; ++dd)
+#pragma unroll
+            for (int hh = 0; hh < KH; ++hh)
+#pragma unroll
+                for (int j = 0; j < NV; ++j)
+                    vq[dd][hh][j] = *reinterpret_cast<const u32x4 *>(base + (dd * H + hh) * W + j * VE);
+    }
 #pragma unroll
     for (int dd = 0; dd < KD; ++dd) {
 #pragma unroll
         for (int hh = 0; hh < KH; ++hh) {
-            const R *row_p = base + (dd * H + hh) * W;
-            u32x4 vq[NV];
-#pragma unroll
-            for (int j = 0; j < NV; ++j) vq[j] = u32x4{0u, 0u, 0u, 0u};
-            if (active) {                 // idle lanes load nothing and scan zeros
-#pragma unroll
-                for (int j = 0; j < NV; ++j) vq[j] = *reinterpret_cast<const u32x4 *>(row_p + j * VE);
-            }
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
-                const u32x4 t = vq[j];
+                const u32x4 t = vq[dd][hh][j];
                 q[dd][hh][4 * j] = t.x;
                 q[dd][hh][4 * j + 1] = t.y;
                 q[dd][hh][4 * j + 2] = t.z;
                 q[dd][hh][4 * j + 3] = t.w;
             }
-            if constexpr (NX > 0) {
-                // the next group's first columns, across lanes (ds_bpermute)
+        }
+    }
+    if constexpr (NX > 0) {
+        // the next group's first columns, across lanes (ds_bpermute); at a
+        // row end, or in the wave's last lane, from memory
+        const bool from_lane = g + 1 < G && (p.rpw > 0 || lane != 63);
+        const bool from_mem = !from_lane && p.spill_load && active;
+#pragma unroll
+        for (int dd = 0; dd < KD; ++dd) {
+#pragma unroll
+            for (int hh = 0; hh < KH; ++hh) {
                 const uint32_t nb = __shfl_down(q[dd][hh][0], 1);
-                const bool in_wave = p.rpw > 0 || lane != 63;
-                uint32_t sp = 0;
-                if (g + 1 < G && in_wave) {
-                    sp = nb;
-                } else if (p.spill_load && active) {
-                    // row end, or the wave's last lane
+                uint32_t sp = from_lane ? nb : 0u;
+                if (from_mem) {
+                    const R *row_p = base + (dd * H + hh) * W;
 #pragma unroll
                     for (int j = 0; j < NX; ++j) {
                         if (w0 + NV * VE + j < W) {
