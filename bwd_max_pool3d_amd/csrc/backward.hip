@@ -27,15 +27,6 @@ namespace mp3d {
 
 namespace {
 
-// Blocks are dealt to the 8 XCDs round-robin by block id; renumber them so
-// that each XCD walks one contiguous run of tiles (tiles of one plane re-read
-// the windows on their borders through that XCD's L2).
-__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks)
-{
-    if (nblocks % 8u) return b;
-    return (b % 8u) * (nblocks / 8u) + b / 8u;
-}
-
 // Pack VE rounded accumulator values into one 16-byte store.
 template <typename T>
 __device__ __forceinline__ u32x4 pack16(const float *a)

@@ -24,15 +24,6 @@ namespace mp3d {
 
 namespace {
 
-// Blocks are dealt to the 8 XCDs round-robin by block id; renumber them so
-// that each XCD walks one contiguous run of tiles (neighbouring tiles share
-// halo rows through that XCD's L2).
-__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks)
-{
-    if (nblocks % 8u) return b;
-    return (b % 8u) * (nblocks / 8u) + b / 8u;
-}
-
 __device__ __forceinline__ bool better(float v, float best) {
     return v > best || (v != v && best == best);
 }

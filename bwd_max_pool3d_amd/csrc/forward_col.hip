@@ -1,23 +1,26 @@
 // forward_col.hip -- forward for any window rule (fixed or adaptive) when
 // whole H*W slices can be read as 16-byte vectors, the windows along D are
-// at most MAXKD wide, and the tile's D-partials fit in LDS.
+// at most 8 wide, and a tile's D-partials fit in LDS.
 //
 // Same definition as the other forward kernels ("Struct Maxpool3dForward",
 // teenygrad, description; PR #308 page, Summary): per window, the first
 // maximum in d, h, w scan order, NaN ranking above every number.
 //
-// The reduction is split by axis so that every memory access is coalesced
-// and conflict-free:
-//  stage D (registers): a workgroup owns one plane and a run of output
-//    slices od.  Thread i owns the 16-byte column groups i, i+256, ... of
-//    the H*W slice.  For each od it loads the window's slices of its column
-//    straight from HBM (the next window's loads are issued before the
-//    current window is reduced), and reduces them element-wise into
-//    (value, first d) pairs, written to LDS in slice layout.  A slice shared
-//    by two windows is re-read from L2, not HBM.
-//  stage HW (LDS): each output scans its h, w window over the D-partials in
-//    ascending order; among equal values the smaller d wins, so the result
-//    is the first maximum in (d, h, w) order.
+// A workgroup owns one plane and a run of output slices od.  The reduction
+// is split by axis so that every memory access is coalesced:
+//  stage D (registers): thread i owns the 16-byte column groups i,
+//    i + 256, ... of the H*W slice.  For each od it loads the window's
+//    slices of its column (the next window's loads are issued before the
+//    current window is reduced; a slice shared by two windows is read
+//    twice, the second time from L2), and reduces them element-wise to the
+//    first maximum over d, written to LDS as the value and its d offset.
+//  stage HW (LDS): each output takes the maximum of the D-partials over its
+//    h, w window, then the smallest key d << 24 | (h * W + w) among the
+//    partials equal to it: the smallest d, then the first (h, w) in scan
+//    order, which is the first maximum in (d, h, w) order.
+// Both stages find a maximum first (IEEE 754-2019 maximum, NaN when an
+// operand is NaN) and its first position second; windows holding a NaN take
+// the first NaN instead, on a path of their own.
 #include "dtype.hpp"
 #include "kernels.hpp"
 
@@ -25,10 +28,11 @@ namespace mp3d {
 
 namespace {
 
-// Loads of one window's slices of one column group: slot j holds slice
-// ds + j while j < n.  Plain (cached) loads: a slice shared by two
-// neighbouring windows is then served from L2 the second time; streaming
-// loads bypass L2 and read it from HBM again.
+// One window's slices of one column group: slot j holds slice ds + j for
+// j < n and repeats slice ds + n - 1 beyond.  The loads carry no branch, so
+// that every load of a tile is in flight at once; a repeated slice never
+// comes first among equal values.  Plain (cached) loads: a slice shared by
+// two neighbouring windows is served from L2 the second time.
 template <int MAXKD>
 struct ColWin {
     u32x4 q[MAXKD];
@@ -40,38 +44,45 @@ __device__ __forceinline__ void col_load(ColWin<MAXKD> &w, const R *__restrict__
 {
 #pragma unroll
     for (int j = 0; j < MAXKD; ++j)
-        if (j < n) w.q[j] = *reinterpret_cast<const u32x4 *>(col + (int64_t)j * hw);
+        w.q[j] = *reinterpret_cast<const u32x4 *>(col + (int64_t)min(j, n - 1) * hw);
 }
 
-// Element-wise first maximum over the n loaded slices; writes the values
-// and the winning slice offset (0..n-1) of the VE elements to LDS.
+// Element-wise first maximum over the window's slots: writes the values and
+// the winning slot (the d offset in the window) to LDS.
 template <typename T, int MAXKD>
-__device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, int32_t n, float *pv,
-                                           uint8_t *pd)
+__device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, float *pv, uint8_t *pd)
 {
     constexpr int VE = 16 / (int)sizeof(typename T::raw);
-    float best[VE];
-    int32_t bd[VE];
-    T::unpack(w.q[0], best);
+    float v[MAXKD][VE];
 #pragma unroll
-    for (int i = 0; i < VE; ++i) bd[i] = 0;
-#pragma unroll
-    for (int j = 1; j < MAXKD; ++j) {
-        if (j < n) {
-            float v[VE];
-            T::unpack(w.q[j], v);
-#pragma unroll
-            for (int i = 0; i < VE; ++i) {
-                const bool take = (best[i] == best[i]) && !(v[i] <= best[i]);
-                best[i] = take ? v[i] : best[i];
-                bd[i] = take ? j : bd[i];
-            }
-        }
-    }
+    for (int j = 0; j < MAXKD; ++j) T::unpack(w.q[j], v[j]);
 #pragma unroll
     for (int i = 0; i < VE; ++i) {
-        pv[i] = best[i];
-        pd[i] = (uint8_t)bd[i];
+        float m = v[0][i];
+#pragma unroll
+        for (int j = 1; j < MAXKD; ++j) m = __builtin_elementwise_maximum(m, v[j][i]);
+        // the first slot equal to the maximum (the first NaN when it is
+        // NaN), found from the last slot back; the value is taken from the
+        // slot itself, which keeps the sign of a zero and a NaN's bits
+        int32_t jd = MAXKD - 1;
+        float val = v[MAXKD - 1][i];
+        if (m == m) {
+#pragma unroll
+            for (int j = MAXKD - 2; j >= 0; --j) {
+                const bool hit = v[j][i] == m;
+                jd = hit ? j : jd;
+                val = hit ? v[j][i] : val;
+            }
+        } else {
+#pragma unroll
+            for (int j = MAXKD - 2; j >= 0; --j) {
+                const bool hit = v[j][i] != v[j][i];
+                jd = hit ? j : jd;
+                val = hit ? v[j][i] : val;
+            }
+        }
+        pv[i] = val;
+        pd[i] = (uint8_t)jd;
     }
 }
 
@@ -87,12 +98,12 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
     const int32_t H = B.X, W = Cw.X, HW = H * W;
     const int32_t tid = threadIdx.x;
 
-    // LDS: window table (oh then ow) | D-partial values | D-partial offsets
+    // LDS: window table (oh then ow) | D-partial values | D-partial d offsets
     int2 *tab = reinterpret_cast<int2 *>(smem);
     float *pv = reinterpret_cast<float *>(smem + p.tab_bytes);
     uint8_t *pd = reinterpret_cast<uint8_t *>(smem + p.tab_bytes + p.pv_bytes);
 
-    const uint32_t t = blockIdx.x;
+    const uint32_t t = xcd_local_block(blockIdx.x, gridDim.x);
     const uint32_t plane = p.ntd_div.div(t);
     const int32_t td = (int32_t)(t - plane * (uint32_t)p.ntd);
     const int32_t od0 = td * p.tod, od1 = min(od0 + p.tod, A.O);
@@ -103,30 +114,26 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         tab[j] = j < B.O ? make_int2(B.start(j), B.end(j))
                          : make_int2(Cw.start(j - B.O), Cw.end(j - B.O));
 
-    // stage D
+    // stage D: the loads of two windows in flight while the previous one
+    // is reduced
     const int32_t ngroups = HW / VE;
     for (int32_t gi = tid; gi < ngroups; gi += kBlock) {
         const R *col = xp + gi * VE;
         ColWin<MAXKD> wa, wb;
         int32_t ds = A.start(od0);
-        int32_t na = A.end(od0) - ds;
-        col_load<R, MAXKD>(wa, col + (int64_t)ds * HW, HW, na);
+        col_load<R, MAXKD>(wa, col + (int64_t)ds * HW, HW, A.end(od0) - ds);
         for (int32_t odl = 0; odl < cd; odl += 2) {
-            int32_t nb = 0, dsb = 0;
             if (odl + 1 < cd) {
-                dsb = A.start(od0 + odl + 1);
-                nb = A.end(od0 + odl + 1) - dsb;
-                col_load<R, MAXKD>(wb, col + (int64_t)dsb * HW, HW, nb);
+                ds = A.start(od0 + odl + 1);
+                col_load<R, MAXKD>(wb, col + (int64_t)ds * HW, HW, A.end(od0 + odl + 1) - ds);
             }
-            col_reduce<T, MAXKD>(wa, na, pv + odl * HW + gi * VE, pd + odl * HW + gi * VE);
+            col_reduce<T, MAXKD>(wa, pv + odl * HW + gi * VE, pd + odl * HW + gi * VE);
             if (odl + 2 < cd) {
                 ds = A.start(od0 + odl + 2);
-                na = A.end(od0 + odl + 2) - ds;
-                col_load<R, MAXKD>(wa, col + (int64_t)ds * HW, HW, na);
+                col_load<R, MAXKD>(wa, col + (int64_t)ds * HW, HW, A.end(od0 + odl + 2) - ds);
             }
             if (odl + 1 < cd)
-                col_reduce<T, MAXKD>(wb, nb, pv + (odl + 1) * HW + gi * VE,
-                                     pd + (odl + 1) * HW + gi * VE);
+                col_reduce<T, MAXKD>(wb, pv + (odl + 1) * HW + gi * VE, pd + (odl + 1) * HW + gi * VE);
         }
     }
     __syncthreads();
@@ -143,32 +150,36 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         const int2 wh = tab[oh], ww = tab[B.O + ow];
         const float *sv = pv + odl * HW;
         const uint8_t *sd = pd + odl * HW;
-        int32_t bi = wh.x * W + ww.x;
-        float best = sv[bi];
-        int32_t bd = sd[bi];
+        float m = sv[wh.x * W + ww.x];
         for (int32_t h = wh.x; h < wh.y; ++h) {
 #pragma unroll 4
-            for (int32_t w = ww.x; w < ww.y; ++w) {
-                const int32_t i = h * W + w;
-                const float v = sv[i];
-                const int32_t d = sd[i];
-                const bool vnan = v != v, bnan = best != best;
-                // larger value; or an equal value (or NaN against a NaN best)
-                // from an earlier slice; or the first NaN
-                const bool take = (v > best) || ((v == best || (vnan && bnan)) && d < bd) ||
-                                  (vnan && !bnan);
-                best = take ? v : best;
-                bd = take ? d : bd;
-                bi = take ? i : bi;
+            for (int32_t w = ww.x; w < ww.y; ++w) m = __builtin_elementwise_maximum(m, sv[h * W + w]);
+        }
+        uint32_t bk = 0xffffffffu;
+        if (m == m) {
+            for (int32_t h = wh.x; h < wh.y; ++h) {
+#pragma unroll 4
+                for (int32_t w = ww.x; w < ww.y; ++w) {
+                    const int32_t i = h * W + w;
+                    bk = min(bk, sv[i] == m ? ((uint32_t)sd[i] << 24) | (uint32_t)i : 0xffffffffu);
+                }
+            }
+        } else {
+            for (int32_t h = wh.x; h < wh.y; ++h) {
+                for (int32_t w = ww.x; w < ww.y; ++w) {
+                    const int32_t i = h * W + w;
+                    bk = min(bk, sv[i] != sv[i] ? ((uint32_t)sd[i] << 24) | (uint32_t)i : 0xffffffffu);
+                }
             }
         }
-        const int32_t dwin = A.start(od0 + (int32_t)odl) + bd;
-        const int32_t pos = dwin * HW + bi;
+        const int32_t bi = (int32_t)(bk & 0xffffffu);
+        const int32_t pos = (A.start(od0 + (int32_t)odl) + (int32_t)(bk >> 24)) * HW + bi;
+        const float best = sv[bi];        // the element itself: keeps the sign of a zero
         R raw;
         if (T::exact_nan || best == best)
             raw = T::back(best);
         else
-            raw = xp[pos];            // NaN: copy the element's own bits
+            raw = xp[pos];                // NaN: copy the element's own bits
         st_stream(y + obase + e, raw);
         st_stream(idx + obase + e, pos);
     }
@@ -178,8 +189,9 @@ template <typename T, int MAXKD>
 hipError_t launch_col(const void *x, void *y, int32_t *idx, const ColPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
-    hipLaunchKernelGGL((fwd_col_kernel<T, MAXKD>), dim3(p.ntiles), dim3(kBlock), p.lds_bytes, s,
-                       (const R *)x, (R *)y, idx, p);
+    int64_t grid = p.ntiles;
+    hipLaunchKernelGGL((fwd_col_kernel<T, MAXKD>), dim3((uint32_t)grid), dim3(kBlock),
+                       p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
 

@@ -18,14 +18,6 @@ namespace mp3d {
 
 namespace {
 
-// Blocks are dealt to the 8 XCDs round-robin by block id; renumber them so
-// that each XCD walks one contiguous run of the work.
-__device__ inline uint32_t xcd_local_block(uint32_t b, uint32_t nblocks)
-{
-    if (nblocks % 8u) return b;
-    return (b % 8u) * (nblocks / 8u) + b / 8u;
-}
-
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // Binary16 windows without NaN, in two passes over the registers: each

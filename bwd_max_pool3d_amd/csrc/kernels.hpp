@@ -74,6 +74,15 @@ struct ColPlan {
     uint32_t tab_bytes, pv_bytes, lds_bytes;
 };
 
+// Workgroups are dealt to the 8 XCDs round-robin by workgroup id; renumber
+// them so that each XCD walks one contiguous run of the work (and shares
+// its L2 across neighbouring tiles).
+__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks)
+{
+    if (nblocks % 8u) return b;
+    return (b % 8u) * (nblocks / 8u) + b / 8u;
+}
+
 size_t lds_limit();
 int device_cus();      // compute units of the current device
 

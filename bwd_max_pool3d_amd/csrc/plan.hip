@@ -154,7 +154,8 @@ bool plan_col(const Geom &g, int es, const void *x, ColPlan *p)
 {
     const Axis &A = g.ax[0], &B = g.ax[1], &Cw = g.ax[2];
     const int64_t HW = (int64_t)B.X * Cw.X;
-    if ((HW * es) % 16 || (uintptr_t)x % 16) return false;
+    // keys hold the offset in the slice in 24 bits
+    if ((HW * es) % 16 || (uintptr_t)x % 16 || HW >= ((int64_t)1 << 24)) return false;
     // widest window along D (all windows of a fixed axis have width k)
     int64_t maxkd = A.k;
     if (!A.k) {
@@ -165,8 +166,9 @@ bool plan_col(const Geom &g, int es, const void *x, ColPlan *p)
     const int64_t cap = std::min<int64_t>(kLdsCap, (int64_t)lds_limit());
     const int64_t tab = ((int64_t)(B.O + Cw.O) * 8 + 15) & ~(int64_t)15;
     if (tab > 16 * 1024) return false;
-    const int64_t per_slice = ((HW * 4 + 15) & ~(int64_t)15) + HW;   // value + offset
-    int32_t tod = (int32_t)std::min<int64_t>(A.O, (cap - tab - 16) / per_slice);
+    // per output slice: D-partial value + d offset
+    const int64_t per_slice = HW * 5 + 16;
+    int32_t tod = (int32_t)std::min<int64_t>(A.O, (cap - tab) / per_slice);
     if (tod < 1) return false;
     const int64_t per_plane = cdiv(kWantTiles, std::max<int64_t>(g.planes, 1));
     tod = std::min<int32_t>(tod, (int32_t)std::max<int64_t>(1, A.O / per_plane));
