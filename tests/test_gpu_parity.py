@@ -49,6 +49,10 @@ CASES = [
     ((2, 1, 3, 5, 1032), None, (3, 3, 3), (2, 2, 2)),     # rows wider than a wave
     ((1, 1, 7, 300, 300), None, (2, 3, 3), (2, 2, 2)),    # slices larger than LDS
     ((1, 1, 2, 1, 70000), None, (1, 1, 5), (1, 1, 3)),    # rows larger than LDS
+    ((1, 2, 6, 7, 13), None, (2, 2, 2), (1, 1, 1)),       # overlap, stride 1
+    ((2, 1, 6, 7, 13), None, (3, 3, 3), (1, 1, 1)),       # three windows per element and axis
+    ((1, 1, 5, 33, 70), None, (3, 3, 3), (2, 2, 2)),      # rows not a multiple of 16 bytes
+    ((1, 2, 4, 3, 40), None, (3, 2, 3), (2, 1, 2)),       # mixed kernel and stride per axis
     ((2, 1, 3, 5000, 1), (2, 777, 1), None, None),
 ]
 
