@@ -33,6 +33,14 @@ int fail(int code, const char *fmt, ...)
     return code;
 }
 
+// MP3D_SMALL=0 turns the small-tensor kernels off, so that the general
+// kernels can be exercised on small inputs (read on every call).
+bool small_enabled()
+{
+    const char *v = getenv("MP3D_SMALL");
+    return !(v && strcmp(v, "0") == 0);
+}
+
 bool log_enabled()
 {
     static int on = -1;
@@ -118,6 +126,11 @@ int run_forward(const void *x, void *y, int32_t *idx, const Geom &g, hipStream_t
                     T::code, cp.tod, cp.ntiles, cp.maxkd, cp.lds_bytes);
         return hip_status(launch_forward_col<T>(x, y, idx, cp, s), "forward column launch");
     }
+    SmallPlan sp;
+    if (small_enabled() && plan_small_forward(g, &sp)) {
+        if (log_enabled()) fprintf(stderr, "[mp3d] forward small dtype=%d outputs=%u\n", T::code, sp.total);
+        return hip_status(launch_forward_small<T>(x, y, idx, sp, s), "forward small launch");
+    }
     FwdPlan p;
     if (plan_forward(g, (int)sizeof(typename T::raw), &p)) {
         if (log_enabled())
@@ -148,6 +161,11 @@ int run_backward(const void *gy, const int32_t *idx, void *gx, const Geom &g, bo
         GatherPlan p{g, g.ax[0].X / g.ax[0].O, g.ax[1].X / g.ax[1].O, g.ax[2].X / g.ax[2].O};
         if (log_enabled()) fprintf(stderr, "[mp3d] backward gather dtype=%d\n", T::code);
         return hip_status(launch_backward_gather<T>(gy, idx, gx, p, s), "backward gather launch");
+    }
+    SmallPlan sp;
+    if (small_enabled() && plan_small_backward(g, &sp)) {
+        if (log_enabled()) fprintf(stderr, "[mp3d] backward small dtype=%d inputs=%u\n", T::code, sp.total);
+        return hip_status(launch_backward_small<T>(gy, idx, gx, sp, s), "backward small launch");
     }
     BwdPlan p;
     plan_backward(g, &p);

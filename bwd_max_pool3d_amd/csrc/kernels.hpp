@@ -42,6 +42,18 @@ struct BwdPlan {
     uint32_t lds_bytes;
 };
 
+// Small tensors with small windows (small.hip): one thread per output
+// (forward) or per input element (backward).  total < 2^31 threads.
+constexpr int kSmallK = 3;                 // forward: widest window per axis
+constexpr int64_t kSmallFwd = 1 << 18;     // forward: at most this many outputs
+constexpr int64_t kSmallBwd = 1 << 20;     // backward: at most this many input elements
+struct SmallPlan {
+    Geom g;
+    uint32_t total;            // threads
+    FastDiv plane_div;         // by out_plane (forward) or in_plane (backward)
+    FastDiv a2_div, a1_div;    // by the W extent, then the H extent (outputs or inputs)
+};
+
 // Backward gather path (windows tile every axis): q = X / O per axis.
 struct GatherPlan {
     Geom g;
@@ -93,6 +105,8 @@ bool plan_fixed(const Geom &g, int elem_bytes, const void *x, const void *y,
 bool plan_forward(const Geom &g, int elem_bytes, FwdPlan *p);
 bool plan_col(const Geom &g, int elem_bytes, const void *x, ColPlan *p);
 bool plan_backward(const Geom &g, BwdPlan *p);
+bool plan_small_forward(const Geom &g, SmallPlan *p);
+bool plan_small_backward(const Geom &g, SmallPlan *p);
 
 template <typename T>
 hipError_t launch_forward_tile(const void *x, void *y, int32_t *idx,
@@ -109,6 +123,12 @@ hipError_t launch_forward_direct(const void *x, void *y, int32_t *idx,
 template <typename T>
 hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
                                 const BwdPlan &p, hipStream_t s);
+template <typename T>
+hipError_t launch_forward_small(const void *x, void *y, int32_t *idx,
+                                const SmallPlan &p, hipStream_t s);
+template <typename T>
+hipError_t launch_backward_small(const void *gy, const int32_t *idx, void *gx,
+                                 const SmallPlan &p, hipStream_t s);
 template <typename T>
 hipError_t launch_backward_gather(const void *gy, const int32_t *idx, void *gx,
                                   const GatherPlan &p, hipStream_t s);

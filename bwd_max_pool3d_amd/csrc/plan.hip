@@ -191,6 +191,57 @@ bool plan_col(const Geom &g, int es, const void *x, ColPlan *p)
     return true;
 }
 
+// Most windows that contain one position of the axis: 1 or 2, or 0 when
+// it may be more.
+static int32_t axis_cover(const Axis &a)
+{
+    if (a.k) return a.k <= a.s ? 1 : a.k <= 2 * a.s ? 2 : 0;
+    if (a.O > 65536) return 0;
+    int32_t c = 1;
+    for (int32_t o = 0; o + 1 < a.O; ++o) {
+        if (a.end(o) > a.start(o + 1)) c = 2;
+        if (o + 2 < a.O && a.end(o) > a.start(o + 2)) return 0;
+    }
+    return c;
+}
+
+static int64_t axis_widest(const Axis &a)
+{
+    if (a.k) return a.k;
+    if (a.O > 65536) return (int64_t)1 << 31;
+    int64_t m = 0;
+    for (int32_t o = 0; o < a.O; ++o) m = std::max<int64_t>(m, a.end(o) - a.start(o));
+    return m;
+}
+
+bool plan_small_forward(const Geom &g, SmallPlan *p)
+{
+    const int64_t total = g.planes * (int64_t)g.out_plane;
+    if (total > kSmallFwd) return false;
+    for (int a = 0; a < 3; ++a)
+        if (axis_widest(g.ax[a]) > kSmallK) return false;
+    p->g = g;
+    p->total = (uint32_t)total;
+    p->plane_div = FastDiv((uint32_t)g.out_plane);
+    p->a2_div = FastDiv((uint32_t)g.ax[2].O);
+    p->a1_div = FastDiv((uint32_t)g.ax[1].O);
+    return true;
+}
+
+bool plan_small_backward(const Geom &g, SmallPlan *p)
+{
+    const int64_t total = g.planes * (int64_t)g.in_plane;
+    if (total > kSmallBwd) return false;
+    for (int a = 0; a < 3; ++a)
+        if (!axis_cover(g.ax[a])) return false;
+    p->g = g;
+    p->total = (uint32_t)total;
+    p->plane_div = FastDiv((uint32_t)g.in_plane);
+    p->a2_div = FastDiv((uint32_t)g.ax[2].X);
+    p->a1_div = FastDiv((uint32_t)g.ax[1].X);
+    return true;
+}
+
 bool plan_backward(const Geom &g, BwdPlan *p)
 {
     const int32_t D = g.ax[0].X, H = g.ax[1].X, W = g.ax[2].X;

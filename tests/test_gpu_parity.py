@@ -75,9 +75,18 @@ def _tiles(shape, out, k, s, orc):
     return True
 
 
+@pytest.fixture(params=["any", "general"])
+def kernels(request, monkeypatch):
+    """'general' turns the small-tensor kernels off (MP3D_SMALL=0), so the
+    general kernels are checked on the same small cases."""
+    if request.param == "general":
+        monkeypatch.setenv("MP3D_SMALL", "0")
+    return request.param
+
+
 @pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
 @pytest.mark.parametrize("case", CASES, ids=_case_id)
-def test_small_forward_backward(orc, case, dtype):
+def test_small_forward_backward(orc, case, dtype, kernels):
     shape, out, k, s = case
     code = _gpu.CODE[dtype]
     base = abs(hash((shape, out, k, s))) % 10000
