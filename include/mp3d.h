@@ -101,7 +101,10 @@ int amp3d_forward(const void *x, void *y, int32_t *idx, int dtype,
  *      when the windows tile every axis: X % O == 0 and, for fixed windows,
  *      stride == X / O and kernel <= stride.  Otherwise MP3D_ENOTDIV.
  *   1  accumulate: zero-filled binary32 accumulator, atomic scatter of gy
- *      at idx, one rounding store.  Valid for every geometry.
+ *      at idx, one rounding store.  Valid for every geometry.  Small
+ *      tensors (at most 2^20 input elements, each in at most two windows
+ *      per axis) take an ordered gather instead: the same sums, added in
+ *      ascending output order, with no accumulator.
  *  -1  choose: 0 when valid, else 1.
  * Each idx[o] must lie inside window o, as the forward produces it; idx
  * values outside [0, D*H*W) are ignored (never written, never a fault),
@@ -123,6 +126,11 @@ const char *mp3d_strerror(int code);
 
 /* Message for the calling thread's most recent failed call ("" if none). */
 const char *mp3d_last_error(void);
+
+/* Environment (read by the library, never required):
+ *   MP3D_LOG=1    print the kernel path chosen for each call to stderr.
+ *   MP3D_SMALL=0  never use the small-tensor kernels (for testing the
+ *                 general kernels on small inputs; read on every call). */
 
 #ifdef __cplusplus
 }
