@@ -9,12 +9,14 @@
 //    at most one window, so every gx element is computed in one pass from
 //    the single window containing it -- no zero pass, no atomics, one
 //    coalesced store per element.
-//  * bwd_tile: when windows overlap several outputs may land on one input.
-//    Each workgroup owns a box of one plane's gx, zero-fills a binary32
-//    accumulator for it in LDS, adds every gy whose idx falls in the box
-//    with an LDS compare-and-swap loop, then rounds and stores the box once.  The
-//    zero fill, the atomic scatter and the cast of the page's scheme all
-//    happen on-chip, so HBM sees gy and idx read and gx written once.
+//  * bwd_slab / bwd_box: when windows overlap several outputs may land on
+//    one input.  Each workgroup owns a box of one plane's gx (whole slices
+//    when they fit), zero-fills a binary32 accumulator for it in LDS, adds
+//    every gy whose idx falls in the box with an LDS compare-and-swap loop,
+//    then rounds and stores the box once.  The zero fill, the atomic
+//    scatter and the cast of the page's scheme all happen on-chip, so HBM
+//    sees gy and idx read and gx written once.
+// (Small tensors take the ordered gather of small.hip instead.)
 // Accumulation is binary32 from +0 (so -0 contributions give +0) and the
 // sum is rounded once to the storage type.
 #include <algorithm>

@@ -31,7 +31,7 @@ struct FwdPlan {
 // Backward accumulate path: each workgroup owns an input box
 // [d0,d0+td) x [h0,h0+th) x [w0,w0+tw) of one plane, zero-fills a binary32
 // accumulator for it in LDS, adds every gy whose idx lands in the box with
-// LDS atomics, and stores the rounded box once.
+// an LDS compare-and-swap loop, and stores the rounded box once.
 struct BwdPlan {
     Geom g;
     int32_t td, th, tw;        // input tile extents
