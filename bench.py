@@ -21,7 +21,9 @@ Timing: K steps launched back to back between two synchronisations give
 the step time and the metric; a second pass of K steps with a HIP event
 pair around every op on its launch stream gives the per-op durations and
 the roofline of the dominant op (those events cost a few microseconds per
-op, so that pass is not the metric).
+op, so that pass is not the metric).  The values-only forward of each
+workload (no index written) is timed the same way, apart from the step, and
+reported on its own.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (planes shard across GPUs with no communication, so more GPUs are not
@@ -70,7 +72,9 @@ class Op:
 
 
 def build_ops(torch, mp, workloads):
-    fwd_ops, bwd_ops = [], []
+    """The step's ops (forwards, then backwards) and, apart from the step,
+    the values-only forward of each workload (idx NULL: |x|+|y| bytes)."""
+    fwd_ops, bwd_ops, vo_ops = [], [], []
     for wl in workloads.WORKLOADS:
         x = wl.make_x().cuda()
         N, C, D, H, W = wl.shape
@@ -89,6 +93,12 @@ def build_ops(torch, mp, workloads):
         else:
             f = (lambda x=x, wl=wl, y=y, idx=idx: mp.mp3d_forward(x, wl.kernel, wl.stride, out=(y, idx)))
         fwd_ops.append(Op(wl, "fwd", f, fbytes, nin, "forward"))
+        if wl.adaptive:
+            v = (lambda x=x, o3=o3, y=y: mp.amp3d_forward(x, o3, out=y, indices=False))
+        else:
+            v = (lambda x=x, wl=wl, y=y: mp.mp3d_forward(x, wl.kernel, wl.stride, out=y,
+                                                         indices=False))
+        vo_ops.append(Op(wl, "fwd_values", v, nin * es + nout * es, nin, "values-only forward"))
         if wl.backward:
             gy = wl.make_gy(oshape).cuda()
             gx = torch.empty(wl.shape, dtype=x.dtype, device="cuda")
@@ -96,7 +106,7 @@ def build_ops(torch, mp, workloads):
             b = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
                 gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, out=gx))
             bwd_ops.append(Op(wl, "bwd", b, bbytes, nin, "backward"))
-    return fwd_ops + bwd_ops
+    return fwd_ops + bwd_ops, vo_ops
 
 
 def cpu_baseline(target_s: float):
@@ -214,12 +224,13 @@ def main():
     torch.cuda.empty_cache()
 
     print("[bench] building inputs", file=sys.stderr, flush=True)
-    ops = build_ops(torch, mp, workloads)
+    ops, vo_ops = build_ops(torch, mp, workloads)
     if args.only:
         # forward ops must still run once so their idx feeds the backward
         for op in ops:
             op.fn()
         ops = [op for op in ops if args.only in op.name]
+        vo_ops = [op for op in vo_ops if args.only in op.name]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
@@ -258,17 +269,34 @@ def main():
             op.ms.append(e0.elapsed_time(e1))
     print("[bench] timed %d steps with per-op events" % args.steps, file=sys.stderr, flush=True)
 
+    # Values-only forwards (not part of the step): same events, K times each.
+    for op in vo_ops:
+        op.fn()
+    vo_evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in vo_ops] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for step in range(args.steps):
+        for op, (e0, e1) in zip(vo_ops, vo_evs[step]):
+            e0.record(stream)
+            op.fn()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    for step in range(args.steps):
+        for op, (e0, e1) in zip(vo_ops, vo_evs[step]):
+            op.ms.append(e0.elapsed_time(e1))
+
     ms_step = (t1 - t0) * 1e3 / args.steps
     ms_step_ev = (t3 - t2) * 1e3 / args.steps
     step_bytes = sum(op.nbytes for op in ops)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    per_op = []
-    for op in ops:
+    def op_row(op):
         avg = sum(op.ms) / len(op.ms)
-        per_op.append({"op": op.name, "ms": round(avg, 5), "bytes": op.nbytes,
-                       "GB_s": round(op.nbytes / (avg * 1e-3) / 1e9, 1),
-                       "elems_per_s": round(op.elems / (avg * 1e-3), 1),
-                       "frac_of_peak": round(op.nbytes / (avg * 1e-3) / 1e9 / PEAK_GBS, 4)})
+        return {"op": op.name, "ms": round(avg, 5), "bytes": op.nbytes,
+                "GB_s": round(op.nbytes / (avg * 1e-3) / 1e9, 1),
+                "elems_per_s": round(op.elems / (avg * 1e-3), 1),
+                "frac_of_peak": round(op.nbytes / (avg * 1e-3) / 1e9 / PEAK_GBS, 4)}
+
+    per_op = [op_row(op) for op in ops]
     dom = max(per_op, key=lambda r: r["ms"])
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -296,6 +324,7 @@ def main():
         "copy_GB_s": round(copy_gbs, 1),
         "roofline": roofline,
         "per_op": per_op,
+        "values_only_forward": [op_row(op) for op in vo_ops],
     }
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)

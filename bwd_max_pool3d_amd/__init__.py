@@ -7,6 +7,7 @@ PyTorch fallback: if the library is missing every call raises ImportError.
 
   mp3d_forward(x, kernel, stride) -> (y, idx)        fixed windows, no padding
   amp3d_forward(x, out_size) -> (y, idx)             adaptive windows
+      (indices=False: y only, no index written)
   mp3d_backward(gy, idx, in_shape, kernel=None, stride=None, overlap=-1) -> gx
   mp3d_out_size(X, k, s) -> int
 
@@ -64,7 +65,14 @@ def mp3d_out_size(X: int, k: int, s: int) -> int:
     return out.value
 
 
-def _outputs(x: torch.Tensor, shape, out):
+def _outputs(x: torch.Tensor, shape, out, indices: bool):
+    if not indices:
+        if out is None:
+            return torch.empty(shape, dtype=x.dtype, device=x.device), None
+        _check_tensor(out, "y")
+        if tuple(out.shape) != shape or out.dtype != x.dtype:
+            raise ValueError("out must be y of shape %s, dtype %s" % (shape, x.dtype))
+        return out, None
     if out is None:
         return (torch.empty(shape, dtype=x.dtype, device=x.device),
                 torch.empty(shape, dtype=torch.int32, device=x.device))
@@ -77,32 +85,34 @@ def _outputs(x: torch.Tensor, shape, out):
     return y, idx
 
 
-def mp3d_forward(x: torch.Tensor, kernel, stride=None, out=None):
-    """Fixed-window forward: returns (y, idx).  ``out`` may supply a
-    preallocated (y, idx) pair."""
+def mp3d_forward(x: torch.Tensor, kernel, stride=None, out=None, indices: bool = True):
+    """Fixed-window forward: returns (y, idx), or y alone when ``indices``
+    is False (no index is computed into memory).  ``out`` may supply a
+    preallocated (y, idx) pair, or y."""
     lib = _lib.load()
     _check_tensor(x, "x")
     k = _triple(kernel)
     s = _triple(stride if stride is not None else kernel)
     N, C, D, H, W = x.shape
     o = tuple(mp3d_out_size(X, ka, sa) for X, ka, sa in zip((D, H, W), k, s))
-    y, idx = _outputs(x, (N, C) + o, out)
-    _lib.check(lib.mp3d_forward(x.data_ptr(), y.data_ptr(), idx.data_ptr(), _code(x),
-                                N, C, D, H, W, *k, *s, _stream(x)))
-    return y, idx
+    y, idx = _outputs(x, (N, C) + o, out, indices)
+    _lib.check(lib.mp3d_forward(x.data_ptr(), y.data_ptr(), idx.data_ptr() if indices else None,
+                                _code(x), N, C, D, H, W, *k, *s, _stream(x)))
+    return (y, idx) if indices else y
 
 
-def amp3d_forward(x: torch.Tensor, out_size, out=None):
-    """Adaptive-window forward: returns (y, idx).  ``out`` may supply a
-    preallocated (y, idx) pair."""
+def amp3d_forward(x: torch.Tensor, out_size, out=None, indices: bool = True):
+    """Adaptive-window forward: returns (y, idx), or y alone when
+    ``indices`` is False.  ``out`` may supply a preallocated (y, idx) pair,
+    or y."""
     lib = _lib.load()
     _check_tensor(x, "x")
     o = _triple(out_size)
     N, C, D, H, W = x.shape
-    y, idx = _outputs(x, (N, C) + o, out)
-    _lib.check(lib.amp3d_forward(x.data_ptr(), y.data_ptr(), idx.data_ptr(), _code(x),
-                                 N, C, D, H, W, *o, _stream(x)))
-    return y, idx
+    y, idx = _outputs(x, (N, C) + o, out, indices)
+    _lib.check(lib.amp3d_forward(x.data_ptr(), y.data_ptr(), idx.data_ptr() if indices else None,
+                                 _code(x), N, C, D, H, W, *o, _stream(x)))
+    return (y, idx) if indices else y
 
 
 def mp3d_backward(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel=None,

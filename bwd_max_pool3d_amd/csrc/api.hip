@@ -145,7 +145,7 @@ int run_forward(const void *x, void *y, int32_t *idx, const Geom &g, hipStream_t
 int forward(const void *x, void *y, int32_t *idx, int dtype, const Geom &g, hipStream_t s)
 {
     if (g.planes == 0) return MP3D_OK;
-    if (!x || !y || !idx) return fail(MP3D_EINVAL, "null tensor pointer");
+    if (!x || !y) return fail(MP3D_EINVAL, "null tensor pointer");   // idx NULL: values only
     switch (dtype) {
     case MP3D_F32: return run_forward<F32>(x, y, idx, g, s);
     case MP3D_F16: return run_forward<F16>(x, y, idx, g, s);

@@ -194,7 +194,7 @@ __device__ __forceinline__ void reduce_tile(const FwdPlan &p, const Tile &tl, co
                 const int32_t bw = pw[rr * cw + owl];
                 const int64_t o = obase + ((tl.od0 + odl) * OH + tl.oh0 + ohl) * OW + tl.ow0 + owl;
                 y[o] = box[rr * lw + bw - tl.bw0];
-                idx[o] = (bd * H + bh) * W + bw;
+                if (idx) idx[o] = (bd * H + bh) * W + bw;
             }
         }
     }
@@ -294,7 +294,7 @@ fwd_direct_kernel(const typename T::raw *__restrict__ x, typename T::raw *__rest
                 }
             }
         y[e] = rbest;
-        idx[e] = pbest;
+        if (idx) idx[e] = pbest;
     }
 }
 

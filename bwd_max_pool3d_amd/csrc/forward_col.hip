@@ -181,7 +181,7 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         else
             raw = xp[pos];                // NaN: copy the element's own bits
         st_stream(y + obase + e, raw);
-        st_stream(idx + obase + e, pos);
+        if (idx) st_stream(idx + obase + e, pos);
     }
 }
 

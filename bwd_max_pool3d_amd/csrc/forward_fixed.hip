@@ -275,7 +275,7 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
         const int32_t cnt = nrow * OW;
         const int64_t first = (int64_t)row0 * OW;
         // idx: 4 per vector
-        {
+        if (idx) {
             const int32_t head = min((int32_t)((4 - first % 4) % 4), cnt);
             const int32_t nvec = (cnt - head) / 4, tail0 = head + nvec * 4;
             if (lane < head) idx[first + lane] = s_idx[wv][lane];
@@ -308,7 +308,7 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
     } else if (active) {
         if (p.vec_store && ow0 + V <= OW) {
             static_assert(V == 4, "vector store assumes four outputs");
-            st_stream(reinterpret_cast<i32x4 *>(idx + obase), i32x4{io[0], io[1], io[2], io[3]});
+            if (idx) st_stream(reinterpret_cast<i32x4 *>(idx + obase), i32x4{io[0], io[1], io[2], io[3]});
             if constexpr (sizeof(R) == 4) {
                 st_stream(reinterpret_cast<u32x4 *>(y + obase),
                           u32x4{__builtin_bit_cast(uint32_t, yo[0]), __builtin_bit_cast(uint32_t, yo[1]),
@@ -323,7 +323,7 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
             for (int o = 0; o < V; ++o) {
                 if (ow0 + o < OW) {
                     y[obase + o] = yo[o];
-                    idx[obase + o] = io[o];
+                    if (idx) idx[obase + o] = io[o];
                 }
             }
         }

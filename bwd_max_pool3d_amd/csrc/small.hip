@@ -73,7 +73,7 @@ fwd_small_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
                 pbest = take ? at[dd][hh][ww] : pbest;
             }
     y[e] = rbest;
-    idx[e] = pbest;
+    if (idx) idx[e] = pbest;
 }
 
 // One thread per input element, reached by at most two windows per axis.

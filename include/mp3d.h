@@ -72,8 +72,10 @@ enum mp3d_dtype { MP3D_F32 = 0, MP3D_F16 = 1, MP3D_BF16 = 2 };
  * description): kernel (kd, kh, kw), stride (sd, sh, sw), no padding.
  * Output extents are (D-kd)/sd+1, (H-kh)/sh+1, (W-kw)/sw+1; the caller
  * sizes y and idx from mp3d_out_size.  Writes y (dtype) and idx (int32).
- * MP3D_EINVAL if any kernel or stride is <= 0 or a kernel exceeds its
- * axis. */
+ * idx may be NULL: then only y is written (values-only forward, for callers
+ * that need no backward; y is the same as with idx).  MP3D_EINVAL if x or
+ * y is NULL with work to do, any kernel or stride is <= 0 or a kernel
+ * exceeds its axis. */
 int mp3d_forward(const void *x, void *y, int32_t *idx, int dtype,
                  int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
                  int32_t kd, int32_t kh, int32_t kw,
@@ -81,7 +83,8 @@ int mp3d_forward(const void *x, void *y, int32_t *idx, int dtype,
 
 /* Forward with adaptive windows (PR #308, Summary): output extents
  * (od, oh, ow), each >= 1 (an extent larger than its axis is allowed; the
- * windows then have width 1 or 2 and overlap).  Writes y and idx. */
+ * windows then have width 1 or 2 and overlap).  Writes y and idx; idx may
+ * be NULL, as for mp3d_forward. */
 int amp3d_forward(const void *x, void *y, int32_t *idx, int dtype,
                   int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
                   int32_t od, int32_t oh, int32_t ow, void *stream);

@@ -42,10 +42,11 @@ def out_shape(orc, shape, out=None, k=None, s=None):
     return tuple(orc.fixed_out(X, ka, sa) for X, ka, sa in zip(shape[2:], k, s))
 
 
-def gpu_forward(x: torch.Tensor, out=None, k=None, s=None, poison=True):
-    """Run the forward on the device copy of ``x``; outputs come back on
-    the CPU.  With ``poison`` the outputs start filled with NaN / -7 so an
-    unwritten element cannot pass."""
+def gpu_forward(x: torch.Tensor, out=None, k=None, s=None, poison=True, indices=True):
+    """Run the forward on the device copy of ``x``.  With ``poison`` the
+    outputs start filled with NaN / -7 so an unwritten element cannot pass.
+    With ``indices`` False the values-only forward runs (idx NULL) and y
+    alone is returned."""
     xd = x.cuda() if not x.is_cuda else x
     N, C = x.shape[:2]
     if k is None:
@@ -56,11 +57,11 @@ def gpu_forward(x: torch.Tensor, out=None, k=None, s=None, poison=True):
     if poison:
         pre = (torch.full((N, C) + o3, POISON[x.dtype], dtype=x.dtype, device=xd.device),
                torch.full((N, C) + o3, -7, dtype=torch.int32, device=xd.device))
+        if not indices:
+            pre = pre[0]
     if k is None:
-        y, idx = mp.amp3d_forward(xd, o3, out=pre)
-    else:
-        y, idx = mp.mp3d_forward(xd, k, s, out=pre)
-    return y, idx
+        return mp.amp3d_forward(xd, o3, out=pre, indices=indices)
+    return mp.mp3d_forward(xd, k, s, out=pre, indices=indices)
 
 
 def oracle_forward(orc, x: torch.Tensor, out=None, k=None, s=None):

@@ -66,7 +66,7 @@ def bwd(*, gy=FAKE, dtype=0, shape=(1, 1, 4, 4, 4), out=(2, 2, 2), k=(0, 0, 0), 
     (lambda: fwd(dtype=3), _lib.MP3D_EDTYPE),
     (lambda: fwd(dtype=-1), _lib.MP3D_EDTYPE),
     (lambda: fwd(x=None), _lib.MP3D_EINVAL),
-    (lambda: fwd(idx=None), _lib.MP3D_EINVAL),
+    (lambda: fwd(y=None), _lib.MP3D_EINVAL),            # idx NULL is allowed: values only
     (lambda: fwd(k=(0, 2, 2)), _lib.MP3D_EINVAL),
     (lambda: fwd(s=(2, 2, -1)), _lib.MP3D_EINVAL),
     (lambda: fwd(k=(5, 2, 2)), _lib.MP3D_EINVAL),

@@ -106,6 +106,23 @@ def test_small_forward_backward(orc, case, dtype, kernels):
         _gpu.check_backward(orc, gy, idx.cpu(), shape, gx1, exact=True, what="forced accumulate")
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_values_only_forward(orc, case, dtype, kernels):
+    """idx NULL: y alone, bit for bit the oracle's (and so the indexed
+    forward's), on every draw kind."""
+    shape, out, k, s = case
+    code = _gpu.CODE[dtype]
+    base = abs(hash((shape, out, k, s))) % 10000
+    for j, kind in enumerate(("normal", "ties", "zeros", "sparse_nan", "special")):
+        x = _pins.from_storage(_pins.draw(shape, code, kind, base + j), code)
+        y = _gpu.gpu_forward(x, out, k, s, indices=False)
+        assert isinstance(y, torch.Tensor)
+        yo, _ = _gpu.oracle_forward(orc, x, out, k, s)
+        assert np.array_equal(_gpu.storage(y).view(np.uint8), yo.view(np.uint8)), \
+            "%s values-only %s: y bits differ" % (_case_id(case), kind)
+
+
 @pytest.mark.parametrize("case", _golden.pr308_cases(), ids=lambda c: "%s-%s-%s" % (
     c[1], "x".join(map(str, c[2])), "x".join(map(str, c[3]))))
 def test_pr308_shapes(orc, case):
@@ -322,6 +339,12 @@ def test_workload_full_size(orc, wl):
         _gpu.assert_forward_match(y[n_:n_ + 1, c_:c_ + 1], idx[n_:n_ + 1, c_:c_ + 1], yo, io,
                                   "%s plane %d" % (wl.name, p))
     _full_properties(orc, wl, xd, y, idx)
+    # values-only forward (idx NULL): the same y, bit for bit
+    yv = _gpu.gpu_forward(xd, out, k, s, indices=False)
+    assert torch.equal(yv.view(torch.int16 if yv.element_size() == 2 else torch.int32),
+                       y.view(torch.int16 if y.element_size() == 2 else torch.int32)), \
+        "%s values-only y differs" % wl.name
+    del yv
     if not wl.backward:
         return
     gy = wl.make_gy(tuple(y.shape))
