@@ -22,8 +22,8 @@ the step time and the metric; a second pass of K steps with a HIP event
 pair around every op on its launch stream gives the per-op durations and
 the roofline of the dominant op (those events cost a few microseconds per
 op, so that pass is not the metric).  The values-only forward of each
-workload (no index written) is timed the same way, apart from the step, and
-reported on its own.
+workload (no index written) and the ordered backward (overlap=2) are timed
+the same way, apart from the step, and reported on their own.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (planes shard across GPUs with no communication, so more GPUs are not
@@ -73,7 +73,8 @@ class Op:
 
 def build_ops(torch, mp, workloads):
     """The step's ops (forwards, then backwards) and, apart from the step,
-    the values-only forward of each workload (idx NULL: |x|+|y| bytes)."""
+    the variants: the values-only forward of each workload (idx NULL:
+    |x|+|y| bytes) and the ordered (bit-reproducible) backward."""
     fwd_ops, bwd_ops, vo_ops = [], [], []
     for wl in workloads.WORKLOADS:
         x = wl.make_x().cuda()
@@ -106,6 +107,9 @@ def build_ops(torch, mp, workloads):
             b = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
                 gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, out=gx))
             bwd_ops.append(Op(wl, "bwd", b, bbytes, nin, "backward"))
+            o = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
+                gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, overlap=2, out=gx))
+            vo_ops.append(Op(wl, "bwd_ordered", o, bbytes, nin, "ordered backward"))
     return fwd_ops + bwd_ops, vo_ops
 
 
@@ -269,7 +273,7 @@ def main():
             op.ms.append(e0.elapsed_time(e1))
     print("[bench] timed %d steps with per-op events" % args.steps, file=sys.stderr, flush=True)
 
-    # Values-only forwards (not part of the step): same events, K times each.
+    # Variants (not part of the step): same events, K times each.
     for op in vo_ops:
         op.fn()
     vo_evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -324,7 +328,8 @@ def main():
         "copy_GB_s": round(copy_gbs, 1),
         "roofline": roofline,
         "per_op": per_op,
-        "values_only_forward": [op_row(op) for op in vo_ops],
+        "values_only_forward": [op_row(op) for op in vo_ops if op.kind == "fwd_values"],
+        "ordered_backward": [op_row(op) for op in vo_ops if op.kind == "bwd_ordered"],
     }
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)

@@ -9,6 +9,7 @@ PyTorch fallback: if the library is missing every call raises ImportError.
   amp3d_forward(x, out_size) -> (y, idx)             adaptive windows
       (indices=False: y only, no index written)
   mp3d_backward(gy, idx, in_shape, kernel=None, stride=None, overlap=-1) -> gx
+      (overlap=2: ordered, bit-reproducible sums)
   mp3d_out_size(X, k, s) -> int
 
 x, y, gy and gx are float32, float16 or bfloat16; idx is int32, flat within
@@ -119,8 +120,10 @@ def mp3d_backward(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel=None,
                   stride=None, overlap: int = -1, out: torch.Tensor | None = None):
     """Backward: gx of shape ``in_shape``.  ``kernel``/``stride`` None means
     adaptive windows; ``overlap`` -1 lets the library pick the gather path
-    when the windows tile every axis, 0 forces it, 1 forces accumulation.
-    ``out`` may supply a preallocated gx."""
+    when the windows tile every axis, 0 forces it, 1 forces accumulation,
+    2 asks for the ordered backward (each gx element the ascending-order
+    binary32 sum, the same bits on every run).  ``out`` may supply a
+    preallocated gx."""
     lib = _lib.load()
     _check_tensor(gy, "gy")
     _check_tensor(idx, "idx")

@@ -153,11 +153,13 @@ int forward(const void *x, void *y, int32_t *idx, int dtype, const Geom &g, hipS
     }
 }
 
+enum class BwdPath { gather, accumulate, ordered };
+
 template <typename T>
-int run_backward(const void *gy, const int32_t *idx, void *gx, const Geom &g, bool gather,
+int run_backward(const void *gy, const int32_t *idx, void *gx, const Geom &g, BwdPath path,
                  hipStream_t s)
 {
-    if (gather) {
+    if (path == BwdPath::gather) {
         GatherPlan p{g, g.ax[0].X / g.ax[0].O, g.ax[1].X / g.ax[1].O, g.ax[2].X / g.ax[2].O};
         if (log_enabled()) fprintf(stderr, "[mp3d] backward gather dtype=%d\n", T::code);
         return hip_status(launch_backward_gather<T>(gy, idx, gx, p, s), "backward gather launch");
@@ -167,12 +169,19 @@ int run_backward(const void *gy, const int32_t *idx, void *gx, const Geom &g, bo
         if (log_enabled()) fprintf(stderr, "[mp3d] backward small dtype=%d inputs=%u\n", T::code, sp.total);
         return hip_status(launch_backward_small<T>(gy, idx, gx, sp, s), "backward small launch");
     }
+    const bool ordered = path == BwdPath::ordered;
     BwdPlan p;
-    plan_backward(g, &p);
-    if (log_enabled())
-        fprintf(stderr, "[mp3d] backward accumulate dtype=%d box=(%d,%d,%d) tiles=%lld lds=%u\n",
-                T::code, p.td, p.th, p.tw, (long long)p.ntiles, p.lds_bytes);
-    return hip_status(launch_backward_tile<T>(gy, idx, gx, p, s), "backward tile launch");
+    if (plan_backward(g, ordered, &p)) {
+        if (log_enabled())
+            fprintf(stderr, "[mp3d] backward %s dtype=%d box=(%d,%d,%d) tiles=%lld lds=%u phases=%d\n",
+                    ordered ? "ordered slab" : "accumulate", T::code, p.td, p.th, p.tw,
+                    (long long)p.ntiles, p.lds_bytes, p.nphase);
+        return hip_status(launch_backward_tile<T>(gy, idx, gx, p, s), "backward tile launch");
+    }
+    OrdPlan op;
+    plan_ordered(g, &op);
+    if (log_enabled()) fprintf(stderr, "[mp3d] backward ordered gather dtype=%d\n", T::code);
+    return hip_status(launch_backward_ordered<T>(gy, idx, gx, op, s), "backward ordered launch");
 }
 
 // Windows tile an axis -- each position in exactly one window, the one
@@ -271,8 +280,8 @@ int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype, int64
 {
     int rc = check_common(dtype, N, C, D, H, W);
     if (rc) return rc;
-    if (overlap < -1 || overlap > 1)
-        return fail(MP3D_EINVAL, "overlap must be -1, 0 or 1 (got %d)", overlap);
+    if (overlap < -1 || overlap > 2)
+        return fail(MP3D_EINVAL, "overlap must be -1, 0, 1 or 2 (got %d)", overlap);
     const int64_t X[3] = {D, H, W};
     const int32_t O[3] = {od, oh, ow}, K[3] = {kd, kh, kw}, S[3] = {sd, sh, sw};
     const char *names[3] = {"D", "H", "W"};
@@ -294,12 +303,15 @@ int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype, int64
         return fail(MP3D_ENOTDIV, "overlap=0 needs windows that tile every axis");
     if (g.planes == 0) return MP3D_OK;
     if (!gy || !idx || !gx) return fail(MP3D_EINVAL, "null tensor pointer");
-    const bool gather = overlap == 0 || (overlap == -1 && tiles);
+    // the gather is already the ordered sum (one window per input)
+    const BwdPath path = overlap == 0 || ((overlap == -1 || overlap == 2) && tiles)
+                             ? BwdPath::gather
+                             : overlap == 2 ? BwdPath::ordered : BwdPath::accumulate;
     const hipStream_t s = (hipStream_t)stream;
     switch (dtype) {
-    case MP3D_F32: return run_backward<F32>(gy, idx, gx, g, gather, s);
-    case MP3D_F16: return run_backward<F16>(gy, idx, gx, g, gather, s);
-    default: return run_backward<BF16>(gy, idx, gx, g, gather, s);
+    case MP3D_F32: return run_backward<F32>(gy, idx, gx, g, path, s);
+    case MP3D_F16: return run_backward<F16>(gy, idx, gx, g, path, s);
+    default: return run_backward<BF16>(gy, idx, gx, g, path, s);
     }
 }
 

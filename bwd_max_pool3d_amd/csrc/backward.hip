@@ -63,7 +63,7 @@ __device__ __forceinline__ void lds_add(float *a, float v)
     }
 }
 
-constexpr int kRound = 8;        // windows per thread fetched per round
+constexpr int kRound = kBwdRound;          // windows per thread fetched per round
 constexpr int kSlabBlock = kSlabThreads;  // threads per slab workgroup
 
 // Round the accumulator a[0, n) into dst[0, n): 16-byte streaming stores for
@@ -99,8 +99,15 @@ __device__ __forceinline__ void store_span(typename T::raw *dst, const float *a,
 // output slices [od0, od1) that can reach the slab is one contiguous run of
 // gy and idx, and the slab is one contiguous run of gx.
 //
-// The scatter adds with lds_add (compare-and-swap).
-template <typename T, int NT>
+// ORD false: the scatter adds with lds_add (compare-and-swap), in the order
+// the swaps land.  ORD true: one round holds every window (the plan sees to
+// it); each window's class is its rank among the windows containing its
+// argmax, (rank_d * mh + rank_h) * mw + rank_w, and the classes are added
+// in ascending order, one phase each.  For one input the ranks order its
+// windows as their flat output numbers do, so each element's fold is the
+// ascending-order sum, and within a phase every input has at most one
+// window, so plain LDS read-modify-writes suffice.
+template <typename T, int NT, bool ORD>
 __global__ void __launch_bounds__(NT)
 bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
                 typename T::raw *__restrict__ gx, BwdPlan p)
@@ -149,16 +156,47 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
     for (int32_t e = tid; e < (n + shift + 3) / 4; e += NT)
         reinterpret_cast<u32x4 *>(acc)[e] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-    for (int32_t round = 0;; ++round) {
+    if constexpr (ORD) {
+        const Axis B = p.g.ax[1], Cw = p.g.ax[2];
+        const uint32_t W = (uint32_t)Cw.X, OW = (uint32_t)Cw.O;
+        int32_t cls[kRound];
 #pragma unroll
         for (int k = 0; k < kRound; ++k) {
+            const uint32_t e = (uint32_t)(k * NT + tid);
             const uint32_t l = (uint32_t)ri[k] - (uint32_t)ibase;
-            if (ri[k] >= 0 && l < (uint32_t)n) lds_add(&a[l], T::widen(rg[k]));
+            cls[k] = -1;
+            if (ri[k] >= 0 && l < (uint32_t)n) {
+                const uint32_t pos = (uint32_t)ri[k];
+                const uint32_t pd = p.hw_div.div(pos), prow = pos - pd * (uint32_t)HW;
+                const uint32_t ph = p.w_div.div(prow), pw = prow - ph * W;
+                const uint32_t q = p.ohw_div.div(e), orow = e - q * (uint32_t)OHW;
+                const uint32_t oh = p.ow_div.div(orow), ow = orow - oh * OW;
+                const uint32_t rd = (uint32_t)od0 + q - (uint32_t)A.first_reaching((int32_t)pd);
+                const uint32_t rh = oh - (uint32_t)B.first_reaching((int32_t)ph);
+                const uint32_t rw = ow - (uint32_t)Cw.first_reaching((int32_t)pw);
+                // an idx outside its window gives a rank out of range: dropped
+                if (rd < (uint32_t)p.md && rh < (uint32_t)p.mh && rw < (uint32_t)p.mw)
+                    cls[k] = (int32_t)((rd * p.mh + rh) * p.mw + rw);
+            }
         }
-        if ((round + 1) * kRound * NT >= nw) break;
-        fetch(round + 1);
+        for (int32_t j = 0; j < p.nphase; ++j) {
+#pragma unroll
+            for (int k = 0; k < kRound; ++k)
+                if (cls[k] == j) a[ri[k] - ibase] += T::widen(rg[k]);
+            __syncthreads();
+        }
+    } else {
+        for (int32_t round = 0;; ++round) {
+#pragma unroll
+            for (int k = 0; k < kRound; ++k) {
+                const uint32_t l = (uint32_t)ri[k] - (uint32_t)ibase;
+                if (ri[k] >= 0 && l < (uint32_t)n) lds_add(&a[l], T::widen(rg[k]));
+            }
+            if ((round + 1) * kRound * NT >= nw) break;
+            fetch(round + 1);
+        }
+        __syncthreads();
     }
-    __syncthreads();
     store_span<T, NT>(dst, a, n, head);
 }
 
@@ -244,8 +282,12 @@ hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
         // one workgroup per slab; a multiple of 8 lets blocks map per XCD
         // (the surplus blocks exit at once)
         if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
-        hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock>), dim3((uint32_t)grid),
-                           dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
+        if (p.nphase)
+            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, true>), dim3((uint32_t)grid),
+                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
+        else
+            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, false>), dim3((uint32_t)grid),
+                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
     } else {
         hipLaunchKernelGGL(bwd_box_kernel<T>, dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
                            (const R *)gy, idx, (R *)gx, p);

@@ -32,6 +32,13 @@ struct FwdPlan {
 // [d0,d0+td) x [h0,h0+th) x [w0,w0+tw) of one plane, zero-fills a binary32
 // accumulator for it in LDS, adds every gy whose idx lands in the box with
 // an LDS compare-and-swap loop, and stores the rounded box once.
+//
+// Ordered variant (nphase > 0, slabs only): every window reaching a slab is
+// held in registers at once (one round), each gets a class -- its rank
+// among the windows that contain its argmax, lexicographic over (d, h, w)
+// -- and the classes are added one phase at a time with a barrier between
+// phases.  Two outputs of one class never share an input, so a phase needs
+// no atomics, and every element's fold runs in ascending output order.
 struct BwdPlan {
     Geom g;
     int32_t td, th, tw;        // input tile extents
@@ -40,6 +47,20 @@ struct BwdPlan {
     TileSplit split;           // tile number -> (plane, td, th, tw)
     int32_t slab;              // boxes are whole H*W slices
     uint32_t lds_bytes;
+    int32_t nphase;            // ordered: md*mh*mw phases; 0: compare-and-swap scatter
+    int32_t md, mh, mw;        // ordered: most windows containing a position, per axis
+    FastDiv hw_div, w_div;     // by H*W and W (input positions)
+    FastDiv ohw_div, ow_div;   // by OH*OW and OW (outputs)
+};
+constexpr int kBwdRound = 8;               // slab: windows per thread fetched per round
+constexpr int kMaxPhase = 64;              // ordered slab: at most this many phases
+
+// Ordered gather for any geometry (small.hip): one thread per input
+// element visits every window containing it in ascending output order.
+struct OrdPlan {
+    Geom g;
+    int64_t total;             // input elements
+    FastDiv a2_div, a1_div;    // by W, then by H
 };
 
 // Small tensors with small windows (small.hip): one thread per output
@@ -104,9 +125,14 @@ bool plan_fixed(const Geom &g, int elem_bytes, const void *x, const void *y,
 
 bool plan_forward(const Geom &g, int elem_bytes, FwdPlan *p);
 bool plan_col(const Geom &g, int elem_bytes, const void *x, ColPlan *p);
-bool plan_backward(const Geom &g, BwdPlan *p);
+// plan_backward with ordered = false always succeeds; with ordered = true
+// it fails when the ordered slab cannot hold the geometry (slices larger
+// than the accumulator, a slab reached by more windows than one round
+// holds, or more than kMaxPhase phases): the ordered gather serves then.
+bool plan_backward(const Geom &g, bool ordered, BwdPlan *p);
 bool plan_small_forward(const Geom &g, SmallPlan *p);
 bool plan_small_backward(const Geom &g, SmallPlan *p);
+void plan_ordered(const Geom &g, OrdPlan *p);
 
 template <typename T>
 hipError_t launch_forward_tile(const void *x, void *y, int32_t *idx,
@@ -132,5 +158,8 @@ hipError_t launch_backward_small(const void *gy, const int32_t *idx, void *gx,
 template <typename T>
 hipError_t launch_backward_gather(const void *gy, const int32_t *idx, void *gx,
                                   const GatherPlan &p, hipStream_t s);
+template <typename T>
+hipError_t launch_backward_ordered(const void *gy, const int32_t *idx, void *gx,
+                                   const OrdPlan &p, hipStream_t s);
 
 }  // namespace mp3d

@@ -242,7 +242,33 @@ bool plan_small_backward(const Geom &g, SmallPlan *p)
     return true;
 }
 
-bool plan_backward(const Geom &g, BwdPlan *p)
+// Most windows that contain one position of the axis (0: not known, an
+// adaptive axis with too many windows to scan).  The count only grows at
+// a window start, so scanning the starts is enough.
+static int32_t axis_depth(const Axis &a)
+{
+    if (a.k) return (int32_t)std::min<int64_t>(cdiv(a.k, a.s), a.O);
+    if (a.O > (1 << 20)) return 0;
+    int32_t m = 1;
+    for (int32_t o = 0; o < a.O; ++o) {
+        const int32_t x = a.start(o);
+        m = std::max(m, a.last_starting(x) - a.first_reaching(x) + 1);
+    }
+    return m;
+}
+
+// Most windows (output slices) reaching one slab of td slices.
+static int64_t slab_reach(const Axis &a, int32_t td)
+{
+    int64_t m = 0;
+    for (int32_t d0 = 0; d0 < a.X; d0 += td) {
+        const int32_t d1 = std::min(d0 + td, a.X);
+        m = std::max<int64_t>(m, a.last_starting(d1 - 1) + 1 - a.first_reaching(d0));
+    }
+    return m;
+}
+
+bool plan_backward(const Geom &g, bool ordered, BwdPlan *p)
 {
     const int32_t D = g.ax[0].X, H = g.ax[1].X, W = g.ax[2].X;
     const int64_t budget = std::min<int64_t>(kAccBudget, (int64_t)lds_limit() - 64);
@@ -266,6 +292,30 @@ bool plan_backward(const Geom &g, BwdPlan *p)
         const int32_t tw = (int32_t)std::min<int64_t>(W, budget / 4);
         p->tw = (int32_t)cdiv(W, cdiv(W, tw));
     }
+    p->nphase = 0;
+    p->md = p->mh = p->mw = 0;
+    if (ordered) {
+        if (!(p->th == H && p->tw == W)) return false;
+        const Axis &A = g.ax[0];
+        const int32_t md = axis_depth(A), mh = axis_depth(g.ax[1]), mw = axis_depth(g.ax[2]);
+        if (!md || !mh || !mw || (int64_t)md * mh * mw > kMaxPhase) return false;
+        if (D > (1 << 20)) return false;             // bounds the slab scans below
+        // every window reaching a slab must fit one round of the workgroup
+        const int64_t ohw = (int64_t)g.ax[1].O * g.ax[2].O;
+        const int64_t cap = (int64_t)kBwdRound * kSlabThreads;
+        int32_t td = p->td;
+        while (td > 1 && slab_reach(A, td) * ohw > cap) td = (int32_t)cdiv(D, cdiv(D, td - 1));
+        if (slab_reach(A, td) * ohw > cap) return false;
+        p->td = td;
+        p->nphase = md * mh * mw;
+        p->md = md;
+        p->mh = mh;
+        p->mw = mw;
+        p->hw_div = FastDiv((uint32_t)(H * W));
+        p->w_div = FastDiv((uint32_t)W);
+        p->ohw_div = FastDiv((uint32_t)ohw);
+        p->ow_div = FastDiv((uint32_t)g.ax[2].O);
+    }
     p->ntd = (int32_t)cdiv(D, p->td);
     p->nth = (int32_t)cdiv(H, p->th);
     p->ntw = (int32_t)cdiv(W, p->tw);
@@ -275,6 +325,14 @@ bool plan_backward(const Geom &g, BwdPlan *p)
     // + alignment shift and the rounding of the zero fill to 16 bytes
     p->lds_bytes = (uint32_t)(((int64_t)p->td * p->th * p->tw + 8) * 4);
     return true;
+}
+
+void plan_ordered(const Geom &g, OrdPlan *p)
+{
+    p->g = g;
+    p->total = g.planes * (int64_t)g.in_plane;
+    p->a2_div = FastDiv((uint32_t)g.ax[2].X);
+    p->a1_div = FastDiv((uint32_t)g.ax[1].X);
 }
 
 }  // namespace mp3d

@@ -1,12 +1,16 @@
 // small.hip -- forward and backward for small tensors with small windows,
 // where the cost is latency, not bandwidth: one thread per output (forward)
 // or per input element (backward), every load it needs issued at once.
+// Also the ordered gather for any geometry, the general fallback of the
+// ordered (bit-reproducible) backward.
 //
 // Definitions as in the other kernels: the forward takes the first maximum
 // of each window in d, h, w scan order, NaN ranking above every number
 // ("Struct Maxpool3dForward", teenygrad, description; PR #308 page,
 // Summary); the backward sets gx[p] to the sum of gy[o] over the outputs o
 // whose idx[o] is p (PR #308 page, Summary).
+#include <algorithm>
+
 #include "dtype.hpp"
 #include "kernels.hpp"
 
@@ -131,7 +135,54 @@ bwd_small_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restri
     gx[e] = T::narrow(acc);
 }
 
+// Any geometry: one thread per input element (grid-stride) visits every
+// window containing it, in ascending output order, and keeps the elements
+// whose argmax it is: the ordered binary32 sum from +0, rounded once.  The
+// general fallback of the ordered backward; loads follow one another.
+template <typename T>
+__global__ void __launch_bounds__(kBlock)
+bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
+                   typename T::raw *__restrict__ gx, OrdPlan p)
+{
+    const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
+    const int32_t OH = B.O, OW = Cw.O;
+    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < p.total;
+         e += (int64_t)gridDim.x * kBlock) {
+        const int64_t plane = e / p.g.in_plane;
+        const int32_t i = (int32_t)(e - plane * p.g.in_plane);
+        const uint32_t r = p.a2_div.div((uint32_t)i);
+        const int32_t w = i - (int32_t)r * Cw.X;
+        const uint32_t d = p.a1_div.div(r);
+        const int32_t h = (int32_t)(r - d * (uint32_t)B.X);
+        const int32_t d0 = A.first_reaching((int32_t)d), d1 = A.last_starting((int32_t)d);
+        const int32_t h0 = B.first_reaching(h), h1 = B.last_starting(h);
+        const int32_t w0 = Cw.first_reaching(w), w1 = Cw.last_starting(w);
+        const int64_t obase = plane * p.g.out_plane;
+        float acc = 0.0f;
+        for (int32_t od = d0; od <= d1; ++od)
+            for (int32_t oh = h0; oh <= h1; ++oh)
+                for (int32_t ow = w0; ow <= w1; ++ow) {
+                    const int64_t o = obase + ((int64_t)od * OH + oh) * OW + ow;
+                    const int32_t v = idx[o];
+                    const float g = T::widen(gy[o]);
+                    if (v == i) acc = acc + g;
+                }
+        gx[e] = T::narrow(acc);
+    }
+}
+
 }  // namespace
+
+template <typename T>
+hipError_t launch_backward_ordered(const void *gy, const int32_t *idx, void *gx, const OrdPlan &p,
+                                   hipStream_t s)
+{
+    using R = typename T::raw;
+    const int64_t grid = std::min<int64_t>((p.total + kBlock - 1) / kBlock, (int64_t)1 << 20);
+    hipLaunchKernelGGL(bwd_ordered_kernel<T>, dim3((uint32_t)grid), dim3(kBlock), 0, s,
+                       (const R *)gy, idx, (R *)gx, p);
+    return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_forward_small(const void *x, void *y, int32_t *idx, const SmallPlan &p,
@@ -159,5 +210,8 @@ template hipError_t launch_forward_small<BF16>(const void *, void *, int32_t *, 
 template hipError_t launch_backward_small<F32>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_small<F16>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_small<BF16>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F32>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F16>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<BF16>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
 
 }  // namespace mp3d

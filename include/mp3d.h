@@ -104,10 +104,18 @@ int amp3d_forward(const void *x, void *y, int32_t *idx, int dtype,
  *      when the windows tile every axis: X % O == 0 and, for fixed windows,
  *      stride == X / O and kernel <= stride.  Otherwise MP3D_ENOTDIV.
  *   1  accumulate: zero-filled binary32 accumulator, atomic scatter of gy
- *      at idx, one rounding store.  Valid for every geometry.  Small
- *      tensors (at most 2^20 input elements, each in at most two windows
- *      per axis) take an ordered gather instead: the same sums, added in
- *      ascending output order, with no accumulator.
+ *      at idx, one rounding store.  Valid for every geometry.  The order
+ *      of the additions into one element is not fixed, so an element
+ *      reached by three or more outputs may differ in its last bits from
+ *      run to run.  Small tensors (at most 2^20 input elements, each in at
+ *      most two windows per axis) take an ordered gather instead: the same
+ *      sums, added in ascending output order, with no accumulator.
+ *   2  ordered: every element is the binary32 sum of its contributions in
+ *      ascending output order, from +0, rounded once -- the same bits on
+ *      every run.  Valid for every geometry: the gather when the windows
+ *      tile, else the ordered gather for small tensors, else slabs whose
+ *      contributions are added rank by rank (no atomics), else the ordered
+ *      gather at any size (slower: loads one after another).
  *  -1  choose: 0 when valid, else 1.
  * Each idx[o] must lie inside window o, as the forward produces it; idx
  * values outside [0, D*H*W) are ignored (never written, never a fault),

@@ -77,7 +77,8 @@ def bwd(*, gy=FAKE, dtype=0, shape=(1, 1, 4, 4, 4), out=(2, 2, 2), k=(0, 0, 0), 
     (lambda: afwd(out=(0, 2, 2)), _lib.MP3D_EINVAL),
     (lambda: afwd(x=None), _lib.MP3D_EINVAL),
     (lambda: afwd(out=(65536, 65536, 2)), _lib.MP3D_EOVERFLOW),
-    (lambda: bwd(overlap=2), _lib.MP3D_EINVAL),
+    (lambda: bwd(overlap=3), _lib.MP3D_EINVAL),
+    (lambda: bwd(overlap=-2), _lib.MP3D_EINVAL),
     (lambda: bwd(gy=None), _lib.MP3D_EINVAL),
     (lambda: bwd(shape=(1, 1, 5, 5, 5), overlap=0), _lib.MP3D_ENOTDIV),
     (lambda: bwd(shape=(1, 1, 8, 8, 8), out=(2, 2, 2), k=(3, 3, 3), s=(3, 3, 3), overlap=0),

@@ -54,6 +54,8 @@ CASES = [
     ((1, 1, 5, 33, 70), None, (3, 3, 3), (2, 2, 2)),      # rows not a multiple of 16 bytes
     ((1, 2, 4, 3, 40), None, (3, 2, 3), (2, 1, 2)),       # mixed kernel and stride per axis
     ((2, 1, 3, 5000, 1), (2, 777, 1), None, None),
+    ((1, 2, 9, 10, 11), None, (5, 5, 5), (1, 1, 1)),      # five windows per element and axis
+    ((2, 2, 12, 20, 24), None, (3, 3, 3), (2, 2, 2)),     # several slabs per plane
 ]
 
 
@@ -104,6 +106,26 @@ def test_small_forward_backward(orc, case, dtype, kernels):
         # the accumulate path must also be exact here: one contribution per cell
         gx1 = _gpu.gpu_backward(gy, idx.cpu(), shape, k, s, overlap=1)
         _gpu.check_backward(orc, gy, idx.cpu(), shape, gx1, exact=True, what="forced accumulate")
+    # the ordered backward is exact for every geometry
+    gx2 = _gpu.gpu_backward(gy, idx.cpu(), shape, k, s, overlap=2)
+    _gpu.check_backward(orc, gy, idx.cpu(), shape, gx2, exact=True, what="ordered")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+@pytest.mark.parametrize("case", [c for c in CASES if c[2] is None or c[2] != c[3]], ids=_case_id)
+def test_ordered_backward_many_contributions(orc, case, dtype, kernels):
+    """Gradients on an idx where many outputs share an argmax (forward of
+    data whose maximum sits on window overlaps), so that the order of the
+    additions shows in the low bits: the ordered backward must match the
+    oracle's ascending-order sum bit for bit."""
+    shape, out, k, s = case
+    code = _gpu.CODE[dtype]
+    base = abs(hash((shape, out, k, s, "many"))) % 10000
+    x = _pins.from_storage(_pins.draw(shape, code, "ties", base), code)
+    _, idx = _gpu.gpu_forward(x, out, k, s)
+    gy = _pins.from_storage(_pins.draw(tuple(idx.shape), code, "normal", base + 1), code)
+    gx = _gpu.gpu_backward(gy, idx.cpu(), shape, k, s, overlap=2)
+    _gpu.check_backward(orc, gy, idx.cpu(), shape, gx, exact=True, what="ordered, ties")
 
 
 @pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
@@ -360,3 +382,15 @@ def test_workload_full_size(orc, wl):
                             (1, 1, D, H, W), gx[sl], exact=exact,
                             what="%s plane %d" % (wl.name, p))
     _full_backward_property(gyd, idx, gx, wl.shape)
+    # ordered backward: bit-exact on the sampled planes, and the same bits twice
+    gx2 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=2)
+    gx3 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=2, poison=False)
+    torch.cuda.synchronize()
+    iv = torch.int32 if gx2.element_size() == 4 else torch.int16
+    assert torch.equal(gx2.view(iv), gx3.view(iv)), "%s: ordered backward not reproducible" % wl.name
+    for p in planes:
+        n_, c_ = divmod(p, C)
+        sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
+        _gpu.check_backward(orc, gy[sl].contiguous(), idx[sl].cpu().contiguous(),
+                            (1, 1, D, H, W), gx2[sl], exact=True,
+                            what="%s ordered plane %d" % (wl.name, p))
