@@ -75,7 +75,7 @@ def build_ops(torch, mp, workloads):
     """The step's ops (forwards, then backwards) and, apart from the step,
     the variants: the values-only forward of each workload (idx NULL:
     |x|+|y| bytes) and the ordered (bit-reproducible) backward."""
-    fwd_ops, bwd_ops, vo_ops = [], [], []
+    fwd_ops, bwd_ops, vo_ops, ord_ops = [], [], [], []
     for wl in workloads.WORKLOADS:
         x = wl.make_x().cuda()
         N, C, D, H, W = wl.shape
@@ -109,8 +109,9 @@ def build_ops(torch, mp, workloads):
             bwd_ops.append(Op(wl, "bwd", b, bbytes, nin, "backward"))
             o = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
                 gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, overlap=2, out=gx))
-            vo_ops.append(Op(wl, "bwd_ordered", o, bbytes, nin, "ordered backward"))
-    return fwd_ops + bwd_ops, vo_ops
+            ord_ops.append(Op(wl, "bwd_ordered", o, bbytes, nin, "ordered backward"))
+    # the variants run in the step's order: forwards, then backwards
+    return fwd_ops + bwd_ops, vo_ops + ord_ops
 
 
 def cpu_baseline(target_s: float):

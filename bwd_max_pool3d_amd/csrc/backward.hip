@@ -63,7 +63,6 @@ __device__ __forceinline__ void lds_add(float *a, float v)
     }
 }
 
-constexpr int kRound = kBwdRound;          // windows per thread fetched per round
 constexpr int kSlabBlock = kSlabThreads;  // threads per slab workgroup
 
 // Round the accumulator a[0, n) into dst[0, n): 16-byte streaming stores for
@@ -107,7 +106,7 @@ __device__ __forceinline__ void store_span(typename T::raw *dst, const float *a,
 // windows as their flat output numbers do, so each element's fold is the
 // ascending-order sum, and within a phase every input has at most one
 // window, so plain LDS read-modify-writes suffice.
-template <typename T, int NT, bool ORD>
+template <typename T, int NT, bool ORD, int kRound>
 __global__ void __launch_bounds__(NT)
 bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
                 typename T::raw *__restrict__ gx, BwdPlan p)
@@ -159,21 +158,29 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
     if constexpr (ORD) {
         const Axis B = p.g.ax[1], Cw = p.g.ax[2];
         const uint32_t W = (uint32_t)Cw.X, OW = (uint32_t)Cw.O;
+        // first window reaching x, in 32 bits (the plan admits only axes
+        // where that form is exact)
+        auto reach = [](const Axis &ax, uint32_t x) -> uint32_t {
+            if (ax.k) return x < (uint32_t)ax.k ? 0u : ax.dS.div(x - (uint32_t)ax.k) + 1u;
+            return ax.dX.div(x * (uint32_t)ax.O);
+        };
+        const int32_t nslot = (nw + NT - 1) / NT;     // slots that hold a window somewhere
         int32_t cls[kRound];
 #pragma unroll
         for (int k = 0; k < kRound; ++k) {
+            cls[k] = -1;
+            if (k >= nslot) continue;
             const uint32_t e = (uint32_t)(k * NT + tid);
             const uint32_t l = (uint32_t)ri[k] - (uint32_t)ibase;
-            cls[k] = -1;
             if (ri[k] >= 0 && l < (uint32_t)n) {
                 const uint32_t pos = (uint32_t)ri[k];
                 const uint32_t pd = p.hw_div.div(pos), prow = pos - pd * (uint32_t)HW;
                 const uint32_t ph = p.w_div.div(prow), pw = prow - ph * W;
                 const uint32_t q = p.ohw_div.div(e), orow = e - q * (uint32_t)OHW;
                 const uint32_t oh = p.ow_div.div(orow), ow = orow - oh * OW;
-                const uint32_t rd = (uint32_t)od0 + q - (uint32_t)A.first_reaching((int32_t)pd);
-                const uint32_t rh = oh - (uint32_t)B.first_reaching((int32_t)ph);
-                const uint32_t rw = ow - (uint32_t)Cw.first_reaching((int32_t)pw);
+                const uint32_t rd = (uint32_t)od0 + q - reach(A, pd);
+                const uint32_t rh = oh - reach(B, ph);
+                const uint32_t rw = ow - reach(Cw, pw);
                 // an idx outside its window gives a rank out of range: dropped
                 if (rd < (uint32_t)p.md && rh < (uint32_t)p.mh && rw < (uint32_t)p.mw)
                     cls[k] = (int32_t)((rd * p.mh + rh) * p.mw + rw);
@@ -182,7 +189,7 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
         for (int32_t j = 0; j < p.nphase; ++j) {
 #pragma unroll
             for (int k = 0; k < kRound; ++k)
-                if (cls[k] == j) a[ri[k] - ibase] += T::widen(rg[k]);
+                if (k < nslot && cls[k] == j) a[ri[k] - ibase] += T::widen(rg[k]);
             __syncthreads();
         }
     } else {
@@ -283,10 +290,10 @@ hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
         // (the surplus blocks exit at once)
         if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
         if (p.nphase)
-            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, true>), dim3((uint32_t)grid),
-                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
+            hipLaunchKernelGGL((bwd_slab_kernel<T, kOrdThreads, true, kOrdRound>), dim3((uint32_t)grid),
+                               dim3(kOrdThreads), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
         else
-            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, false>), dim3((uint32_t)grid),
+            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, false, kBwdRound>), dim3((uint32_t)grid),
                                dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
     } else {
         hipLaunchKernelGGL(bwd_box_kernel<T>, dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,

@@ -53,6 +53,8 @@ struct BwdPlan {
     FastDiv ohw_div, ow_div;   // by OH*OW and OW (outputs)
 };
 constexpr int kBwdRound = 8;               // slab: windows per thread fetched per round
+constexpr int kOrdThreads = 256;           // threads per ordered slab workgroup
+constexpr int kOrdRound = 8;               // ordered slab: windows per thread (one round)
 constexpr int kMaxPhase = 64;              // ordered slab: at most this many phases
 
 // Ordered gather for any geometry (small.hip): one thread per input

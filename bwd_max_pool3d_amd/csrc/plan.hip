@@ -18,6 +18,7 @@ namespace {
 
 constexpr int64_t kLdsCap = 64 * 1024;     // forward LDS per workgroup, all uses
 constexpr int64_t kAccBudget = 40 * 1024;   // backward accumulator per workgroup
+constexpr int64_t kOrdBudget = 40 * 1024;   // the same, ordered slabs
 constexpr int64_t kWantTiles = 1024;        // >= 4 workgroups per CU
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -271,7 +272,8 @@ static int64_t slab_reach(const Axis &a, int32_t td)
 bool plan_backward(const Geom &g, bool ordered, BwdPlan *p)
 {
     const int32_t D = g.ax[0].X, H = g.ax[1].X, W = g.ax[2].X;
-    const int64_t budget = std::min<int64_t>(kAccBudget, (int64_t)lds_limit() - 64);
+    const int64_t budget = std::min<int64_t>(ordered ? kOrdBudget : kAccBudget,
+                                             (int64_t)lds_limit() - 64);
     const int64_t slice = (int64_t)H * W * 4;
     p->g = g;
     if (slice <= budget) {
@@ -296,13 +298,15 @@ bool plan_backward(const Geom &g, bool ordered, BwdPlan *p)
     p->md = p->mh = p->mw = 0;
     if (ordered) {
         if (!(p->th == H && p->tw == W)) return false;
+        for (int a = 0; a < 3; ++a)                    // the kernel ranks in 32 bits
+            if (!g.ax[a].k && !g.ax[a].fast) return false;
         const Axis &A = g.ax[0];
         const int32_t md = axis_depth(A), mh = axis_depth(g.ax[1]), mw = axis_depth(g.ax[2]);
         if (!md || !mh || !mw || (int64_t)md * mh * mw > kMaxPhase) return false;
         if (D > (1 << 20)) return false;             // bounds the slab scans below
         // every window reaching a slab must fit one round of the workgroup
         const int64_t ohw = (int64_t)g.ax[1].O * g.ax[2].O;
-        const int64_t cap = (int64_t)kBwdRound * kSlabThreads;
+        const int64_t cap = (int64_t)kOrdRound * kOrdThreads;
         int32_t td = p->td;
         while (td > 1 && slab_reach(A, td) * ohw > cap) td = (int32_t)cdiv(D, cdiv(D, td - 1));
         if (slab_reach(A, td) * ohw > cap) return false;
