@@ -1,5 +1,6 @@
-"""CPU oracle for 3-D max pooling: forward window max + int32 argmax, and
-the backward that routes each output gradient to its argmax.
+"""CPU oracle for 3-D max pooling: forward window max + int32 argmax (and,
+for padded / dilated windows, int64 argmax), and the backward that routes
+each output gradient to its argmax.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
 the benchmark's CPU-baseline leg may import this package.  The product path
@@ -64,6 +65,11 @@ class Oracle:
         lib.oracle_fixed_out.restype = _i64
         lib.oracle_forward.argtypes = [_vp, _vp, _vp, ctypes.c_int] + [_i64] * 7 + [_vp, _vp]
         lib.oracle_forward.restype = None
+        lib.oracle_fixed_out_ex.argtypes = [_i64] * 5 + [ctypes.c_int]
+        lib.oracle_fixed_out_ex.restype = _i64
+        lib.oracle_forward_ex.argtypes = ([_vp, _vp, _vp, ctypes.c_int] + [_i64] * 7
+                                          + [_vp] * 4)
+        lib.oracle_forward_ex.restype = None
         lib.oracle_backward.argtypes = [_vp, _vp, _vp, ctypes.c_int] + [_i64] * 7 + [_vp] * 4
         lib.oracle_backward.restype = None
         lib.oracle_widen_array.argtypes = [_vp, ctypes.c_int, _i64, _vp]
@@ -79,6 +85,10 @@ class Oracle:
 
     def fixed_out(self, X: int, k: int, s: int) -> int:
         return self.lib.oracle_fixed_out(X, k, s)
+
+    def fixed_out_ex(self, X: int, k: int, s: int, pad: int = 0, dil: int = 1,
+                     ceil_mode: bool = False) -> int:
+        return self.lib.oracle_fixed_out_ex(X, k, s, pad, dil, int(bool(ceil_mode)))
 
     # -- conversions ---------------------------------------------------
     def widen(self, bits: np.ndarray, dtype: int) -> np.ndarray:
@@ -113,6 +123,21 @@ class Oracle:
         s64 = np.asarray(s, np.int64)
         self.lib.oracle_forward(_ptr(x), _ptr(y), _ptr(idx), dtype, N * C,
                                 D, H, W, OD, OH, OW, _ptr(k64), _ptr(s64))
+        return y, idx
+
+    def forward_ex(self, x: np.ndarray, dtype: int, out: tuple[int, int, int],
+                   k, s, pad=(0, 0, 0), dil=(1, 1, 1)):
+        """Forward with padding and dilation; an axis with k == 0 uses
+        adaptive windows.  Returns (y, idx) with idx int64 (-1 where a
+        window has no tap inside the input)."""
+        self._check(x, dtype)
+        N, C, D, H, W = x.shape
+        OD, OH, OW = out
+        y = np.empty((N, C, OD, OH, OW), x.dtype)
+        idx = np.empty((N, C, OD, OH, OW), np.int64)
+        arrs = [np.asarray(v, np.int64) for v in (k, s, pad, dil)]
+        self.lib.oracle_forward_ex(_ptr(x), _ptr(y), _ptr(idx), dtype, N * C,
+                                   D, H, W, OD, OH, OW, *[_ptr(a) for a in arrs])
         return y, idx
 
     def backward(self, gy: np.ndarray, idx: np.ndarray, dtype: int,

@@ -251,6 +251,126 @@ void oracle_forward(const void *x, void *y, int32_t *idx, int dtype,
 }
 
 /* ---------------------------------------------------------------------- */
+/* Forward with padding and dilation                                       */
+/* ---------------------------------------------------------------------- */
+
+/* The pages define fixed windows without padding only.  Reading taken for
+ * the wider surface: window o takes the k taps o*s - pad + j*dil, j = 0..k-1
+ * (they span (k-1)*dil + 1 positions, the effective kernel of the FlagGems
+ * conv_transpose2d PR page, Implementation); taps outside [0, X) are
+ * padding and are skipped.  Output extent: floor mode counts the spans
+ * that fit X + 2*pad; ceil mode rounds the count up and then drops a last
+ * window that would start at or beyond X + pad.  -1 if no span fits. */
+int64_t oracle_fixed_out_ex(int64_t X, int64_t k, int64_t s, int64_t pad, int64_t dil,
+                            int ceil_mode)
+{
+    if (k <= 0 || s <= 0 || pad < 0 || dil <= 0)
+        return -1;
+    int64_t span = (k - 1) * dil + 1;
+    int64_t room = X + 2 * pad - span;
+    if (room < 0)
+        return -1;
+    int64_t n = room / s;
+    if (ceil_mode && n * s < room)
+        n += 1;                                    /* one more, partial, window */
+    int64_t O = n + 1;
+    if (ceil_mode && (O - 1) * s >= X + pad)
+        O -= 1;
+    return O;
+}
+
+/* Position of tap j of window o on one axis, or -1 if it is padding or past
+ * the window.  k == 0: adaptive windows (contiguous, no padding). */
+static int64_t tap_position(int64_t X, int64_t O, int64_t k, int64_t s, int64_t pad,
+                            int64_t dil, int64_t o, int64_t j)
+{
+    int64_t q;
+    if (k > 0) {
+        if (j >= k)
+            return -1;
+        q = o * s - pad + j * dil;
+    } else {
+        int64_t a, b;
+        oracle_window(X, O, 0, 0, o, &a, &b);
+        if (j >= b - a)
+            return -1;
+        q = a + j;
+    }
+    return (q >= 0 && q < X) ? q : -1;
+}
+
+/* Forward over the taps of each window, in d, h, w scan order of the tap
+ * numbers (the same order as the positions, which grow with j).  idx is
+ * int64; a window with no tap inside the input gives y = -inf, idx = -1.
+ * k/s/pad/dil are arrays of 3; k[a] == 0 selects adaptive windows. */
+void oracle_forward_ex(const void *x, void *y, int64_t *idx, int dtype,
+                       int64_t P, int64_t D, int64_t H, int64_t W,
+                       int64_t OD, int64_t OH, int64_t OW,
+                       const int64_t *k, const int64_t *s,
+                       const int64_t *pad, const int64_t *dil)
+{
+    const int64_t plane_in = D * H * W;
+    const int64_t plane_out = OD * OH * OW;
+    const int es = dtype_size(dtype);
+    /* most taps any window can have on an axis */
+    int64_t nt[3];
+    const int64_t X[3] = {D, H, W};
+    const int64_t O[3] = {OD, OH, OW};
+    for (int a = 0; a < 3; ++a) {
+        if (k[a] > 0) {
+            nt[a] = k[a];
+        } else {
+            nt[a] = 0;
+            for (int64_t o = 0; o < O[a]; ++o) {
+                int64_t lo, hi;
+                oracle_window(X[a], O[a], 0, 0, o, &lo, &hi);
+                if (hi - lo > nt[a])
+                    nt[a] = hi - lo;
+            }
+        }
+    }
+    for (int64_t p = 0; p < P; ++p)
+        for (int64_t od = 0; od < OD; ++od)
+            for (int64_t oh = 0; oh < OH; ++oh)
+                for (int64_t ow = 0; ow < OW; ++ow) {
+                    int64_t best_i = -1;
+                    double best = 0.0;
+                    for (int64_t jd = 0; jd < nt[0]; ++jd) {
+                        int64_t d = tap_position(D, OD, k[0], s[0], pad[0], dil[0], od, jd);
+                        if (d < 0)
+                            continue;
+                        for (int64_t jh = 0; jh < nt[1]; ++jh) {
+                            int64_t h = tap_position(H, OH, k[1], s[1], pad[1], dil[1], oh, jh);
+                            if (h < 0)
+                                continue;
+                            for (int64_t jw = 0; jw < nt[2]; ++jw) {
+                                int64_t w = tap_position(W, OW, k[2], s[2], pad[2], dil[2], ow, jw);
+                                if (w < 0)
+                                    continue;
+                                int64_t i = (d * H + h) * W + w;
+                                double v = load_f64(x, dtype, p * plane_in + i);
+                                int take = best_i < 0 || v > best || (isnan(v) && !isnan(best));
+                                if (take) {
+                                    best = v;
+                                    best_i = i;
+                                }
+                            }
+                        }
+                    }
+                    int64_t o = p * plane_out + (od * OH + oh) * OW + ow;
+                    if (best_i >= 0) {
+                        memcpy((char *)y + o * es,
+                               (const char *)x + (p * plane_in + best_i) * es, es);
+                    } else if (dtype == ORACLE_F32) {
+                        ((float *)y)[o] = -INFINITY;
+                    } else {
+                        ((uint16_t *)y)[o] = dtype == ORACLE_F16 ? 0xfc00 : 0xff80;
+                    }
+                    idx[o] = best_i;
+                }
+}
+
+/* ---------------------------------------------------------------------- */
 /* Backward                                                                */
 /* ---------------------------------------------------------------------- */
 

@@ -20,6 +20,9 @@ Sources of truth used here, none of which is the oracle's own code:
   * torch's CPU max_pool3d / adaptive_max_pool3d and their autograd
     backward, on tie-free data;
   * closed forms (ramps, constants, identity and global windows);
+  * for padding, dilation and ceil mode (no page defines them for pooling):
+    torch's CPU max_pool3d and its output shapes, and identities with the
+    plain forward (subsampling for dilation, a -inf border for padding);
   * numpy's unbuffered ``add.at`` accumulation and ``bincount`` for the
     backward, and the exact ``math.fsum`` invariant for disjoint windows.
 """
@@ -434,6 +437,116 @@ def pin_backward_torch(orc):
         assert np.allclose(r["ref64"], xt.grad.numpy(), rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# padding, dilation and ceil mode (forward_ex)
+# ---------------------------------------------------------------------------
+
+# (shape, kernel, stride, pad, dilation, ceil_mode); every case is one torch
+# accepts (pad <= kernel / 2, at least one window per axis)
+EX_CASES = [
+    ((1, 2, 7, 8, 9), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),
+    ((1, 1, 7, 8, 9), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), True),
+    ((2, 1, 6, 7, 5), (2, 2, 2), (2, 2, 2), (1, 0, 1), (1, 1, 1), True),
+    ((1, 1, 9, 9, 9), (3, 2, 3), (1, 2, 3), (1, 1, 0), (2, 3, 1), False),
+    ((1, 1, 9, 10, 11), (3, 3, 2), (2, 3, 2), (1, 1, 1), (2, 2, 3), True),
+    ((1, 1, 5, 6, 7), (1, 1, 1), (2, 2, 2), (0, 0, 0), (1, 1, 1), True),
+    ((1, 1, 4, 5, 6), (4, 5, 2), (3, 2, 1), (2, 2, 1), (1, 1, 2), True),
+    ((1, 1, 2, 3, 4), (2, 2, 2), (1, 1, 1), (1, 1, 1), (3, 2, 2), False),   # all-padding windows
+]
+
+
+def ex_out(orc, shape, k, s, pad, dil, ceil_mode):
+    return tuple(orc.fixed_out_ex(X, *a, ceil_mode=ceil_mode)
+                 for X, a in zip(shape[2:], zip(k, s, pad, dil)))
+
+
+def pin_out_size_ex(orc):
+    """Output extents with padding, dilation and ceil mode equal torch's
+    pooling output shape over a grid of small axes (and -1 exactly where no
+    window fits)."""
+    for X in range(1, 11):
+        for k in range(1, 5):
+            for s in range(1, 4):
+                for pad in range(0, k // 2 + 1):
+                    for dil in range(1, 4):
+                        for cm in (False, True):
+                            got = orc.fixed_out_ex(X, k, s, pad, dil, cm)
+                            if X + 2 * pad < (k - 1) * dil + 1:
+                                assert got == -1, (X, k, s, pad, dil, cm)
+                                continue
+                            t = F.max_pool1d(torch.zeros(1, 1, X), k, s, pad, dil, ceil_mode=cm)
+                            assert got == t.shape[-1], (X, k, s, pad, dil, cm, got, t.shape)
+
+
+def pin_forward_ex_torch(orc):
+    """Values and indices with padding, dilation and ceil mode equal torch's
+    CPU max_pool3d on tie-free data (values on tie-heavy data); a window
+    whose taps are all padding gives -inf and index -1 (torch's index there
+    is not a position, so only its -inf is compared)."""
+    seed = 1301
+    for shape, k, s, pad, dil, cm in EX_CASES:
+        o3 = ex_out(orc, shape, k, s, pad, dil, cm)
+        for dt in (F32, F16, BF16):
+            for kind in ("distinct", "ties"):
+                seed += 1
+                n = int(np.prod(shape))
+                if kind == "distinct" and n > {F32: 1 << 24, F16: 4096, BF16: 512}[dt]:
+                    continue
+                x = draw(shape, dt, kind, seed)
+                y, idx = orc.forward_ex(x, dt, o3, k, s, pad, dil)
+                xt = torch.from_numpy(widen_torch(x, dt))
+                ty, ti = F.max_pool3d(xt, k, s, pad, dil, ceil_mode=cm, return_indices=True)
+                assert tuple(ty.shape[2:]) == o3, (shape, k, s, pad, dil, cm)
+                assert np.array_equal(widen_torch(y, dt), ty.numpy()), (shape, dt, kind)
+                empty = idx < 0
+                assert np.all(np.isneginf(widen_torch(y, dt)[empty]))
+                if kind == "distinct":
+                    assert np.array_equal(idx[~empty], ti.numpy()[~empty]), (shape, dt, kind)
+
+
+def pin_forward_ex_identities(orc):
+    """Identities that tie the padded / dilated forward to the plain one
+    (itself pinned above): no padding and dilation 1 is the plain forward;
+    stride = m * dilation with no padding is the plain forward with stride m
+    over every dil-th element; padding is an explicit -inf border."""
+    x = draw((2, 1, 9, 10, 11), F32, "ties", 1401)
+    for k, s in [((3, 2, 2), (2, 1, 2)), ((1, 3, 2), (1, 2, 2))]:
+        o3 = _out_of(orc, x.shape, None, k, s)
+        y0, i0 = orc.forward(x, F32, o3, k, s)
+        y1, i1 = orc.forward_ex(x, F32, o3, k, s)
+        assert np.array_equal(y0, y1) and np.array_equal(i0.astype(np.int64), i1)
+    # dilation 2 and 3, stride a multiple of it, offset 0
+    D, H, W = x.shape[2:]
+    for dil, k, m in [((2, 3, 2), (2, 2, 3), (1, 1, 2)), ((3, 2, 1), (3, 2, 2), (1, 2, 1))]:
+        s = tuple(a * b for a, b in zip(dil, m))
+        o3 = ex_out(orc, x.shape, k, s, (0, 0, 0), dil, False)
+        y, idx = orc.forward_ex(x, F32, o3, k, s, (0, 0, 0), dil)
+        sub = np.ascontiguousarray(x[:, :, ::dil[0], ::dil[1], ::dil[2]])
+        so3 = _out_of(orc, sub.shape, None, k, m)
+        sy, sidx = orc.forward(sub, F32, so3, k, m)
+        assert o3 == tuple(min(a, b) for a, b in zip(o3, so3))
+        sd, sh, sw = sub.shape[2:]
+        sd_, rem = np.divmod(sidx, sh * sw)
+        sh_, sw_ = np.divmod(rem, sw)
+        full = ((sd_ * dil[0]) * H + sh_ * dil[1]) * W + sw_ * dil[2]
+        sl = (slice(None), slice(None)) + tuple(slice(0, n) for n in o3)
+        assert np.array_equal(y, sy[sl]) and np.array_equal(idx, full[sl].astype(np.int64))
+    # padding: an explicit -inf border, then no padding
+    for k, s, pad, dil, cm in [((3, 3, 2), (2, 1, 2), (1, 1, 1), (1, 2, 1), False),
+                               ((2, 3, 3), (2, 2, 3), (1, 1, 1), (1, 1, 1), True)]:
+        o3 = ex_out(orc, x.shape, k, s, pad, dil, cm)
+        y, idx = orc.forward_ex(x, F32, o3, k, s, pad, dil)
+        big = np.pad(x, [(0, 0), (0, 0)] + [(p, p + 2 * max(s)) for p in pad],
+                     constant_values=-np.inf).astype(np.float32)
+        by, bidx = orc.forward_ex(np.ascontiguousarray(big), F32, o3, k, s, (0, 0, 0), dil)
+        BH, BW = big.shape[3:]
+        bd, rem = np.divmod(bidx, BH * BW)
+        bh, bw = np.divmod(rem, BW)
+        back = ((bd - pad[0]) * H + (bh - pad[1])) * W + (bw - pad[2])
+        assert np.array_equal(y, by) and np.array_equal(idx, back)
+
+
 ALL_PINS = [pin_widen, pin_round, pin_windows_adaptive, pin_windows_fixed,
             pin_forward_brute, pin_forward_torch, pin_forward_closed_forms,
-            pin_backward, pin_backward_torch]
+            pin_backward, pin_backward_torch, pin_out_size_ex, pin_forward_ex_torch,
+            pin_forward_ex_identities]

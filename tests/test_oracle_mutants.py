@@ -23,7 +23,11 @@ MUTANTS = {
     "fixed_out_ceil_mode": (
         "return (X - k) / s + 1;", "return (X - k + s - 1) / s + 1;"),
     "index_h_w_transposed": (
-        "best_i = i;", "best_i = (d * W + w) * H + h;"),
+        "idx[o] = (int32_t)best_i;",
+        "idx[o] = (int32_t)(((best_i / (H * W)) * W + best_i % W) * H + (best_i / W) % H);"),
+    "ex_index_h_w_transposed": (
+        "idx[o] = best_i;",
+        "idx[o] = best_i < 0 ? -1 : ((best_i / (H * W)) * W + best_i % W) * H + (best_i / W) % H;"),
     "scan_w_before_h": (
         "for (int64_t h = h0; h < h1; ++h)\n"
         "                            for (int64_t w = w0; w < w1; ++w) {",
@@ -52,6 +56,20 @@ MUTANTS = {
         "ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
     "bf16_widen_subnormal_scale": (
         "ldexp((double)m, -133)", "ldexp((double)m, -132)"),
+    "ex_tap_ignores_dilation": (
+        "q = o * s - pad + j * dil;", "q = o * s - pad + j;"),
+    "ex_padding_added": (
+        "q = o * s - pad + j * dil;", "q = o * s + pad + j * dil;"),
+    "ex_right_padding_read": (
+        "return (q >= 0 && q < X) ? q : -1;", "return (q >= 0 && q < X + 1) ? q : -1;"),
+    "ex_span_ignores_dilation": (
+        "int64_t span = (k - 1) * dil + 1;", "int64_t span = k;"),
+    "ex_floor_mode_rounds_up": (
+        "if (ceil_mode && n * s < room)", "if (n * s < room)"),
+    "ex_ceil_keeps_window_in_padding": (
+        "if (ceil_mode && (O - 1) * s >= X + pad)", "if (0)"),
+    "ex_empty_window_zero": (
+        "((float *)y)[o] = -INFINITY;", "((float *)y)[o] = 0.0f;"),
 }
 
 
