@@ -11,9 +11,14 @@ PyTorch fallback: if the library is missing every call raises ImportError.
   mp3d_backward(gy, idx, in_shape, kernel=None, stride=None, overlap=-1) -> gx
       (overlap=2: ordered, bit-reproducible sums)
   mp3d_out_size(X, k, s) -> int
+  mp3d_forward_ex(x, kernel, stride, padding, dilation, ceil_mode, index_dtype)
+      -> (y, idx)                                    padding / dilation / ceil mode,
+                                                     int32 or int64 idx
+  mp3d_backward_ex(gy, idx, in_shape, kernel, stride, padding, dilation) -> gx
+  mp3d_out_size_ex(X, k, s, pad, dilation, ceil_mode) -> int
 
-x, y, gy and gx are float32, float16 or bfloat16; idx is int32, flat within
-each D*H*W plane.
+x, y, gy and gx are float32, float16 or bfloat16; idx is int32 (int64 on
+request: index_dtype=torch.int64), flat within each D*H*W plane.
 """
 from __future__ import annotations
 
@@ -24,7 +29,10 @@ import torch
 from . import _lib
 from ._lib import Mp3dError  # noqa: F401
 
-__all__ = ["mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size", "Mp3dError"]
+__all__ = ["mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
+           "mp3d_forward_ex", "mp3d_backward_ex", "mp3d_out_size_ex", "Mp3dError"]
+
+_IDX = {torch.int32: _lib.MP3D_IDX_I32, torch.int64: _lib.MP3D_IDX_I64}
 
 _DTYPE = {torch.float32: _lib.MP3D_F32, torch.float16: _lib.MP3D_F16,
           torch.bfloat16: _lib.MP3D_BF16}
@@ -66,7 +74,7 @@ def mp3d_out_size(X: int, k: int, s: int) -> int:
     return out.value
 
 
-def _outputs(x: torch.Tensor, shape, out, indices: bool):
+def _outputs(x: torch.Tensor, shape, out, indices: bool, idx_dtype=torch.int32):
     if not indices:
         if out is None:
             return torch.empty(shape, dtype=x.dtype, device=x.device), None
@@ -76,20 +84,26 @@ def _outputs(x: torch.Tensor, shape, out, indices: bool):
         return out, None
     if out is None:
         return (torch.empty(shape, dtype=x.dtype, device=x.device),
-                torch.empty(shape, dtype=torch.int32, device=x.device))
+                torch.empty(shape, dtype=idx_dtype, device=x.device))
     y, idx = out
     _check_tensor(y, "y")
     _check_tensor(idx, "idx")
     if (tuple(y.shape) != shape or tuple(idx.shape) != shape or y.dtype != x.dtype
-            or idx.dtype != torch.int32):
-        raise ValueError("out must be (y, idx) of shape %s, dtypes (%s, int32)" % (shape, x.dtype))
+            or idx.dtype != idx_dtype):
+        raise ValueError("out must be (y, idx) of shape %s, dtypes (%s, %s)" % (
+            shape, x.dtype, idx_dtype))
     return y, idx
 
 
-def mp3d_forward(x: torch.Tensor, kernel, stride=None, out=None, indices: bool = True):
+def mp3d_forward(x: torch.Tensor, kernel, stride=None, out=None, indices: bool = True,
+                 index_dtype=torch.int32):
     """Fixed-window forward: returns (y, idx), or y alone when ``indices``
     is False (no index is computed into memory).  ``out`` may supply a
-    preallocated (y, idx) pair, or y."""
+    preallocated (y, idx) pair, or y.  ``index_dtype`` torch.int64 gives
+    torch-style int64 indices (through mp3d_forward_ex)."""
+    if index_dtype != torch.int32:
+        return mp3d_forward_ex(x, kernel, stride, out=out, indices=indices,
+                               index_dtype=index_dtype)
     lib = _lib.load()
     _check_tensor(x, "x")
     k = _triple(kernel)
@@ -102,14 +116,25 @@ def mp3d_forward(x: torch.Tensor, kernel, stride=None, out=None, indices: bool =
     return (y, idx) if indices else y
 
 
-def amp3d_forward(x: torch.Tensor, out_size, out=None, indices: bool = True):
+def amp3d_forward(x: torch.Tensor, out_size, out=None, indices: bool = True,
+                  index_dtype=torch.int32):
     """Adaptive-window forward: returns (y, idx), or y alone when
     ``indices`` is False.  ``out`` may supply a preallocated (y, idx) pair,
-    or y."""
+    or y.  ``index_dtype`` torch.int64 gives int64 indices."""
     lib = _lib.load()
     _check_tensor(x, "x")
     o = _triple(out_size)
     N, C, D, H, W = x.shape
+    if index_dtype != torch.int32:
+        if index_dtype not in _IDX:
+            raise TypeError("index_dtype must be torch.int32 or torch.int64")
+        y, idx = _outputs(x, (N, C) + o, out, indices, index_dtype)
+        zero = _arr3((0, 0, 0))
+        _lib.check(lib.mp3d_forward_ex(x.data_ptr(), y.data_ptr(),
+                                       idx.data_ptr() if indices else None, _code(x),
+                                       _IDX[index_dtype], N, C, D, H, W, *o, zero, zero, zero,
+                                       _arr3((1, 1, 1)), _stream(x)))
+        return (y, idx) if indices else y
     y, idx = _outputs(x, (N, C) + o, out, indices)
     _lib.check(lib.amp3d_forward(x.data_ptr(), y.data_ptr(), idx.data_ptr() if indices else None,
                                  _code(x), N, C, D, H, W, *o, _stream(x)))
@@ -127,8 +152,8 @@ def mp3d_backward(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel=None,
     lib = _lib.load()
     _check_tensor(gy, "gy")
     _check_tensor(idx, "idx")
-    if idx.dtype != torch.int32:
-        raise TypeError("idx must be int32")
+    if idx.dtype not in _IDX:
+        raise TypeError("idx must be int32 or int64")
     if idx.shape != gy.shape or idx.device != gy.device:
         raise ValueError("idx and gy must have the same shape and device")
     N, C, D, H, W = (int(v) for v in in_shape)
@@ -139,6 +164,8 @@ def mp3d_backward(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel=None,
     else:
         k = _triple(kernel)
         s = _triple(stride if stride is not None else kernel)
+    if idx.dtype == torch.int64:
+        return mp3d_backward_ex(gy, idx, in_shape, k, s, 0, 1, overlap=overlap, out=out)
     if out is None:
         out = torch.empty((N, C, D, H, W), dtype=gy.dtype, device=gy.device)
     else:
@@ -148,4 +175,72 @@ def mp3d_backward(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel=None,
     od, oh, ow = gy.shape[2:]
     _lib.check(lib.mp3d_backward(gy.data_ptr(), idx.data_ptr(), out.data_ptr(), _code(gy),
                                  N, C, D, H, W, od, oh, ow, *k, *s, int(overlap), _stream(gy)))
+    return out
+
+
+def mp3d_out_size_ex(X: int, k: int, s: int, pad: int = 0, dilation: int = 1,
+                     ceil_mode: bool = False) -> int:
+    """Output extent of a fixed axis with padding, dilation and ceil mode,
+    as the library computes it."""
+    out = ctypes.c_int64()
+    _lib.check(_lib.load().mp3d_out_size_ex(X, k, s, pad, dilation, int(bool(ceil_mode)),
+                                            ctypes.byref(out)))
+    return out.value
+
+
+def _arr3(v):
+    return (ctypes.c_int32 * 3)(*v)
+
+
+def mp3d_forward_ex(x: torch.Tensor, kernel, stride=None, padding=0, dilation=1,
+                    ceil_mode: bool = False, index_dtype=torch.int32, out=None,
+                    indices: bool = True):
+    """Fixed-window forward with padding, dilation and ceil mode, and int32
+    or int64 indices: returns (y, idx), or y alone when ``indices`` is
+    False.  ``out`` may supply a preallocated (y, idx) pair, or y."""
+    lib = _lib.load()
+    _check_tensor(x, "x")
+    if index_dtype not in _IDX:
+        raise TypeError("index_dtype must be torch.int32 or torch.int64")
+    k = _triple(kernel)
+    s = _triple(stride if stride is not None else kernel)
+    pd, dl = _triple(padding), _triple(dilation)
+    N, C, D, H, W = x.shape
+    o = tuple(mp3d_out_size_ex(X, *a, ceil_mode=ceil_mode)
+              for X, a in zip((D, H, W), zip(k, s, pd, dl)))
+    y, idx = _outputs(x, (N, C) + o, out, indices, index_dtype)
+    _lib.check(lib.mp3d_forward_ex(x.data_ptr(), y.data_ptr(), idx.data_ptr() if indices else None,
+                                   _code(x), _IDX[index_dtype], N, C, D, H, W, *o, _arr3(k),
+                                   _arr3(s), _arr3(pd), _arr3(dl), _stream(x)))
+    return (y, idx) if indices else y
+
+
+def mp3d_backward_ex(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel, stride=None,
+                     padding=0, dilation=1, overlap: int = -1, out: torch.Tensor | None = None):
+    """Backward for mp3d_forward_ex: gx of shape ``in_shape`` from gy and
+    idx (int32 or int64).  The ceil mode is read from gy's extents.
+    ``overlap`` as for mp3d_backward."""
+    lib = _lib.load()
+    _check_tensor(gy, "gy")
+    _check_tensor(idx, "idx")
+    if idx.dtype not in _IDX:
+        raise TypeError("idx must be int32 or int64")
+    if idx.shape != gy.shape or idx.device != gy.device:
+        raise ValueError("idx and gy must have the same shape and device")
+    N, C, D, H, W = (int(v) for v in in_shape)
+    if gy.shape[:2] != (N, C):
+        raise ValueError("gy's N, C do not match in_shape")
+    k = _triple(kernel)
+    s = _triple(stride if stride is not None else kernel)
+    pd, dl = _triple(padding), _triple(dilation)
+    if out is None:
+        out = torch.empty((N, C, D, H, W), dtype=gy.dtype, device=gy.device)
+    else:
+        _check_tensor(out, "out")
+        if out.shape != (N, C, D, H, W) or out.dtype != gy.dtype:
+            raise ValueError("out must be a %s tensor of shape %s" % (gy.dtype, (N, C, D, H, W)))
+    od, oh, ow = gy.shape[2:]
+    _lib.check(lib.mp3d_backward_ex(gy.data_ptr(), idx.data_ptr(), out.data_ptr(), _code(gy),
+                                    _IDX[idx.dtype], N, C, D, H, W, od, oh, ow, _arr3(k),
+                                    _arr3(s), _arr3(pd), _arr3(dl), int(overlap), _stream(gy)))
     return out

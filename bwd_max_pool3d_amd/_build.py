@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libmp3d.so")
 SOURCES = ["api.hip", "plan.hip", "forward.hip", "forward_fixed.hip", "forward_col.hip",
-           "backward.hip", "small.hip"]
+           "backward.hip", "small.hip", "forward_ex.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

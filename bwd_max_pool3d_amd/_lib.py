@@ -14,7 +14,10 @@ LIBRARY = os.path.join(HERE, "libmp3d.so")
 MP3D_OK, MP3D_EINVAL, MP3D_EDTYPE, MP3D_ENOTDIV, MP3D_EOVERFLOW, MP3D_EHIP = range(6)
 MP3D_F32, MP3D_F16, MP3D_BF16 = 0, 1, 2
 
+MP3D_IDX_I32, MP3D_IDX_I64 = 0, 1
+
 EXPORTS = ("mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
+           "mp3d_out_size_ex", "mp3d_forward_ex", "mp3d_backward_ex",
            "mp3d_strerror", "mp3d_last_error")
 
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -48,11 +51,19 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mp3d_backward.argtypes = ([_vp, _vp, _vp, ctypes.c_int] + [_i64] * 5 + [_i32] * 9
                                   + [ctypes.c_int, _vp])
     lib.mp3d_out_size.argtypes = [_i64, _i32, _i32, ctypes.POINTER(_i64)]
+    _a3 = ctypes.POINTER(_i32)
+    lib.mp3d_out_size_ex.argtypes = [_i64, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                     ctypes.POINTER(_i64)]
+    lib.mp3d_forward_ex.argtypes = ([_vp, _vp, _vp, ctypes.c_int, ctypes.c_int] + [_i64] * 5
+                                    + [_i32] * 3 + [_a3] * 4 + [_vp])
+    lib.mp3d_backward_ex.argtypes = ([_vp, _vp, _vp, ctypes.c_int, ctypes.c_int] + [_i64] * 5
+                                     + [_i32] * 3 + [_a3] * 4 + [ctypes.c_int, _vp])
     lib.mp3d_strerror.argtypes = [ctypes.c_int]
     lib.mp3d_strerror.restype = ctypes.c_char_p
     lib.mp3d_last_error.argtypes = []
     lib.mp3d_last_error.restype = ctypes.c_char_p
-    for name in ("mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size"):
+    for name in ("mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
+                 "mp3d_out_size_ex", "mp3d_forward_ex", "mp3d_backward_ex"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

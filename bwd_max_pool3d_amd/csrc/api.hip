@@ -82,6 +82,55 @@ int set_fixed_axis(Axis *a, int64_t X, int32_t k, int32_t s, const char *name)
     return MP3D_OK;
 }
 
+// Output extent of a fixed axis with padding and dilation: floor mode
+// counts the windows whose span fits the padded axis; ceil mode also keeps
+// a last partial window if it starts inside the input or the left padding.
+// -1 if not even one window fits.
+int64_t fixed_out_ex(int64_t X, int64_t k, int64_t s, int64_t pad, int64_t dil, bool ceil_mode)
+{
+    const int64_t ext = (k - 1) * dil + 1, room = X + 2 * pad - ext;
+    if (room < 0) return -1;
+    int64_t O = (ceil_mode ? (room + s - 1) / s : room / s) + 1;
+    if (ceil_mode && (O - 1) * s >= X + pad) --O;
+    return O;
+}
+
+// Validation shared by the padded / dilated entry points.
+int check_fixed_ex(int64_t X, int64_t k, int64_t s, int64_t pad, int64_t dil, const char *name)
+{
+    if (k <= 0 || s <= 0)
+        return fail(MP3D_EINVAL, "kernel and stride on %s must be >= 1 (got %lld, %lld)", name,
+                    (long long)k, (long long)s);
+    if (pad < 0 || dil <= 0)
+        return fail(MP3D_EINVAL, "padding on %s must be >= 0 and dilation >= 1 (got %lld, %lld)",
+                    name, (long long)pad, (long long)dil);
+    if ((k - 1) * dil + 1 > kInt32Max || X + 2 * pad > kInt32Max)
+        return fail(MP3D_EOVERFLOW, "window span or padded extent on %s exceeds int32", name);
+    const int64_t ext = (k - 1) * dil + 1;
+    if (2 * pad > k)
+        return fail(MP3D_EINVAL, "padding %lld on %s exceeds half the kernel %lld",
+                    (long long)pad, name, (long long)k);
+    if (X + 2 * pad < ext)
+        return fail(MP3D_EINVAL, "window span %lld exceeds the padded extent %lld on %s",
+                    (long long)ext, (long long)(X + 2 * pad), name);
+    return MP3D_OK;
+}
+
+// A fixed axis with padding and dilation whose output extent O is given:
+// it must be the floor-mode or the ceil-mode extent.
+int set_fixed_axis_ex(Axis *a, int64_t X, int32_t k, int32_t s, int32_t pad, int32_t dil,
+                      int64_t O, const char *name)
+{
+    int rc = check_fixed_ex(X, k, s, pad, dil, name);
+    if (rc) return rc;
+    const int64_t lo = fixed_out_ex(X, k, s, pad, dil, false), hi = fixed_out_ex(X, k, s, pad, dil, true);
+    if (O != lo && O != hi)
+        return fail(MP3D_EINVAL, "output extent %lld on %s is neither %lld (floor) nor %lld (ceil)",
+                    (long long)O, name, (long long)lo, (long long)hi);
+    *a = Axis::make((int32_t)X, (int32_t)O, k, s, pad, dil);
+    return MP3D_OK;
+}
+
 int set_adaptive_axis(Axis *a, int64_t X, int32_t O, const char *name)
 {
     if (O <= 0)
@@ -142,32 +191,52 @@ int run_forward(const void *x, void *y, int32_t *idx, const Geom &g, hipStream_t
     return hip_status(launch_forward_direct<T>(x, y, idx, g, s), "forward direct launch");
 }
 
-int forward(const void *x, void *y, int32_t *idx, int dtype, const Geom &g, hipStream_t s)
+template <typename T, typename IT>
+int run_forward_ex(const void *x, void *y, IT *idx, const Geom &g, hipStream_t s)
+{
+    ExPlan p;
+    plan_ex(g, &p);
+    if (log_enabled())
+        fprintf(stderr, "[mp3d] forward general dtype=%d idx=%d taps<=3:%d outputs=%lld\n", T::code,
+                (int)sizeof(IT) * 8, p.km == 3, (long long)p.total);
+    return hip_status(launch_forward_ex<T, IT>(x, y, idx, p, s), "forward general launch");
+}
+
+template <typename T>
+int forward_t(const void *x, void *y, void *idx, int idx_type, const Geom &g, hipStream_t s)
+{
+    if (idx_type == MP3D_IDX_I64) return run_forward_ex<T, int64_t>(x, y, (int64_t *)idx, g, s);
+    if (!g.plain()) return run_forward_ex<T, int32_t>(x, y, (int32_t *)idx, g, s);
+    return run_forward<T>(x, y, (int32_t *)idx, g, s);
+}
+
+int forward(const void *x, void *y, void *idx, int idx_type, int dtype, const Geom &g,
+            hipStream_t s)
 {
     if (g.planes == 0) return MP3D_OK;
     if (!x || !y) return fail(MP3D_EINVAL, "null tensor pointer");   // idx NULL: values only
     switch (dtype) {
-    case MP3D_F32: return run_forward<F32>(x, y, idx, g, s);
-    case MP3D_F16: return run_forward<F16>(x, y, idx, g, s);
-    default: return run_forward<BF16>(x, y, idx, g, s);
+    case MP3D_F32: return forward_t<F32>(x, y, idx, idx_type, g, s);
+    case MP3D_F16: return forward_t<F16>(x, y, idx, idx_type, g, s);
+    default: return forward_t<BF16>(x, y, idx, idx_type, g, s);
     }
 }
 
 enum class BwdPath { gather, accumulate, ordered };
 
-template <typename T>
-int run_backward(const void *gy, const int32_t *idx, void *gx, const Geom &g, BwdPath path,
+template <typename T, typename IT>
+int run_backward(const void *gy, const IT *idx, void *gx, const Geom &g, BwdPath path,
                  hipStream_t s)
 {
     if (path == BwdPath::gather) {
         GatherPlan p{g, g.ax[0].X / g.ax[0].O, g.ax[1].X / g.ax[1].O, g.ax[2].X / g.ax[2].O};
         if (log_enabled()) fprintf(stderr, "[mp3d] backward gather dtype=%d\n", T::code);
-        return hip_status(launch_backward_gather<T>(gy, idx, gx, p, s), "backward gather launch");
+        return hip_status(launch_backward_gather<T, IT>(gy, idx, gx, p, s), "backward gather launch");
     }
     SmallPlan sp;
     if (small_enabled() && plan_small_backward(g, &sp)) {
         if (log_enabled()) fprintf(stderr, "[mp3d] backward small dtype=%d inputs=%u\n", T::code, sp.total);
-        return hip_status(launch_backward_small<T>(gy, idx, gx, sp, s), "backward small launch");
+        return hip_status(launch_backward_small<T, IT>(gy, idx, gx, sp, s), "backward small launch");
     }
     const bool ordered = path == BwdPath::ordered;
     BwdPlan p;
@@ -176,12 +245,12 @@ int run_backward(const void *gy, const int32_t *idx, void *gx, const Geom &g, Bw
             fprintf(stderr, "[mp3d] backward %s dtype=%d box=(%d,%d,%d) tiles=%lld lds=%u phases=%d\n",
                     ordered ? "ordered slab" : "accumulate", T::code, p.td, p.th, p.tw,
                     (long long)p.ntiles, p.lds_bytes, p.nphase);
-        return hip_status(launch_backward_tile<T>(gy, idx, gx, p, s), "backward tile launch");
+        return hip_status(launch_backward_tile<T, IT>(gy, idx, gx, p, s), "backward tile launch");
     }
     OrdPlan op;
     plan_ordered(g, &op);
     if (log_enabled()) fprintf(stderr, "[mp3d] backward ordered gather dtype=%d\n", T::code);
-    return hip_status(launch_backward_ordered<T>(gy, idx, gx, op, s), "backward ordered launch");
+    return hip_status(launch_backward_ordered<T, IT>(gy, idx, gx, op, s), "backward ordered launch");
 }
 
 // Windows tile an axis -- each position in exactly one window, the one
@@ -189,9 +258,67 @@ int run_backward(const void *gy, const int32_t *idx, void *gx, const Geom &g, Bw
 // fixed windows when stride == X/O and kernel <= stride.
 bool axis_tiles(const Axis &a)
 {
-    if (a.X % a.O != 0) return false;
+    if (a.X % a.O != 0 || !a.plain()) return false;
     if (a.k == 0) return true;
     return a.s == a.X / a.O && a.k <= a.s;
+}
+
+// Axes of the padded / dilated entry points: kernel[a] == stride[a] == 0
+// selects adaptive windows with extent O (padding 0 and dilation 1 there);
+// otherwise fixed windows.  pad and dilation may be NULL (0 and 1).
+int set_axes_ex(Geom *g, int64_t D, int64_t H, int64_t W, int32_t od, int32_t oh, int32_t ow,
+                const int32_t *kernel, const int32_t *stride, const int32_t *pad,
+                const int32_t *dilation)
+{
+    if (!kernel || !stride) return fail(MP3D_EINVAL, "kernel and stride arrays must not be NULL");
+    const int64_t X[3] = {D, H, W};
+    const int32_t O[3] = {od, oh, ow};
+    const char *names[3] = {"D", "H", "W"};
+    for (int a = 0; a < 3; ++a) {
+        const int32_t pa = pad ? pad[a] : 0, dl = dilation ? dilation[a] : 1;
+        int rc;
+        if (kernel[a] == 0 && stride[a] == 0) {
+            if (pa != 0 || dl != 1)
+                return fail(MP3D_EINVAL, "adaptive axis %s takes padding 0 and dilation 1", names[a]);
+            if ((rc = set_adaptive_axis(&g->ax[a], X[a], O[a], names[a]))) return rc;
+        } else if ((rc = set_fixed_axis_ex(&g->ax[a], X[a], kernel[a], stride[a], pa, dl, O[a],
+                                           names[a]))) {
+            return rc;
+        }
+    }
+    return MP3D_OK;
+}
+
+int backward(const void *gy, const void *idx, int idx_type, void *gx, int dtype, Geom &g,
+             int64_t N, int64_t C, int overlap, hipStream_t s)
+{
+    int rc;
+    if (overlap < -1 || overlap > 2)
+        return fail(MP3D_EINVAL, "overlap must be -1, 0, 1 or 2 (got %d)", overlap);
+    if ((rc = finish_geom(&g, N, C))) return rc;
+    const bool tiles = axis_tiles(g.ax[0]) && axis_tiles(g.ax[1]) && axis_tiles(g.ax[2]);
+    if (overlap == 0 && !tiles)
+        return fail(MP3D_ENOTDIV, "overlap=0 needs windows that tile every axis");
+    if (g.planes == 0) return MP3D_OK;
+    if (!gy || !idx || !gx) return fail(MP3D_EINVAL, "null tensor pointer");
+    // the gather is already the ordered sum (one window per input)
+    const BwdPath path = overlap == 0 || ((overlap == -1 || overlap == 2) && tiles)
+                             ? BwdPath::gather
+                             : overlap == 2 ? BwdPath::ordered : BwdPath::accumulate;
+    if (idx_type == MP3D_IDX_I64) {
+        const int64_t *ix = (const int64_t *)idx;
+        switch (dtype) {
+        case MP3D_F32: return run_backward<F32>(gy, ix, gx, g, path, s);
+        case MP3D_F16: return run_backward<F16>(gy, ix, gx, g, path, s);
+        default: return run_backward<BF16>(gy, ix, gx, g, path, s);
+        }
+    }
+    const int32_t *ix = (const int32_t *)idx;
+    switch (dtype) {
+    case MP3D_F32: return run_backward<F32>(gy, ix, gx, g, path, s);
+    case MP3D_F16: return run_backward<F16>(gy, ix, gx, g, path, s);
+    default: return run_backward<BF16>(gy, ix, gx, g, path, s);
+    }
 }
 
 }  // namespace
@@ -245,6 +372,18 @@ int mp3d_out_size(int64_t X, int32_t k, int32_t s, int64_t *out)
     return MP3D_OK;
 }
 
+int mp3d_out_size_ex(int64_t X, int32_t k, int32_t s, int32_t pad, int32_t dilation, int ceil_mode,
+                     int64_t *out)
+{
+    if (!out) return fail(MP3D_EINVAL, "out is NULL");
+    if (ceil_mode != 0 && ceil_mode != 1) return fail(MP3D_EINVAL, "ceil_mode must be 0 or 1");
+    if (X <= 0 || X > kInt32Max) return fail(MP3D_EINVAL, "extent %lld out of range", (long long)X);
+    int rc = check_fixed_ex(X, k, s, pad, dilation, "the axis");
+    if (rc) return rc;
+    *out = fixed_out_ex(X, k, s, pad, dilation, ceil_mode == 1);
+    return MP3D_OK;
+}
+
 int mp3d_forward(const void *x, void *y, int32_t *idx, int dtype, int64_t N, int64_t C,
                  int64_t D, int64_t H, int64_t W, int32_t kd, int32_t kh, int32_t kw,
                  int32_t sd, int32_t sh, int32_t sw, void *stream)
@@ -256,7 +395,7 @@ int mp3d_forward(const void *x, void *y, int32_t *idx, int dtype, int64_t N, int
     if ((rc = set_fixed_axis(&g.ax[1], H, kh, sh, "H"))) return rc;
     if ((rc = set_fixed_axis(&g.ax[2], W, kw, sw, "W"))) return rc;
     if ((rc = finish_geom(&g, N, C))) return rc;
-    return forward(x, y, idx, dtype, g, (hipStream_t)stream);
+    return forward(x, y, idx, MP3D_IDX_I32, dtype, g, (hipStream_t)stream);
 }
 
 int amp3d_forward(const void *x, void *y, int32_t *idx, int dtype, int64_t N, int64_t C,
@@ -270,7 +409,22 @@ int amp3d_forward(const void *x, void *y, int32_t *idx, int dtype, int64_t N, in
     if ((rc = set_adaptive_axis(&g.ax[1], H, oh, "H"))) return rc;
     if ((rc = set_adaptive_axis(&g.ax[2], W, ow, "W"))) return rc;
     if ((rc = finish_geom(&g, N, C))) return rc;
-    return forward(x, y, idx, dtype, g, (hipStream_t)stream);
+    return forward(x, y, idx, MP3D_IDX_I32, dtype, g, (hipStream_t)stream);
+}
+
+int mp3d_forward_ex(const void *x, void *y, void *idx, int dtype, int idx_type, int64_t N,
+                    int64_t C, int64_t D, int64_t H, int64_t W, int32_t od, int32_t oh,
+                    int32_t ow, const int32_t *kernel, const int32_t *stride, const int32_t *pad,
+                    const int32_t *dilation, void *stream)
+{
+    int rc = check_common(dtype, N, C, D, H, W);
+    if (rc) return rc;
+    if (idx_type != MP3D_IDX_I32 && idx_type != MP3D_IDX_I64)
+        return fail(MP3D_EDTYPE, "idx_type %d is not MP3D_IDX_I32 or MP3D_IDX_I64", idx_type);
+    Geom g;
+    if ((rc = set_axes_ex(&g, D, H, W, od, oh, ow, kernel, stride, pad, dilation))) return rc;
+    if ((rc = finish_geom(&g, N, C))) return rc;
+    return forward(x, y, idx, idx_type, dtype, g, (hipStream_t)stream);
 }
 
 int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype, int64_t N,
@@ -280,8 +434,6 @@ int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype, int64
 {
     int rc = check_common(dtype, N, C, D, H, W);
     if (rc) return rc;
-    if (overlap < -1 || overlap > 2)
-        return fail(MP3D_EINVAL, "overlap must be -1, 0, 1 or 2 (got %d)", overlap);
     const int64_t X[3] = {D, H, W};
     const int32_t O[3] = {od, oh, ow}, K[3] = {kd, kh, kw}, S[3] = {sd, sh, sw};
     const char *names[3] = {"D", "H", "W"};
@@ -297,23 +449,23 @@ int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype, int64
                             names[a], g.ax[a].O);
         }
     }
-    if ((rc = finish_geom(&g, N, C))) return rc;
-    const bool tiles = axis_tiles(g.ax[0]) && axis_tiles(g.ax[1]) && axis_tiles(g.ax[2]);
-    if (overlap == 0 && !tiles)
-        return fail(MP3D_ENOTDIV, "overlap=0 needs windows that tile every axis");
-    if (g.planes == 0) return MP3D_OK;
-    if (!gy || !idx || !gx) return fail(MP3D_EINVAL, "null tensor pointer");
-    // the gather is already the ordered sum (one window per input)
-    const BwdPath path = overlap == 0 || ((overlap == -1 || overlap == 2) && tiles)
-                             ? BwdPath::gather
-                             : overlap == 2 ? BwdPath::ordered : BwdPath::accumulate;
-    const hipStream_t s = (hipStream_t)stream;
-    switch (dtype) {
-    case MP3D_F32: return run_backward<F32>(gy, idx, gx, g, path, s);
-    case MP3D_F16: return run_backward<F16>(gy, idx, gx, g, path, s);
-    default: return run_backward<BF16>(gy, idx, gx, g, path, s);
-    }
+    return backward(gy, idx, MP3D_IDX_I32, gx, dtype, g, N, C, overlap, (hipStream_t)stream);
 }
+
+int mp3d_backward_ex(const void *gy, const void *idx, void *gx, int dtype, int idx_type,
+                     int64_t N, int64_t C, int64_t D, int64_t H, int64_t W, int32_t od,
+                     int32_t oh, int32_t ow, const int32_t *kernel, const int32_t *stride,
+                     const int32_t *pad, const int32_t *dilation, int overlap, void *stream)
+{
+    int rc = check_common(dtype, N, C, D, H, W);
+    if (rc) return rc;
+    if (idx_type != MP3D_IDX_I32 && idx_type != MP3D_IDX_I64)
+        return fail(MP3D_EDTYPE, "idx_type %d is not MP3D_IDX_I32 or MP3D_IDX_I64", idx_type);
+    Geom g;
+    if ((rc = set_axes_ex(&g, D, H, W, od, oh, ow, kernel, stride, pad, dilation))) return rc;
+    return backward(gy, idx, idx_type, gx, dtype, g, N, C, overlap, (hipStream_t)stream);
+}
+
 
 const char *mp3d_strerror(int code)
 {

@@ -106,9 +106,9 @@ __device__ __forceinline__ void store_span(typename T::raw *dst, const float *a,
 // windows as their flat output numbers do, so each element's fold is the
 // ascending-order sum, and within a phase every input has at most one
 // window, so plain LDS read-modify-writes suffice.
-template <typename T, int NT, bool ORD, int kRound>
+template <typename T, typename IT, int NT, bool ORD, int kRound>
 __global__ void __launch_bounds__(NT)
-bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
+bwd_slab_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
                 typename T::raw *__restrict__ gx, BwdPlan p)
 {
     using R = typename T::raw;
@@ -146,7 +146,7 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
             const int32_t e = (round * kRound + k) * NT + tid;
             ri[k] = -1;
             if (e < nw) {
-                ri[k] = idx[wbase + e];
+                ri[k] = ld_idx(idx, wbase + e);
                 rg[k] = gy[wbase + e];
             }
         }
@@ -161,7 +161,7 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
         // first window reaching x, in 32 bits (the plan admits only axes
         // where that form is exact)
         auto reach = [](const Axis &ax, uint32_t x) -> uint32_t {
-            if (ax.k) return x < (uint32_t)ax.k ? 0u : ax.dS.div(x - (uint32_t)ax.k) + 1u;
+            if (ax.k) return (uint32_t)ax.first_reaching((int32_t)x);
             return ax.dX.div(x * (uint32_t)ax.O);
         };
         const int32_t nslot = (nw + NT - 1) / NT;     // slots that hold a window somewhere
@@ -208,9 +208,9 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restric
 }
 
 // General boxes [d0,d1) x [h0,h1) x [w0,w1) (a slice does not fit in LDS).
-template <typename T>
+template <typename T, typename IT>
 __global__ void __launch_bounds__(kBlock)
-bwd_box_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
+bwd_box_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
                typename T::raw *__restrict__ gx, BwdPlan p)
 {
     using R = typename T::raw;
@@ -238,7 +238,7 @@ bwd_box_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict
         for (int32_t e = tid; e < cd * ch * cw; e += kBlock) {
             const int32_t owl = e % cw, r = e / cw, ohl = r % ch, odl = r / ch;
             const int64_t o = obase + ((od0 + odl) * B.O + oh0 + ohl) * Cw.O + ow0 + owl;
-            const int32_t i = idx[o];
+            const int32_t i = ld_idx(idx, o);
             if ((uint32_t)i < (uint32_t)p.g.in_plane) {
                 const int32_t d = i / (H * W), rem = i - d * H * W;
                 const int32_t h = rem / W, w = rem - h * W;
@@ -256,9 +256,9 @@ bwd_box_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict
     }
 }
 
-template <typename T>
+template <typename T, typename IT>
 __global__ void __launch_bounds__(kBlock)
-bwd_gather_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
+bwd_gather_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
                   typename T::raw *__restrict__ gx, GatherPlan p)
 {
     const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X;
@@ -272,16 +272,16 @@ bwd_gather_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restr
         const int64_t o = plane * (int64_t)p.g.out_plane +
                           ((d / p.qd) * OH + h / p.qh) * OW + w / p.qw;
         typename T::raw out = T::narrow(0.0f);
-        if (idx[o] == i) out = T::narrow(0.0f + T::widen(gy[o]));
+        if (ld_idx(idx, o) == i) out = T::narrow(0.0f + T::widen(gy[o]));
         gx[e] = out;
     }
 }
 
 }  // namespace
 
-template <typename T>
-hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
-                                const BwdPlan &p, hipStream_t s)
+template <typename T, typename IT>
+hipError_t launch_backward_tile(const void *gy, const IT *idx, void *gx, const BwdPlan &p,
+                                hipStream_t s)
 {
     using R = typename T::raw;
     int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)1 << 24);
@@ -290,36 +290,42 @@ hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
         // (the surplus blocks exit at once)
         if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
         if (p.nphase)
-            hipLaunchKernelGGL((bwd_slab_kernel<T, kOrdThreads, true, kOrdRound>), dim3((uint32_t)grid),
+            hipLaunchKernelGGL((bwd_slab_kernel<T, IT, kOrdThreads, true, kOrdRound>), dim3((uint32_t)grid),
                                dim3(kOrdThreads), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
         else
-            hipLaunchKernelGGL((bwd_slab_kernel<T, kSlabBlock, false, kBwdRound>), dim3((uint32_t)grid),
+            hipLaunchKernelGGL((bwd_slab_kernel<T, IT, kSlabBlock, false, kBwdRound>), dim3((uint32_t)grid),
                                dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
     } else {
-        hipLaunchKernelGGL(bwd_box_kernel<T>, dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
+        hipLaunchKernelGGL((bwd_box_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
                            (const R *)gy, idx, (R *)gx, p);
     }
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_backward_gather(const void *gy, const int32_t *idx, void *gx,
-                                  const GatherPlan &p, hipStream_t s)
+template <typename T, typename IT>
+hipError_t launch_backward_gather(const void *gy, const IT *idx, void *gx, const GatherPlan &p,
+                                  hipStream_t s)
 {
     using R = typename T::raw;
     const int64_t total = p.g.planes * (int64_t)p.g.in_plane;
     int64_t grid = (total + kBlock - 1) / kBlock;
     if (grid > (1 << 20)) grid = 1 << 20;
-    hipLaunchKernelGGL(bwd_gather_kernel<T>, dim3((uint32_t)grid), dim3(kBlock), 0, s,
+    hipLaunchKernelGGL((bwd_gather_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
                        (const R *)gy, idx, (R *)gx, p);
     return hipGetLastError();
 }
 
-template hipError_t launch_backward_tile<F32>(const void *, const int32_t *, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_tile<F16>(const void *, const int32_t *, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_tile<BF16>(const void *, const int32_t *, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_gather<F32>(const void *, const int32_t *, void *, const GatherPlan &, hipStream_t);
-template hipError_t launch_backward_gather<F16>(const void *, const int32_t *, void *, const GatherPlan &, hipStream_t);
-template hipError_t launch_backward_gather<BF16>(const void *, const int32_t *, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F32, int32_t>(const void *, const int32_t *, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F32, int64_t>(const void *, const int64_t *, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F16, int32_t>(const void *, const int32_t *, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F16, int64_t>(const void *, const int64_t *, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<BF16, int32_t>(const void *, const int32_t *, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<BF16, int64_t>(const void *, const int64_t *, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F32, int32_t>(const void *, const int32_t *, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F32, int64_t>(const void *, const int64_t *, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F16, int32_t>(const void *, const int32_t *, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F16, int64_t>(const void *, const int64_t *, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<BF16, int32_t>(const void *, const int32_t *, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<BF16, int64_t>(const void *, const int64_t *, void *, const GatherPlan &, hipStream_t);
 
 }  // namespace mp3d

@@ -7,6 +7,11 @@
 // Summary) requires a disjoint tiling when the axis divides evenly and an
 // overlap otherwise; window o = [floor(o*X/O), ceil((o+1)*X/O)) has both
 // properties.
+// Padding and dilation of fixed windows: the pages give no pooling rule
+// beyond "no padding".  Reading taken: window o takes the k taps
+// o*S - pad + j*dil, a tap outside the axis is padding that never wins, and
+// the taps span (k-1)*dil + 1 positions (the effective kernel of the
+// FlagGems conv_transpose2d PR page, Implementation, scatter condition).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,17 +44,25 @@ struct FastDiv {
 };
 
 // One spatial axis: extent X split into O windows; k > 0 selects fixed
-// windows of width k and stride s, k == 0 adaptive windows.  When every
-// numerator below fits 31 bits (`fast`), the divisions by O, X and s use
-// precomputed multiply-high constants instead of 64-bit division.
+// windows, k == 0 adaptive windows.  A fixed window o has k taps at
+// o*s - pad + j*dil (j < k), spanning ext = (k-1)*dil + 1 positions; taps
+// outside [0, X) are padding and never taken.  With pad = 0 and dil = 1
+// (`plain`) window o is [o*s, o*s + k).  When every numerator below fits 31
+// bits (`fast`), the divisions by O, X and s use precomputed multiply-high
+// constants instead of 64-bit division.
 struct Axis {
     int32_t X, O, k, s;
+    int32_t pad, dil, ext;
     FastDiv dO, dX, dS;
     int32_t fast;
 
-    __host__ static Axis make(int32_t X, int32_t O, int32_t k, int32_t s) {
+    __host__ static Axis make(int32_t X, int32_t O, int32_t k, int32_t s, int32_t pad = 0,
+                              int32_t dil = 1) {
         Axis a;
         a.X = X; a.O = O; a.k = k; a.s = s;
+        a.pad = k ? pad : 0;
+        a.dil = k ? dil : 1;
+        a.ext = k ? (k - 1) * dil + 1 : 0;
         a.dO = FastDiv((uint32_t)O);
         a.dX = FastDiv((uint32_t)X);
         a.dS = FastDiv((uint32_t)(s > 0 ? s : 1));
@@ -58,27 +71,31 @@ struct Axis {
         return a;
     }
 
+    __host__ __device__ inline bool plain() const { return pad == 0 && dil == 1; }
+
+    // Span [start, end) of window o; for fixed windows it may reach into
+    // the padding (start < 0 or end > X).
     __host__ __device__ inline int32_t start(int32_t o) const {
-        if (k) return o * s;
+        if (k) return o * s - pad;
         if (fast) return (int32_t)dO.div((uint32_t)(o * X));
         return (int32_t)(((int64_t)o * X) / O);
     }
     __host__ __device__ inline int32_t end(int32_t o) const {
-        if (k) return o * s + k;
+        if (k) return o * s - pad + ext;
         if (fast) return (int32_t)dO.div((uint32_t)((o + 1) * X + O - 1));
         return (int32_t)((((int64_t)o + 1) * X + O - 1) / O);
     }
-    // First window whose end lies beyond position p (windows before it
+    // First window whose span ends beyond position p (windows before it
     // cannot contain p or anything after it).
     __host__ __device__ inline int32_t first_reaching(int32_t p) const {
-        if (k) return p < k ? 0 : (int32_t)dS.div((uint32_t)(p - k)) + 1;
+        if (k) return p + pad < ext ? 0 : (int32_t)dS.div((uint32_t)(p + pad - ext)) + 1;
         if (fast) return (int32_t)dX.div((uint32_t)(p * O));
         return (int32_t)(((int64_t)p * O) / X);
     }
-    // Last window that starts at or before position p, clamped to O-1.
+    // Last window whose span starts at or before position p, clamped to O-1.
     __host__ __device__ inline int32_t last_starting(int32_t p) const {
         int32_t o;
-        if (k) o = (int32_t)dS.div((uint32_t)p);
+        if (k) o = (int32_t)dS.div((uint32_t)(p + pad));
         else if (fast) o = (int32_t)dX.div((uint32_t)((p + 1) * O - 1));
         else o = (int32_t)(((((int64_t)p + 1) * O) - 1) / X);
         return o < O - 1 ? o : O - 1;
@@ -125,6 +142,10 @@ struct Geom {
     Axis ax[3];              // d, h, w
     int32_t in_plane;        // D*H*W (fits int32 by validation)
     int32_t out_plane;       // OD*OH*OW
+
+    __host__ __device__ inline bool plain() const {
+        return ax[0].plain() && ax[1].plain() && ax[2].plain();
+    }
 };
 
 }  // namespace mp3d

@@ -13,6 +13,20 @@ namespace mp3d {
 constexpr int kBlock = 256;            // threads per workgroup (4 waves)
 constexpr int kSlabThreads = 512;      // threads per backward slab workgroup
 
+// Index elements come as int32 (the library's own) or int64 (torch's).  An
+// int64 value outside the int32 range reads as -1, which the backward
+// ignores like any value outside the plane.
+template <typename IT>
+__device__ __forceinline__ int32_t ld_idx(const IT *p, int64_t o)
+{
+    if constexpr (sizeof(IT) == 4) {
+        return p[o];
+    } else {
+        const int64_t v = p[o];
+        return v == (int64_t)(int32_t)v ? (int32_t)v : -1;
+    }
+}
+
 // Forward through LDS: each workgroup owns an output tile
 // [od0,od0+tod) x [oh0,oh0+toh) x [ow0,ow0+tow) of one plane, stages the
 // input box those windows cover in LDS, and reduces every window there.
@@ -56,6 +70,16 @@ constexpr int kBwdRound = 8;               // slab: windows per thread fetched p
 constexpr int kOrdThreads = 256;           // threads per ordered slab workgroup
 constexpr int kOrdRound = 8;               // ordered slab: windows per thread (one round)
 constexpr int kMaxPhase = 64;              // ordered slab: at most this many phases
+
+// General forward (forward_ex.hip): one thread per output, any geometry.
+struct ExPlan {
+    Geom g;
+    int64_t total;             // outputs
+    int32_t km;                // 3: at most three taps per window and axis; 0: any
+    int32_t fast32;            // total < 2^31: plane_div applies
+    FastDiv plane_div;         // by out_plane
+    FastDiv ow_div, oh_div;    // by OW, then by OH
+};
 
 // Ordered gather for any geometry (small.hip): one thread per input
 // element visits every window containing it in ascending output order.
@@ -135,6 +159,7 @@ bool plan_backward(const Geom &g, bool ordered, BwdPlan *p);
 bool plan_small_forward(const Geom &g, SmallPlan *p);
 bool plan_small_backward(const Geom &g, SmallPlan *p);
 void plan_ordered(const Geom &g, OrdPlan *p);
+void plan_ex(const Geom &g, ExPlan *p);
 
 template <typename T>
 hipError_t launch_forward_tile(const void *x, void *y, int32_t *idx,
@@ -148,20 +173,22 @@ hipError_t launch_forward_col(const void *x, void *y, int32_t *idx,
 template <typename T>
 hipError_t launch_forward_direct(const void *x, void *y, int32_t *idx,
                                  const Geom &g, hipStream_t s);
-template <typename T>
-hipError_t launch_backward_tile(const void *gy, const int32_t *idx, void *gx,
-                                const BwdPlan &p, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_forward_ex(const void *x, void *y, IT *idx, const ExPlan &p, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_backward_tile(const void *gy, const IT *idx, void *gx, const BwdPlan &p,
+                                hipStream_t s);
 template <typename T>
 hipError_t launch_forward_small(const void *x, void *y, int32_t *idx,
                                 const SmallPlan &p, hipStream_t s);
-template <typename T>
-hipError_t launch_backward_small(const void *gy, const int32_t *idx, void *gx,
-                                 const SmallPlan &p, hipStream_t s);
-template <typename T>
-hipError_t launch_backward_gather(const void *gy, const int32_t *idx, void *gx,
-                                  const GatherPlan &p, hipStream_t s);
-template <typename T>
-hipError_t launch_backward_ordered(const void *gy, const int32_t *idx, void *gx,
-                                   const OrdPlan &p, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_backward_small(const void *gy, const IT *idx, void *gx, const SmallPlan &p,
+                                 hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_backward_gather(const void *gy, const IT *idx, void *gx, const GatherPlan &p,
+                                  hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_backward_ordered(const void *gy, const IT *idx, void *gx, const OrdPlan &p,
+                                   hipStream_t s);
 
 }  // namespace mp3d

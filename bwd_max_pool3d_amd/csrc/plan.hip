@@ -196,7 +196,7 @@ bool plan_col(const Geom &g, int es, const void *x, ColPlan *p)
 // it may be more.
 static int32_t axis_cover(const Axis &a)
 {
-    if (a.k) return a.k <= a.s ? 1 : a.k <= 2 * a.s ? 2 : 0;
+    if (a.k) return a.ext <= a.s ? 1 : a.ext <= 2 * a.s ? 2 : 0;
     if (a.O > 65536) return 0;
     int32_t c = 1;
     for (int32_t o = 0; o + 1 < a.O; ++o) {
@@ -248,7 +248,7 @@ bool plan_small_backward(const Geom &g, SmallPlan *p)
 // a window start, so scanning the starts is enough.
 static int32_t axis_depth(const Axis &a)
 {
-    if (a.k) return (int32_t)std::min<int64_t>(cdiv(a.k, a.s), a.O);
+    if (a.k) return (int32_t)std::min<int64_t>(cdiv(a.ext, a.s), a.O);
     if (a.O > (1 << 20)) return 0;
     int32_t m = 1;
     for (int32_t o = 0; o < a.O; ++o) {
@@ -298,8 +298,11 @@ bool plan_backward(const Geom &g, bool ordered, BwdPlan *p)
     p->md = p->mh = p->mw = 0;
     if (ordered) {
         if (!(p->th == H && p->tw == W)) return false;
-        for (int a = 0; a < 3; ++a)                    // the kernel ranks in 32 bits
-            if (!g.ax[a].k && !g.ax[a].fast) return false;
+        // the kernel ranks in 32 bits, and a rank counts windows between the
+        // first one reaching a position and the window itself: all of them
+        // contain the position only when windows are contiguous
+        for (int a = 0; a < 3; ++a)
+            if ((!g.ax[a].k && !g.ax[a].fast) || g.ax[a].dil != 1) return false;
         const Axis &A = g.ax[0];
         const int32_t md = axis_depth(A), mh = axis_depth(g.ax[1]), mw = axis_depth(g.ax[2]);
         if (!md || !mh || !mw || (int64_t)md * mh * mw > kMaxPhase) return false;
@@ -329,6 +332,21 @@ bool plan_backward(const Geom &g, bool ordered, BwdPlan *p)
     // + alignment shift and the rounding of the zero fill to 16 bytes
     p->lds_bytes = (uint32_t)(((int64_t)p->td * p->th * p->tw + 8) * 4);
     return true;
+}
+
+void plan_ex(const Geom &g, ExPlan *p)
+{
+    p->g = g;
+    p->total = g.planes * (int64_t)g.out_plane;
+    p->km = 3;
+    for (int a = 0; a < 3; ++a) {
+        const Axis &ax = g.ax[a];
+        if ((ax.k ? (int64_t)ax.k : axis_widest(ax)) > 3) p->km = 0;
+    }
+    p->fast32 = p->total < ((int64_t)1 << 31);
+    p->plane_div = FastDiv((uint32_t)g.out_plane);
+    p->ow_div = FastDiv((uint32_t)g.ax[2].O);
+    p->oh_div = FastDiv((uint32_t)g.ax[1].O);
 }
 
 void plan_ordered(const Geom &g, OrdPlan *p)

@@ -84,9 +84,9 @@ fwd_small_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
 // The (at most 8) windows are visited in ascending output order, so the
 // binary32 sum from +0 is the same fold the ordered definition gives, bit
 // for bit, and it is rounded once.
-template <typename T>
+template <typename T, typename IT>
 __global__ void __launch_bounds__(kBlock)
-bwd_small_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
+bwd_small_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
                  typename T::raw *__restrict__ gx, SmallPlan p)
 {
     using R = typename T::raw;
@@ -124,7 +124,7 @@ bwd_small_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restri
             c[a] = min(max(q, 0), O[a] - 1);          // in range even when unused
         }
         const int64_t o = obase + ((int64_t)c[0] * OH + c[1]) * OW + c[2];
-        ri[k] = idx[o];
+        ri[k] = ld_idx(idx, o);
         rg[k] = gy[o];
         on[k] = valid;
     }
@@ -139,9 +139,9 @@ bwd_small_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restri
 // window containing it, in ascending output order, and keeps the elements
 // whose argmax it is: the ordered binary32 sum from +0, rounded once.  The
 // general fallback of the ordered backward; loads follow one another.
-template <typename T>
+template <typename T, typename IT>
 __global__ void __launch_bounds__(kBlock)
-bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const int32_t *__restrict__ idx,
+bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
                    typename T::raw *__restrict__ gx, OrdPlan p)
 {
     const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
@@ -163,7 +163,7 @@ bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const int32_t *__rest
             for (int32_t oh = h0; oh <= h1; ++oh)
                 for (int32_t ow = w0; ow <= w1; ++ow) {
                     const int64_t o = obase + ((int64_t)od * OH + oh) * OW + ow;
-                    const int32_t v = idx[o];
+                    const int32_t v = ld_idx(idx, o);
                     const float g = T::widen(gy[o]);
                     if (v == i) acc = acc + g;
                 }
@@ -173,13 +173,13 @@ bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const int32_t *__rest
 
 }  // namespace
 
-template <typename T>
-hipError_t launch_backward_ordered(const void *gy, const int32_t *idx, void *gx, const OrdPlan &p,
+template <typename T, typename IT>
+hipError_t launch_backward_ordered(const void *gy, const IT *idx, void *gx, const OrdPlan &p,
                                    hipStream_t s)
 {
     using R = typename T::raw;
     const int64_t grid = std::min<int64_t>((p.total + kBlock - 1) / kBlock, (int64_t)1 << 20);
-    hipLaunchKernelGGL(bwd_ordered_kernel<T>, dim3((uint32_t)grid), dim3(kBlock), 0, s,
+    hipLaunchKernelGGL((bwd_ordered_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
                        (const R *)gy, idx, (R *)gx, p);
     return hipGetLastError();
 }
@@ -194,12 +194,12 @@ hipError_t launch_forward_small(const void *x, void *y, int32_t *idx, const Smal
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_backward_small(const void *gy, const int32_t *idx, void *gx, const SmallPlan &p,
+template <typename T, typename IT>
+hipError_t launch_backward_small(const void *gy, const IT *idx, void *gx, const SmallPlan &p,
                                  hipStream_t s)
 {
     using R = typename T::raw;
-    hipLaunchKernelGGL(bwd_small_kernel<T>, dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
+    hipLaunchKernelGGL((bwd_small_kernel<T, IT>), dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
                        s, (const R *)gy, idx, (R *)gx, p);
     return hipGetLastError();
 }
@@ -207,11 +207,18 @@ hipError_t launch_backward_small(const void *gy, const int32_t *idx, void *gx, c
 template hipError_t launch_forward_small<F32>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
 template hipError_t launch_forward_small<F16>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
 template hipError_t launch_forward_small<BF16>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_small<F32>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_small<F16>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_small<BF16>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_ordered<F32>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
-template hipError_t launch_backward_ordered<F16>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
-template hipError_t launch_backward_ordered<BF16>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
+
+template hipError_t launch_backward_small<F32, int32_t>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_small<F32, int64_t>(const void *, const int64_t *, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_small<F16, int32_t>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_small<F16, int64_t>(const void *, const int64_t *, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_small<BF16, int32_t>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_small<BF16, int64_t>(const void *, const int64_t *, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F32, int32_t>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F32, int64_t>(const void *, const int64_t *, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F16, int32_t>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F16, int64_t>(const void *, const int64_t *, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<BF16, int32_t>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<BF16, int64_t>(const void *, const int64_t *, void *, const OrdPlan &, hipStream_t);
 
 }  // namespace mp3d

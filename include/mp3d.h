@@ -58,7 +58,8 @@ enum mp3d_status {
     MP3D_EINVAL = 1,    /* null pointer with work to do, a size, kernel,
                            stride or output extent <= 0, a window larger
                            than its axis, or inconsistent shapes */
-    MP3D_EDTYPE = 2,    /* dtype is not one of MP3D_F32/F16/BF16 */
+    MP3D_EDTYPE = 2,    /* dtype is not one of MP3D_F32/F16/BF16, or idx_type
+                           not one of MP3D_IDX_I32/I64 */
     MP3D_ENOTDIV = 3,   /* overlap = 0 asked for, but the windows do not
                            tile every axis (see mp3d_backward) */
     MP3D_EOVERFLOW = 4, /* D*H*W > INT32_MAX (int32 idx impossible) or an
@@ -67,6 +68,9 @@ enum mp3d_status {
 };
 
 enum mp3d_dtype { MP3D_F32 = 0, MP3D_F16 = 1, MP3D_BF16 = 2 };
+
+/* Index element type of the _ex entry points (the others use int32). */
+enum mp3d_index { MP3D_IDX_I32 = 0, MP3D_IDX_I64 = 1 };
 
 /* Forward with fixed windows (teenygrad "Struct Maxpool3dForward",
  * description): kernel (kd, kh, kw), stride (sd, sh, sw), no padding.
@@ -131,6 +135,60 @@ int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype,
 /* Fixed-window output extent (X - k)/s + 1 into *out.  MP3D_EINVAL if
  * k <= 0, s <= 0, X < k or out is NULL. */
 int mp3d_out_size(int64_t X, int32_t k, int32_t s, int64_t *out);
+
+/* --- Padding, dilation, ceil mode and int64 indices ------------------
+ *
+ * The pages define fixed windows without padding ("Struct
+ * Maxpool3dForward", teenygrad, description).  These entry points widen
+ * that surface; the reading taken where the pages are silent: window o on
+ * an axis takes the k taps o*s - pad + j*dil (0 <= j < k), which span
+ * (k-1)*dil + 1 positions (the effective kernel of the FlagGems
+ * conv_transpose2d PR page, Implementation); a tap outside the axis is
+ * padding and is never taken.  y is still the first maximum in d, h, w
+ * scan order (NaN first) and idx its flat plane position.  A window whose
+ * taps all fall in the padding (only possible when the dilation steps over
+ * the whole axis) gives y = -inf and idx = -1.
+ *
+ * Per axis: kernel k >= 1, stride s >= 1, pad >= 0, dilation >= 1,
+ * 2*pad <= k (as torch requires), and the span must fit the padded axis:
+ * X + 2*pad >= (k-1)*dil + 1.  Otherwise MP3D_EINVAL. */
+
+/* Output extent into *out.  ceil_mode 0: (X + 2*pad - span)/s + 1, rounded
+ * down.  ceil_mode 1: rounded up, less one if that last window would start
+ * at or beyond X + pad (so every window starts inside the input or the
+ * left padding). */
+int mp3d_out_size_ex(int64_t X, int32_t k, int32_t s, int32_t pad, int32_t dilation,
+                     int ceil_mode, int64_t *out);
+
+/* Forward with padding and dilation (kernel, stride, pad and dilation are
+ * arrays of 3, d/h/w; pad and dilation may be NULL for 0 and 1).  An axis
+ * with kernel = stride = 0 uses adaptive windows (as amp3d_forward) with
+ * padding 0 and dilation 1.  (od, oh, ow) are the output extents: on a
+ * fixed axis each must be the floor-mode or the ceil-mode extent of
+ * mp3d_out_size_ex, and that choice is the ceil mode.  idx_type selects
+ * int32 or int64 idx; idx may be NULL (values only).  With no padding,
+ * dilation 1 and int32 idx the result is that of mp3d_forward /
+ * amp3d_forward, by the same kernels. */
+int mp3d_forward_ex(const void *x, void *y, void *idx, int dtype, int idx_type,
+                    int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                    int32_t od, int32_t oh, int32_t ow,
+                    const int32_t *kernel, const int32_t *stride,
+                    const int32_t *pad, const int32_t *dilation, void *stream);
+
+/* Backward for the geometries of mp3d_forward_ex: the same sums as
+ * mp3d_backward (the result depends only on gy and idx; the window rule
+ * tells the library which windows can reach a block of gx), with idx of
+ * idx_type.  int64 idx values outside the plane are ignored.  overlap as
+ * for mp3d_backward; overlap 0 needs no padding, dilation 1 and tiling
+ * windows.  The ordered path (overlap 2) adds rank by rank only for
+ * contiguous windows (dilation 1) and otherwise takes the ordered
+ * gather. */
+int mp3d_backward_ex(const void *gy, const void *idx, void *gx, int dtype, int idx_type,
+                     int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                     int32_t od, int32_t oh, int32_t ow,
+                     const int32_t *kernel, const int32_t *stride,
+                     const int32_t *pad, const int32_t *dilation,
+                     int overlap, void *stream);
 
 /* Text for a status code (static storage). */
 const char *mp3d_strerror(int code);

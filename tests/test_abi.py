@@ -62,6 +62,72 @@ def bwd(*, gy=FAKE, dtype=0, shape=(1, 1, 4, 4, 4), out=(2, 2, 2), k=(0, 0, 0), 
     return _lib.load().mp3d_backward(gy, FAKE, FAKE, dtype, *shape, *out, *k, *s, overlap, None)
 
 
+def _a3(v):
+    import ctypes
+    return None if v is None else (ctypes.c_int32 * 3)(*v)
+
+
+def fwdx(*, x=FAKE, dtype=0, it=0, shape=(1, 1, 6, 6, 6), out=(3, 3, 3), k=(3, 3, 3),
+         s=(2, 2, 2), p=(1, 1, 1), d=(1, 1, 1)):
+    return _lib.load().mp3d_forward_ex(x, FAKE, FAKE, dtype, it, *shape, *out, _a3(k), _a3(s),
+                                       _a3(p), _a3(d), None)
+
+
+def bwdx(*, gy=FAKE, dtype=0, it=0, shape=(1, 1, 6, 6, 6), out=(3, 3, 3), k=(3, 3, 3),
+         s=(2, 2, 2), p=(1, 1, 1), d=(1, 1, 1), overlap=-1):
+    return _lib.load().mp3d_backward_ex(gy, FAKE, FAKE, dtype, it, *shape, *out, _a3(k), _a3(s),
+                                        _a3(p), _a3(d), overlap, None)
+
+
+def outx(X, k, s, p=0, d=1, ceil=0):
+    import ctypes
+    v = ctypes.c_int64(-99)
+    rc = _lib.load().mp3d_out_size_ex(X, k, s, p, d, ceil, ctypes.byref(v))
+    return rc, v.value
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: fwdx(it=2), _lib.MP3D_EDTYPE),
+    (lambda: fwdx(dtype=4), _lib.MP3D_EDTYPE),
+    (lambda: fwdx(x=None), _lib.MP3D_EINVAL),
+    (lambda: fwdx(k=None), _lib.MP3D_EINVAL),
+    (lambda: fwdx(p=(2, 1, 1)), _lib.MP3D_EINVAL),        # pad > kernel / 2
+    (lambda: fwdx(p=(-1, 1, 1)), _lib.MP3D_EINVAL),
+    (lambda: fwdx(d=(1, 0, 1)), _lib.MP3D_EINVAL),
+    (lambda: fwdx(out=(5, 3, 3)), _lib.MP3D_EINVAL),      # floor 3, ceil 4: (6+2-3)/2 = 2.5
+    (lambda: fwdx(out=(2, 3, 3)), _lib.MP3D_EINVAL),
+    (lambda: fwdx(shape=(1, 1, 2, 6, 6), out=(1, 3, 3), k=(3, 3, 3), p=(0, 1, 1), d=(2, 1, 1)),
+     _lib.MP3D_EINVAL),                                    # span 5 exceeds 2 + 0
+    (lambda: fwdx(k=(0, 3, 3), s=(0, 2, 2), p=(1, 1, 1)), _lib.MP3D_EINVAL),  # adaptive with pad
+    (lambda: bwdx(overlap=0), _lib.MP3D_ENOTDIV),          # padded windows never take the gather
+    (lambda: bwdx(overlap=5), _lib.MP3D_EINVAL),
+    (lambda: bwdx(it=-1), _lib.MP3D_EDTYPE),
+    (lambda: bwdx(out=(9, 3, 3)), _lib.MP3D_EINVAL),
+])
+def test_validation_codes_ex(call, code):
+    assert call() == code
+    assert _lib.load().mp3d_last_error().decode() != ""
+
+
+def test_out_size_ex():
+    assert outx(10, 3, 2, 1) == (0, 5)
+    assert outx(10, 3, 2, 1, 1, 1) == (0, 6)
+    assert outx(6, 3, 2, 1, 1, 0) == (0, 3)
+    assert outx(6, 3, 2, 1, 1, 1) == (0, 4)      # last window starts at 5 < 6 + 1
+    assert outx(5, 2, 2, 1, 1, 1) == (0, 3)      # (5+2-2)/2 = 2.5 -> 3 + 1 = 4, but 3*2 >= 5+1
+    assert outx(6, 2, 2, 1, 1, 1) == (0, 4)      # (6+2-2)/2 = 3 exactly: 4 windows
+    assert outx(4, 2, 3, 1, 1, 1) == (0, 2)
+    assert outx(2, 2, 1, 1, 3, 0) == (0, 1)
+    assert outx(2, 3, 1, 0, 2, 0)[0] == _lib.MP3D_EINVAL
+    assert outx(5, 2, 2, 0, 1, 2)[0] == _lib.MP3D_EINVAL
+    assert outx(5, 0, 2)[0] == _lib.MP3D_EINVAL
+
+
+def test_ex_empty_batch_is_a_no_op():
+    assert fwdx(x=None, shape=(0, 2, 6, 6, 6)) == _lib.MP3D_OK
+    assert bwdx(gy=None, shape=(3, 0, 6, 6, 6)) == _lib.MP3D_OK
+
+
 @pytest.mark.parametrize("call,code", [
     (lambda: fwd(dtype=3), _lib.MP3D_EDTYPE),
     (lambda: fwd(dtype=-1), _lib.MP3D_EDTYPE),

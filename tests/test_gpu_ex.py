@@ -1,0 +1,128 @@
+"""Padding, dilation, ceil mode and int64 indices on the device, against
+the oracle's padded / dilated forward (itself pinned to torch's CPU pooling)
+and its backward, through the C ABI.  y bits and idx must match exactly;
+gx must match the ordered sum exactly on the ordered path and meet the
+accumulate path's bar otherwise."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import _gpu
+import _pins
+import bwd_max_pool3d_amd as mp
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [torch.float32, torch.float16, torch.bfloat16]
+DT_ID = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
+# (shape, kernel, stride, pad, dilation, ceil_mode)
+CASES = [
+    ((2, 3, 9, 12, 13), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),   # 3-D CNN stem pool
+    ((1, 2, 9, 12, 13), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), True),
+    ((2, 2, 7, 9, 11), (2, 2, 2), (2, 2, 2), (1, 1, 1), (1, 1, 1), True),
+    ((1, 2, 6, 7, 40), (2, 3, 2), (2, 2, 2), (0, 1, 1), (1, 1, 1), False),
+    ((1, 1, 10, 11, 12), (3, 2, 3), (1, 2, 3), (1, 1, 0), (2, 3, 1), False),
+    ((1, 1, 9, 10, 70), (3, 3, 2), (2, 3, 2), (1, 1, 1), (2, 2, 3), True),
+    ((2, 1, 5, 6, 7), (1, 1, 1), (2, 2, 2), (0, 0, 0), (1, 1, 1), True),
+    ((1, 1, 6, 7, 8), (4, 5, 2), (3, 2, 1), (2, 2, 1), (1, 1, 2), True),       # more than 3 taps
+    ((1, 1, 2, 3, 4), (2, 2, 2), (1, 1, 1), (1, 1, 1), (3, 2, 2), False),      # all-padding windows
+    ((1, 1, 3, 200, 300), (3, 3, 3), (1, 2, 2), (1, 1, 1), (1, 1, 1), False),  # slices beyond LDS
+    ((1, 3, 16, 32, 32), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), False),   # stride 1, overlap 3
+]
+
+
+def _cid(c):
+    shape, k, s, p, d, cm = c
+    j = lambda t: "".join(map(str, t))
+    return "%s-k%ss%sp%sd%s%s" % ("x".join(map(str, shape)), j(k), j(s), j(p), j(d),
+                                  "-ceil" if cm else "")
+
+
+def _oracle_ex(orc, x, case):
+    shape, k, s, p, d, cm = case
+    o3 = _pins.ex_out(orc, shape, k, s, p, d, cm)
+    return orc.forward_ex(_gpu.storage(x), _gpu.CODE[x.dtype], o3, k, s, p, d)
+
+
+def _check_forward(y, idx, yo, io, what):
+    assert np.array_equal(idx.cpu().numpy().astype(np.int64), io), "%s: idx differs" % what
+    assert np.array_equal(_gpu.storage(y).view(np.uint8), yo.view(np.uint8)), "%s: y bits differ" % what
+
+
+@pytest.mark.parametrize("index_dtype", [torch.int32, torch.int64], ids=["i32", "i64"])
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+@pytest.mark.parametrize("case", CASES, ids=_cid)
+def test_forward_backward_ex(orc, case, dtype, index_dtype):
+    shape, k, s, p, d, cm = case
+    code = _gpu.CODE[dtype]
+    base = abs(hash(case)) % 10000
+    for j, kind in enumerate(("normal", "ties", "sparse_nan", "special")):
+        x = _pins.from_storage(_pins.draw(shape, code, kind, base + j), code).cuda()
+        y, idx = mp.mp3d_forward_ex(x, k, s, p, d, cm, index_dtype=index_dtype)
+        assert idx.dtype == index_dtype
+        yo, io = _oracle_ex(orc, x, case)
+        _check_forward(y, idx, yo, io, "%s %s" % (_cid(case), kind))
+        yv = mp.mp3d_forward_ex(x, k, s, p, d, cm, index_dtype=index_dtype, indices=False)
+        assert np.array_equal(_gpu.storage(yv).view(np.uint8), yo.view(np.uint8))
+    gy = _pins.from_storage(_pins.draw(tuple(y.shape), code, "normal", base + 9), code).cuda()
+    idx32 = torch.from_numpy(idx.cpu().numpy().astype(np.int32))
+    for overlap, exact in ((-1, False), (2, True)):
+        gx = mp.mp3d_backward_ex(gy, idx, shape, k, s, p, d, overlap=overlap)
+        _gpu.check_backward(orc, gy.cpu(), idx32, shape, gx, exact=exact,
+                            what="%s overlap=%d" % (_cid(case), overlap))
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+def test_int64_plain_and_adaptive(orc, dtype):
+    """int64 indices for the plain fixed and the adaptive forms (the fast
+    kernels write int32 only; int64 goes through the general kernel): the
+    same y and the same positions as the int32 path and the oracle."""
+    code = _gpu.CODE[dtype]
+    for shape, out, k, s in [((2, 3, 10, 12, 14), None, (2, 2, 2), (2, 2, 2)),
+                             ((1, 2, 9, 13, 15), None, (3, 3, 3), (2, 2, 2)),
+                             ((2, 2, 10, 11, 12), (4, 5, 6), None, None),
+                             ((1, 2, 7, 7, 7), (8, 8, 8), None, None)]:
+        x = _pins.from_storage(_pins.draw(shape, code, "ties", 31), code).cuda()
+        if k is None:
+            y, idx = mp.amp3d_forward(x, out, index_dtype=torch.int64)
+            y32, idx32 = mp.amp3d_forward(x, out)
+        else:
+            y, idx = mp.mp3d_forward(x, k, s, index_dtype=torch.int64)
+            y32, idx32 = mp.mp3d_forward(x, k, s)
+        assert idx.dtype == torch.int64
+        yo, io = _gpu.oracle_forward(orc, x.cpu(), out, k, s)
+        _gpu.assert_forward_match(y, idx32, yo, io, "int32 %s" % (shape,))
+        assert np.array_equal(idx.cpu().numpy(), io.astype(np.int64))
+        assert np.array_equal(_gpu.storage(y).view(np.uint8), yo.view(np.uint8))
+        gy = _pins.from_storage(_pins.draw(tuple(y.shape), code, "normal", 32), code).cuda()
+        for overlap in (-1, 2):
+            g64 = mp.mp3d_backward(gy, idx, shape, k, s, overlap=overlap)
+            g32 = mp.mp3d_backward(gy, idx32, shape, k, s, overlap=overlap)
+            _gpu.check_backward(orc, gy.cpu(), idx32.cpu(), shape, g64, exact=overlap == 2,
+                                what="int64 %s" % (shape,))
+            if overlap == 2:
+                assert torch.equal(g64.view(torch.uint8), g32.view(torch.uint8))
+
+
+def test_int64_idx_out_of_range_ignored(orc):
+    """int64 idx values outside the plane (negative, past the plane, past
+    int32) contribute nothing."""
+    shape, k, s, p, d = (1, 2, 6, 7, 8), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1)
+    x = _pins.from_storage(_pins.draw(shape, 0, "normal", 41), 0).cuda()
+    y, idx = mp.mp3d_forward_ex(x, k, s, p, d, index_dtype=torch.int64)
+    bad = idx.clone().view(-1)
+    bad[0::7] = -5
+    bad[1::7] = 6 * 7 * 8
+    bad[2::7] = 1 << 40
+    bad[3::7] = (1 << 32) + 3            # low 32 bits are a valid position
+    bad = bad.view(idx.shape)
+    gy = _pins.from_storage(_pins.draw(tuple(y.shape), 0, "normal", 42), 0).cuda()
+    ref = bad.cpu().numpy()
+    ref = np.where((ref >= 0) & (ref < 6 * 7 * 8), ref, -1).astype(np.int32)
+    for overlap in (-1, 1, 2):
+        gx = mp.mp3d_backward_ex(gy, bad, shape, k, s, p, d, overlap=overlap)
+        _gpu.check_backward(orc, gy.cpu(), torch.from_numpy(ref), shape, gx, exact=overlap == 2,
+                            what="out-of-range int64 overlap=%d" % overlap)
