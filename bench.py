@@ -22,8 +22,10 @@ the step time and the metric; a second pass of K steps with a HIP event
 pair around every op on its launch stream gives the per-op durations and
 the roofline of the dominant op (those events cost a few microseconds per
 op, so that pass is not the metric).  The values-only forward of each
-workload (no index written) and the ordered backward (overlap=2) are timed
-the same way, apart from the step, and reported on their own.
+workload (no index written), the forward with int64 indices, the fixed
+workloads with padding k//2 (forward and backward) and the ordered backward
+(overlap=2) are timed the same way, apart from the step, and reported on
+their own.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (planes shard across GPUs with no communication, so more GPUs are not
@@ -71,11 +73,11 @@ class Op:
         return "%s.%s" % (self.wl.name, self.kind)
 
 
-def build_ops(torch, mp, workloads):
+def build_ops(torch, mp, workloads, variants=True):
     """The step's ops (forwards, then backwards) and, apart from the step,
     the variants: the values-only forward of each workload (idx NULL:
     |x|+|y| bytes) and the ordered (bit-reproducible) backward."""
-    fwd_ops, bwd_ops, vo_ops, ord_ops = [], [], [], []
+    fwd_ops, bwd_ops, vo_ops, ord_ops, exf_ops, exb_ops = [], [], [], [], [], []
     for wl in workloads.WORKLOADS:
         x = wl.make_x().cuda()
         N, C, D, H, W = wl.shape
@@ -110,8 +112,41 @@ def build_ops(torch, mp, workloads):
             o = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
                 gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, overlap=2, out=gx))
             ord_ops.append(Op(wl, "bwd_ordered", o, bbytes, nin, "ordered backward"))
+        if not variants:
+            continue
+        # int64 indices (torch's index type): general forward kernel
+        idx64 = torch.empty(oshape, dtype=torch.int64, device="cuda")
+        if wl.adaptive:
+            f64 = (lambda x=x, o3=o3, y=y, i=idx64: mp.amp3d_forward(
+                x, o3, out=(y, i), index_dtype=torch.int64))
+        else:
+            f64 = (lambda x=x, wl=wl, y=y, i=idx64: mp.mp3d_forward(
+                x, wl.kernel, wl.stride, out=(y, i), index_dtype=torch.int64))
+        exf_ops.append(Op(wl, "fwd_i64", f64, nin * es + nout * es + nout * 8, nin,
+                          "forward, int64 indices"))
+        if not wl.adaptive:
+            # padding k // 2 on every axis (the usual "same"-style pooling)
+            pad = tuple(k // 2 for k in wl.kernel)
+            po3 = tuple(mp.mp3d_out_size_ex(X, k, s, p) for X, k, s, p in
+                        zip(wl.shape[2:], wl.kernel, wl.stride, pad))
+            pshape = (N, C) + po3
+            py = torch.empty(pshape, dtype=x.dtype, device="cuda")
+            pidx = torch.empty(pshape, dtype=torch.int32, device="cuda")
+            npo = py.numel()
+            fp = (lambda x=x, wl=wl, pad=pad, py=py, pidx=pidx: mp.mp3d_forward_ex(
+                x, wl.kernel, wl.stride, pad, out=(py, pidx)))
+            exf_ops.append(Op(wl, "fwd_pad", fp, nin * es + npo * es + npo * 4, nin,
+                              "forward, padding k//2"))
+            if wl.backward:
+                fp()
+                pgy = wl.make_gy(pshape).cuda()
+                pgx = torch.empty(wl.shape, dtype=x.dtype, device="cuda")
+                bp = (lambda g=pgy, i=pidx, wl=wl, pad=pad, gx=pgx: mp.mp3d_backward_ex(
+                    g, i, wl.shape, wl.kernel, wl.stride, pad, out=gx))
+                exb_ops.append(Op(wl, "bwd_pad", bp, npo * es + npo * 4 + nin * es, nin,
+                                  "backward, padding k//2"))
     # the variants run in the step's order: forwards, then backwards
-    return fwd_ops + bwd_ops, vo_ops + ord_ops
+    return fwd_ops + bwd_ops, (vo_ops + exf_ops + ord_ops + exb_ops) if variants else []
 
 
 def cpu_baseline(target_s: float):
@@ -191,6 +226,10 @@ def main():
     ap.add_argument("--only", default=None,
                     help="time only the ops whose name contains this text (profiling aid; "
                          "the JSON then covers that subset)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="report the step alone, without the variant ops (values-only "
+                         "forward, int64 indices, padding, ordered backward); for profiles "
+                         "whose per-kernel averages must cover the step's launches only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the step, run a plain 1 GiB device copy 10 times "
                          "(reference kernel for the HBM byte counters)")
@@ -229,7 +268,7 @@ def main():
     torch.cuda.empty_cache()
 
     print("[bench] building inputs", file=sys.stderr, flush=True)
-    ops, vo_ops = build_ops(torch, mp, workloads)
+    ops, vo_ops = build_ops(torch, mp, workloads, variants=not args.no_variants)
     if args.only:
         # forward ops must still run once so their idx feeds the backward
         for op in ops:
@@ -331,6 +370,8 @@ def main():
         "per_op": per_op,
         "values_only_forward": [op_row(op) for op in vo_ops if op.kind == "fwd_values"],
         "ordered_backward": [op_row(op) for op in vo_ops if op.kind == "bwd_ordered"],
+        "int64_index_forward": [op_row(op) for op in vo_ops if op.kind == "fwd_i64"],
+        "padded": [op_row(op) for op in vo_ops if op.kind in ("fwd_pad", "bwd_pad")],
     }
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
