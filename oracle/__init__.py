@@ -70,6 +70,9 @@ class Oracle:
         lib.oracle_forward_ex.argtypes = ([_vp, _vp, _vp, ctypes.c_int] + [_i64] * 7
                                           + [_vp] * 4)
         lib.oracle_forward_ex.restype = None
+        lib.oracle_argmax_from_output.argtypes = ([_vp, _vp, _vp, ctypes.c_int] + [_i64] * 7
+                                                  + [_vp] * 4)
+        lib.oracle_argmax_from_output.restype = None
         lib.oracle_backward.argtypes = [_vp, _vp, _vp, ctypes.c_int] + [_i64] * 7 + [_vp] * 4
         lib.oracle_backward.restype = None
         lib.oracle_widen_array.argtypes = [_vp, ctypes.c_int, _i64, _vp]
@@ -139,6 +142,21 @@ class Oracle:
         self.lib.oracle_forward_ex(_ptr(x), _ptr(y), _ptr(idx), dtype, N * C,
                                    D, H, W, OD, OH, OW, *[_ptr(a) for a in arrs])
         return y, idx
+
+    def argmax_from_output(self, x: np.ndarray, y: np.ndarray, dtype: int, k=(0, 0, 0),
+                           s=(0, 0, 0), pad=(0, 0, 0), dil=(1, 1, 1)):
+        """The first tap of each window equal to y (the first NaN when y is
+        NaN), int64, -1 where none is; geometry as forward_ex, with the
+        output extents taken from y."""
+        self._check(x, dtype)
+        self._check(y, dtype)
+        N, C, D, H, W = x.shape
+        OD, OH, OW = y.shape[2:]
+        idx = np.empty(y.shape, np.int64)
+        arrs = [np.asarray(v, np.int64) for v in (k, s, pad, dil)]
+        self.lib.oracle_argmax_from_output(_ptr(x), _ptr(y), _ptr(idx), dtype, N * C,
+                                           D, H, W, OD, OH, OW, *[_ptr(a) for a in arrs])
+        return idx
 
     def backward(self, gy: np.ndarray, idx: np.ndarray, dtype: int,
                  in_shape: tuple[int, int, int, int, int], side: bool = True):

@@ -370,6 +370,67 @@ void oracle_forward_ex(const void *x, void *y, int64_t *idx, int dtype,
                 }
 }
 
+/* The argmax recovered from the forward's output, for a backward that is
+ * given x and y instead of idx (the teenygrad backward receives the
+ * forward's inputs and output, "Struct Maxpool3dForward", RuntimeOp).
+ * Reading taken: the first tap of window o in d, h, w scan order whose
+ * element equals y[o] -- equal as numbers, so -0 matches +0 -- or, when
+ * y[o] is a NaN, the first NaN tap; -1 when no tap matches.  Geometry as in
+ * oracle_forward_ex. */
+void oracle_argmax_from_output(const void *x, const void *y, int64_t *idx, int dtype,
+                               int64_t P, int64_t D, int64_t H, int64_t W,
+                               int64_t OD, int64_t OH, int64_t OW,
+                               const int64_t *k, const int64_t *s,
+                               const int64_t *pad, const int64_t *dil)
+{
+    const int64_t plane_in = D * H * W;
+    const int64_t plane_out = OD * OH * OW;
+    const int64_t X[3] = {D, H, W};
+    const int64_t O[3] = {OD, OH, OW};
+    int64_t nt[3];
+    for (int a = 0; a < 3; ++a) {
+        if (k[a] > 0) {
+            nt[a] = k[a];
+        } else {
+            nt[a] = 0;
+            for (int64_t o = 0; o < O[a]; ++o) {
+                int64_t lo, hi;
+                oracle_window(X[a], O[a], 0, 0, o, &lo, &hi);
+                if (hi - lo > nt[a])
+                    nt[a] = hi - lo;
+            }
+        }
+    }
+    for (int64_t p = 0; p < P; ++p)
+        for (int64_t od = 0; od < OD; ++od)
+            for (int64_t oh = 0; oh < OH; ++oh)
+                for (int64_t ow = 0; ow < OW; ++ow) {
+                    int64_t o = p * plane_out + (od * OH + oh) * OW + ow;
+                    double want = load_f64(y, dtype, o);
+                    int64_t found = -1;
+                    for (int64_t jd = 0; jd < nt[0] && found < 0; ++jd) {
+                        int64_t d = tap_position(D, OD, k[0], s[0], pad[0], dil[0], od, jd);
+                        if (d < 0)
+                            continue;
+                        for (int64_t jh = 0; jh < nt[1] && found < 0; ++jh) {
+                            int64_t h = tap_position(H, OH, k[1], s[1], pad[1], dil[1], oh, jh);
+                            if (h < 0)
+                                continue;
+                            for (int64_t jw = 0; jw < nt[2] && found < 0; ++jw) {
+                                int64_t w = tap_position(W, OW, k[2], s[2], pad[2], dil[2], ow, jw);
+                                if (w < 0)
+                                    continue;
+                                int64_t i = (d * H + h) * W + w;
+                                double v = load_f64(x, dtype, p * plane_in + i);
+                                if (isnan(want) ? isnan(v) : v == want)
+                                    found = i;
+                            }
+                        }
+                    }
+                    idx[o] = found;
+                }
+}
+
 /* ---------------------------------------------------------------------- */
 /* Backward                                                                */
 /* ---------------------------------------------------------------------- */

@@ -546,7 +546,50 @@ def pin_forward_ex_identities(orc):
         assert np.array_equal(y, by) and np.array_equal(idx, back)
 
 
+def pin_argmax_from_output(orc):
+    """The argmax recovered from (x, y) is the forward's own argmax when y
+    is the forward's output -- on tie-heavy, zero-signed and NaN data, for
+    plain, adaptive, padded and dilated windows -- and otherwise the first
+    element of the window (numpy's first-occurrence search over each
+    window's taps) equal to y, or -1."""
+    seed = 1501
+    cases = [((2, 2, 7, 8, 9), (2, 2, 2), (2, 2, 2), (0, 0, 0), (1, 1, 1), False),
+             ((1, 2, 9, 8, 7), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), True),
+             ((1, 1, 9, 10, 11), (3, 2, 3), (1, 2, 3), (1, 1, 0), (2, 3, 1), False),
+             ((1, 1, 2, 3, 4), (2, 2, 2), (1, 1, 1), (1, 1, 1), (3, 2, 2), False)]
+    for shape, k, s, pad, dil, cm in cases:
+        o3 = ex_out(orc, shape, k, s, pad, dil, cm)
+        for dt in (F32, F16, BF16):
+            for kind in ("ties", "zeros", "sparse_nan", "special"):
+                seed += 1
+                x = draw(shape, dt, kind, seed)
+                y, idx = orc.forward_ex(x, dt, o3, k, s, pad, dil)
+                got = orc.argmax_from_output(x, y, dt, k, s, pad, dil)
+                assert np.array_equal(got, idx), (shape, dt, kind)
+    # adaptive axes, and y that is not the forward's output
+    x = draw((2, 1, 7, 6, 5), F32, "ties", 1601)
+    y, idx = orc.forward(x, F32, (3, 4, 2))
+    assert np.array_equal(orc.argmax_from_output(x, y, F32), idx.astype(np.int64))
+    rng = np.random.default_rng(1602)
+    y2 = y.copy()
+    y2.reshape(-1)[::3] = rng.integers(-5, 6, y2.size)[::3].astype(np.float32)
+    got = orc.argmax_from_output(x, y2, F32)
+    wd, wh, ww = window_lists(x.shape, (3, 4, 2), (0, 0, 0), (0, 0, 0))
+    for p_ in range(2):
+        for i, (d0, d1) in enumerate(wd):
+            for j, (h0, h1) in enumerate(wh):
+                for l, (w0, w1) in enumerate(ww):
+                    blk = x[p_, 0, d0:d1, h0:h1, w0:w1]
+                    hit = np.flatnonzero(blk.reshape(-1) == y2[p_, 0, i, j, l])
+                    want = -1
+                    if hit.size:
+                        bd, rem = divmod(int(hit[0]), (h1 - h0) * (w1 - w0))
+                        bh, bw = divmod(rem, w1 - w0)
+                        want = ((d0 + bd) * 6 + h0 + bh) * 5 + w0 + bw
+                    assert got[p_, 0, i, j, l] == want
+
+
 ALL_PINS = [pin_widen, pin_round, pin_windows_adaptive, pin_windows_fixed,
             pin_forward_brute, pin_forward_torch, pin_forward_closed_forms,
             pin_backward, pin_backward_torch, pin_out_size_ex, pin_forward_ex_torch,
-            pin_forward_ex_identities]
+            pin_forward_ex_identities, pin_argmax_from_output]

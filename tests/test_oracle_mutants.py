@@ -68,6 +68,11 @@ MUTANTS = {
         "if (ceil_mode && n * s < room)", "if (n * s < room)"),
     "ex_ceil_keeps_window_in_padding": (
         "if (ceil_mode && (O - 1) * s >= X + pad)", "if (0)"),
+    "argmax_from_output_last_match": (
+        "for (int64_t jw = 0; jw < nt[2] && found < 0; ++jw) {",
+        "for (int64_t jw = 0; jw < nt[2]; ++jw) {"),
+    "argmax_from_output_nan_unmatched": (
+        "if (isnan(want) ? isnan(v) : v == want)", "if (v == want)"),
     "ex_empty_window_zero": (
         "((float *)y)[o] = -INFINITY;", "((float *)y)[o] = 0.0f;"),
 }
