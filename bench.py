@@ -23,9 +23,9 @@ pair around every op on its launch stream gives the per-op durations and
 the roofline of the dominant op (those events cost a few microseconds per
 op, so that pass is not the metric).  The values-only forward of each
 workload (no index written), the forward with int64 indices, the fixed
-workloads with padding k//2 (forward and backward) and the ordered backward
-(overlap=2) are timed the same way, apart from the step, and reported on
-their own.
+workloads with padding k//2 (forward and backward), the ordered backward
+(overlap=2) and the index-free backward (argmax recomputed from x and y)
+are timed the same way, apart from the step, and reported on their own.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (planes shard across GPUs with no communication, so more GPUs are not
@@ -112,6 +112,11 @@ def build_ops(torch, mp, workloads, variants=True):
             o = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
                 gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, overlap=2, out=gx))
             ord_ops.append(Op(wl, "bwd_ordered", o, bbytes, nin, "ordered backward"))
+            geo = dict(kernel=None) if wl.adaptive else dict(kernel=wl.kernel, stride=wl.stride)
+            rc = (lambda x=x, y=y, gy=gy, gx=gx, geo=geo: mp.mp3d_backward_recompute(
+                x, y, gy, out=gx, **geo))
+            ord_ops.append(Op(wl, "bwd_recompute", rc, nin * es + 2 * nout * es + nin * es, nin,
+                              "index-free backward (argmax recomputed from x and y)"))
         if not variants:
             continue
         # int64 indices (torch's index type): general forward kernel
@@ -370,6 +375,7 @@ def main():
         "per_op": per_op,
         "values_only_forward": [op_row(op) for op in vo_ops if op.kind == "fwd_values"],
         "ordered_backward": [op_row(op) for op in vo_ops if op.kind == "bwd_ordered"],
+        "index_free_backward": [op_row(op) for op in vo_ops if op.kind == "bwd_recompute"],
         "int64_index_forward": [op_row(op) for op in vo_ops if op.kind == "fwd_i64"],
         "padded": [op_row(op) for op in vo_ops if op.kind in ("fwd_pad", "bwd_pad")],
     }

@@ -16,6 +16,8 @@ PyTorch fallback: if the library is missing every call raises ImportError.
                                                      int32 or int64 idx
   mp3d_backward_ex(gy, idx, in_shape, kernel, stride, padding, dilation) -> gx
   mp3d_out_size_ex(X, k, s, pad, dilation, ceil_mode) -> int
+  mp3d_backward_recompute(x, y, gy, kernel, stride, padding, dilation) -> gx
+      index-free backward: the argmax recomputed from x and y
 
 x, y, gy and gx are float32, float16 or bfloat16; idx is int32 (int64 on
 request: index_dtype=torch.int64), flat within each D*H*W plane.
@@ -30,7 +32,8 @@ from . import _lib
 from ._lib import Mp3dError  # noqa: F401
 
 __all__ = ["mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
-           "mp3d_forward_ex", "mp3d_backward_ex", "mp3d_out_size_ex", "Mp3dError"]
+           "mp3d_forward_ex", "mp3d_backward_ex", "mp3d_out_size_ex",
+           "mp3d_backward_recompute", "Mp3dError"]
 
 _IDX = {torch.int32: _lib.MP3D_IDX_I32, torch.int64: _lib.MP3D_IDX_I64}
 
@@ -243,4 +246,41 @@ def mp3d_backward_ex(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel, stri
     _lib.check(lib.mp3d_backward_ex(gy.data_ptr(), idx.data_ptr(), out.data_ptr(), _code(gy),
                                     _IDX[idx.dtype], N, C, D, H, W, od, oh, ow, _arr3(k),
                                     _arr3(s), _arr3(pd), _arr3(dl), int(overlap), _stream(gy)))
+    return out
+
+
+def mp3d_backward_recompute(x: torch.Tensor, y: torch.Tensor, gy: torch.Tensor, kernel=None,
+                            stride=None, padding=0, dilation=1, overlap: int = -1,
+                            out: torch.Tensor | None = None):
+    """Index-free backward: gx of x's shape, with each window's argmax
+    recomputed from the forward's input ``x`` and output ``y`` (the first
+    element of the window equal to y, the first NaN when y is NaN).
+    ``kernel`` None means adaptive windows (y's extents); ``overlap`` as for
+    mp3d_backward (2: ordered)."""
+    lib = _lib.load()
+    for t, n in ((x, "x"), (y, "y"), (gy, "gy")):
+        _check_tensor(t, n)
+    if not (x.dtype == y.dtype == gy.dtype) or y.shape != gy.shape:
+        raise ValueError("x, y and gy must share a dtype, and y and gy a shape")
+    if x.shape[:2] != y.shape[:2] or x.device != y.device or x.device != gy.device:
+        raise ValueError("x, y and gy must share N, C and device")
+    N, C, D, H, W = x.shape
+    if kernel is None:
+        k = s = pd = (0, 0, 0)
+        dl = (1, 1, 1)
+    else:
+        k = _triple(kernel)
+        s = _triple(stride if stride is not None else kernel)
+        pd, dl = _triple(padding), _triple(dilation)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_tensor(out, "out")
+        if out.shape != x.shape or out.dtype != x.dtype:
+            raise ValueError("out must match x")
+    od, oh, ow = gy.shape[2:]
+    _lib.check(lib.mp3d_backward_recompute(x.data_ptr(), y.data_ptr(), gy.data_ptr(),
+                                           out.data_ptr(), _code(gy), N, C, D, H, W, od, oh, ow,
+                                           _arr3(k), _arr3(s), _arr3(pd), _arr3(dl),
+                                           int(overlap), _stream(gy)))
     return out

@@ -12,9 +12,11 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/mp3d.h"
 #include "dtype.hpp"
+#include "idxsrc.hpp"
 #include "kernels.hpp"
 
 namespace mp3d {
@@ -224,33 +226,59 @@ int forward(const void *x, void *y, void *idx, int idx_type, int dtype, const Ge
 
 enum class BwdPath { gather, accumulate, ordered };
 
-template <typename T, typename IT>
-int run_backward(const void *gy, const IT *idx, void *gx, const Geom &g, BwdPath path,
+template <typename S> struct is_array_src : std::false_type {};
+template <typename IT> struct is_array_src<IdxArray<IT>> : std::true_type {};
+
+// The gather and small-tensor kernels visit every window of each input
+// element, so they take only index arrays; a recomputed argmax (a window
+// scan per call) goes to the slab / box kernels, which ask once per window.
+template <typename T, typename Src>
+int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPath path,
                  hipStream_t s)
 {
-    if (path == BwdPath::gather) {
-        GatherPlan p{g, g.ax[0].X / g.ax[0].O, g.ax[1].X / g.ax[1].O, g.ax[2].X / g.ax[2].O};
-        if (log_enabled()) fprintf(stderr, "[mp3d] backward gather dtype=%d\n", T::code);
-        return hip_status(launch_backward_gather<T, IT>(gy, idx, gx, p, s), "backward gather launch");
-    }
-    SmallPlan sp;
-    if (small_enabled() && plan_small_backward(g, &sp)) {
-        if (log_enabled()) fprintf(stderr, "[mp3d] backward small dtype=%d inputs=%u\n", T::code, sp.total);
-        return hip_status(launch_backward_small<T, IT>(gy, idx, gx, sp, s), "backward small launch");
+    if constexpr (is_array_src<Src>::value) {
+        if (path == BwdPath::gather) {
+            GatherPlan p{g, g.ax[0].X / g.ax[0].O, g.ax[1].X / g.ax[1].O, g.ax[2].X / g.ax[2].O};
+            if (log_enabled()) fprintf(stderr, "[mp3d] backward gather dtype=%d\n", T::code);
+            return hip_status(launch_backward_gather<T, Src>(gy, src, gx, p, s),
+                              "backward gather launch");
+        }
+        SmallPlan sp;
+        if (small_enabled() && plan_small_backward(g, &sp)) {
+            if (log_enabled())
+                fprintf(stderr, "[mp3d] backward small dtype=%d inputs=%u\n", T::code, sp.total);
+            return hip_status(launch_backward_small<T, Src>(gy, src, gx, sp, s),
+                              "backward small launch");
+        }
     }
     const bool ordered = path == BwdPath::ordered;
     BwdPlan p;
     if (plan_backward(g, ordered, &p)) {
         if (log_enabled())
-            fprintf(stderr, "[mp3d] backward %s dtype=%d box=(%d,%d,%d) tiles=%lld lds=%u phases=%d\n",
-                    ordered ? "ordered slab" : "accumulate", T::code, p.td, p.th, p.tw,
-                    (long long)p.ntiles, p.lds_bytes, p.nphase);
-        return hip_status(launch_backward_tile<T, IT>(gy, idx, gx, p, s), "backward tile launch");
+            fprintf(stderr, "[mp3d] backward %s%s dtype=%d box=(%d,%d,%d) tiles=%lld lds=%u phases=%d\n",
+                    ordered ? "ordered slab" : "accumulate",
+                    is_array_src<Src>::value ? "" : " (argmax recomputed)", T::code, p.td, p.th,
+                    p.tw, (long long)p.ntiles, p.lds_bytes, p.nphase);
+        return hip_status(launch_backward_tile<T, Src>(gy, src, gx, p, s), "backward tile launch");
     }
     OrdPlan op;
     plan_ordered(g, &op);
     if (log_enabled()) fprintf(stderr, "[mp3d] backward ordered gather dtype=%d\n", T::code);
-    return hip_status(launch_backward_ordered<T, IT>(gy, idx, gx, op, s), "backward ordered launch");
+    return hip_status(launch_backward_ordered<T, Src>(gy, src, gx, op, s), "backward ordered launch");
+}
+
+template <typename T>
+IdxRecompute<T> recompute_src(const void *x, const void *y, const Geom &g)
+{
+    IdxRecompute<T> r;
+    r.x = (const typename T::raw *)x;
+    r.y = (const typename T::raw *)y;
+    r.g = g;
+    r.fast32 = g.planes * (int64_t)g.out_plane < ((int64_t)1 << 31);
+    r.plane_div = FastDiv((uint32_t)g.out_plane);
+    r.ow_div = FastDiv((uint32_t)g.ax[2].O);
+    r.oh_div = FastDiv((uint32_t)g.ax[1].O);
+    return r;
 }
 
 // Windows tile an axis -- each position in exactly one window, the one
@@ -289,8 +317,10 @@ int set_axes_ex(Geom *g, int64_t D, int64_t H, int64_t W, int32_t od, int32_t oh
     return MP3D_OK;
 }
 
-int backward(const void *gy, const void *idx, int idx_type, void *gx, int dtype, Geom &g,
-             int64_t N, int64_t C, int overlap, hipStream_t s)
+// Shared by the backward entry points.  idx_type < 0: no index array, the
+// argmax is recomputed from x and y (x, y then required).
+int backward(const void *gy, const void *idx, int idx_type, const void *x, const void *y,
+             void *gx, int dtype, Geom &g, int64_t N, int64_t C, int overlap, hipStream_t s)
 {
     int rc;
     if (overlap < -1 || overlap > 2)
@@ -300,20 +330,31 @@ int backward(const void *gy, const void *idx, int idx_type, void *gx, int dtype,
     if (overlap == 0 && !tiles)
         return fail(MP3D_ENOTDIV, "overlap=0 needs windows that tile every axis");
     if (g.planes == 0) return MP3D_OK;
-    if (!gy || !idx || !gx) return fail(MP3D_EINVAL, "null tensor pointer");
+    if (!gy || !gx || (idx_type >= 0 ? !idx : (!x || !y)))
+        return fail(MP3D_EINVAL, "null tensor pointer");
     // the gather is already the ordered sum (one window per input)
     const BwdPath path = overlap == 0 || ((overlap == -1 || overlap == 2) && tiles)
                              ? BwdPath::gather
                              : overlap == 2 ? BwdPath::ordered : BwdPath::accumulate;
+    if (idx_type < 0) {
+        // with windows that tile, every input has at most one contribution:
+        // the accumulate path gives the gather's (and the ordered) result
+        const BwdPath rp = path == BwdPath::ordered ? BwdPath::ordered : BwdPath::accumulate;
+        switch (dtype) {
+        case MP3D_F32: return run_backward<F32>(gy, recompute_src<F32>(x, y, g), gx, g, rp, s);
+        case MP3D_F16: return run_backward<F16>(gy, recompute_src<F16>(x, y, g), gx, g, rp, s);
+        default: return run_backward<BF16>(gy, recompute_src<BF16>(x, y, g), gx, g, rp, s);
+        }
+    }
     if (idx_type == MP3D_IDX_I64) {
-        const int64_t *ix = (const int64_t *)idx;
+        const IdxArray<int64_t> ix{(const int64_t *)idx};
         switch (dtype) {
         case MP3D_F32: return run_backward<F32>(gy, ix, gx, g, path, s);
         case MP3D_F16: return run_backward<F16>(gy, ix, gx, g, path, s);
         default: return run_backward<BF16>(gy, ix, gx, g, path, s);
         }
     }
-    const int32_t *ix = (const int32_t *)idx;
+    const IdxArray<int32_t> ix{(const int32_t *)idx};
     switch (dtype) {
     case MP3D_F32: return run_backward<F32>(gy, ix, gx, g, path, s);
     case MP3D_F16: return run_backward<F16>(gy, ix, gx, g, path, s);
@@ -449,7 +490,8 @@ int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype, int64
                             names[a], g.ax[a].O);
         }
     }
-    return backward(gy, idx, MP3D_IDX_I32, gx, dtype, g, N, C, overlap, (hipStream_t)stream);
+    return backward(gy, idx, MP3D_IDX_I32, nullptr, nullptr, gx, dtype, g, N, C, overlap,
+                    (hipStream_t)stream);
 }
 
 int mp3d_backward_ex(const void *gy, const void *idx, void *gx, int dtype, int idx_type,
@@ -463,7 +505,21 @@ int mp3d_backward_ex(const void *gy, const void *idx, void *gx, int dtype, int i
         return fail(MP3D_EDTYPE, "idx_type %d is not MP3D_IDX_I32 or MP3D_IDX_I64", idx_type);
     Geom g;
     if ((rc = set_axes_ex(&g, D, H, W, od, oh, ow, kernel, stride, pad, dilation))) return rc;
-    return backward(gy, idx, idx_type, gx, dtype, g, N, C, overlap, (hipStream_t)stream);
+    return backward(gy, idx, idx_type, nullptr, nullptr, gx, dtype, g, N, C, overlap,
+                    (hipStream_t)stream);
+}
+
+int mp3d_backward_recompute(const void *x, const void *y, const void *gy, void *gx, int dtype,
+                            int64_t N, int64_t C, int64_t D, int64_t H, int64_t W, int32_t od,
+                            int32_t oh, int32_t ow, const int32_t *kernel, const int32_t *stride,
+                            const int32_t *pad, const int32_t *dilation, int overlap,
+                            void *stream)
+{
+    int rc = check_common(dtype, N, C, D, H, W);
+    if (rc) return rc;
+    Geom g;
+    if ((rc = set_axes_ex(&g, D, H, W, od, oh, ow, kernel, stride, pad, dilation))) return rc;
+    return backward(gy, nullptr, -1, x, y, gx, dtype, g, N, C, overlap, (hipStream_t)stream);
 }
 
 

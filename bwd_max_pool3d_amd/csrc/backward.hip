@@ -23,6 +23,7 @@
 #include <climits>
 
 #include "dtype.hpp"
+#include "idxsrc.hpp"
 #include "kernels.hpp"
 
 namespace mp3d {
@@ -106,9 +107,9 @@ __device__ __forceinline__ void store_span(typename T::raw *dst, const float *a,
 // windows as their flat output numbers do, so each element's fold is the
 // ascending-order sum, and within a phase every input has at most one
 // window, so plain LDS read-modify-writes suffice.
-template <typename T, typename IT, int NT, bool ORD, int kRound>
+template <typename T, typename Src, int NT, bool ORD, int kRound>
 __global__ void __launch_bounds__(NT)
-bwd_slab_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
+bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
                 typename T::raw *__restrict__ gx, BwdPlan p)
 {
     using R = typename T::raw;
@@ -146,7 +147,7 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ i
             const int32_t e = (round * kRound + k) * NT + tid;
             ri[k] = -1;
             if (e < nw) {
-                ri[k] = ld_idx(idx, wbase + e);
+                ri[k] = src(wbase + e);
                 rg[k] = gy[wbase + e];
             }
         }
@@ -208,9 +209,9 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ i
 }
 
 // General boxes [d0,d1) x [h0,h1) x [w0,w1) (a slice does not fit in LDS).
-template <typename T, typename IT>
+template <typename T, typename Src>
 __global__ void __launch_bounds__(kBlock)
-bwd_box_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
+bwd_box_kernel(const typename T::raw *__restrict__ gy, const Src src,
                typename T::raw *__restrict__ gx, BwdPlan p)
 {
     using R = typename T::raw;
@@ -238,7 +239,7 @@ bwd_box_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ id
         for (int32_t e = tid; e < cd * ch * cw; e += kBlock) {
             const int32_t owl = e % cw, r = e / cw, ohl = r % ch, odl = r / ch;
             const int64_t o = obase + ((od0 + odl) * B.O + oh0 + ohl) * Cw.O + ow0 + owl;
-            const int32_t i = ld_idx(idx, o);
+            const int32_t i = src(o);
             if ((uint32_t)i < (uint32_t)p.g.in_plane) {
                 const int32_t d = i / (H * W), rem = i - d * H * W;
                 const int32_t h = rem / W, w = rem - h * W;
@@ -256,9 +257,9 @@ bwd_box_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ id
     }
 }
 
-template <typename T, typename IT>
+template <typename T, typename Src>
 __global__ void __launch_bounds__(kBlock)
-bwd_gather_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
+bwd_gather_kernel(const typename T::raw *__restrict__ gy, const Src src,
                   typename T::raw *__restrict__ gx, GatherPlan p)
 {
     const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X;
@@ -272,15 +273,15 @@ bwd_gather_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__
         const int64_t o = plane * (int64_t)p.g.out_plane +
                           ((d / p.qd) * OH + h / p.qh) * OW + w / p.qw;
         typename T::raw out = T::narrow(0.0f);
-        if (ld_idx(idx, o) == i) out = T::narrow(0.0f + T::widen(gy[o]));
+        if (src(o) == i) out = T::narrow(0.0f + T::widen(gy[o]));
         gx[e] = out;
     }
 }
 
 }  // namespace
 
-template <typename T, typename IT>
-hipError_t launch_backward_tile(const void *gy, const IT *idx, void *gx, const BwdPlan &p,
+template <typename T, typename Src>
+hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const BwdPlan &p,
                                 hipStream_t s)
 {
     using R = typename T::raw;
@@ -290,42 +291,45 @@ hipError_t launch_backward_tile(const void *gy, const IT *idx, void *gx, const B
         // (the surplus blocks exit at once)
         if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
         if (p.nphase)
-            hipLaunchKernelGGL((bwd_slab_kernel<T, IT, kOrdThreads, true, kOrdRound>), dim3((uint32_t)grid),
-                               dim3(kOrdThreads), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
+            hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kOrdThreads, true, kOrdRound>), dim3((uint32_t)grid),
+                               dim3(kOrdThreads), p.lds_bytes, s, (const R *)gy, src, (R *)gx, p);
         else
-            hipLaunchKernelGGL((bwd_slab_kernel<T, IT, kSlabBlock, false, kBwdRound>), dim3((uint32_t)grid),
-                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, idx, (R *)gx, p);
+            hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kSlabBlock, false, kBwdRound>), dim3((uint32_t)grid),
+                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, src, (R *)gx, p);
     } else {
-        hipLaunchKernelGGL((bwd_box_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
-                           (const R *)gy, idx, (R *)gx, p);
+        hipLaunchKernelGGL((bwd_box_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
+                           (const R *)gy, src, (R *)gx, p);
     }
     return hipGetLastError();
 }
 
-template <typename T, typename IT>
-hipError_t launch_backward_gather(const void *gy, const IT *idx, void *gx, const GatherPlan &p,
+template <typename T, typename Src>
+hipError_t launch_backward_gather(const void *gy, const Src &src, void *gx, const GatherPlan &p,
                                   hipStream_t s)
 {
     using R = typename T::raw;
     const int64_t total = p.g.planes * (int64_t)p.g.in_plane;
     int64_t grid = (total + kBlock - 1) / kBlock;
     if (grid > (1 << 20)) grid = 1 << 20;
-    hipLaunchKernelGGL((bwd_gather_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
-                       (const R *)gy, idx, (R *)gx, p);
+    hipLaunchKernelGGL((bwd_gather_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
+                       (const R *)gy, src, (R *)gx, p);
     return hipGetLastError();
 }
 
-template hipError_t launch_backward_tile<F32, int32_t>(const void *, const int32_t *, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_tile<F32, int64_t>(const void *, const int64_t *, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_tile<F16, int32_t>(const void *, const int32_t *, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_tile<F16, int64_t>(const void *, const int64_t *, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_tile<BF16, int32_t>(const void *, const int32_t *, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_tile<BF16, int64_t>(const void *, const int64_t *, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_gather<F32, int32_t>(const void *, const int32_t *, void *, const GatherPlan &, hipStream_t);
-template hipError_t launch_backward_gather<F32, int64_t>(const void *, const int64_t *, void *, const GatherPlan &, hipStream_t);
-template hipError_t launch_backward_gather<F16, int32_t>(const void *, const int32_t *, void *, const GatherPlan &, hipStream_t);
-template hipError_t launch_backward_gather<F16, int64_t>(const void *, const int64_t *, void *, const GatherPlan &, hipStream_t);
-template hipError_t launch_backward_gather<BF16, int32_t>(const void *, const int32_t *, void *, const GatherPlan &, hipStream_t);
-template hipError_t launch_backward_gather<BF16, int64_t>(const void *, const int64_t *, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F32, IdxRecompute<F32>>(const void *, const IdxRecompute<F32> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F16, IdxRecompute<F16>>(const void *, const IdxRecompute<F16> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<BF16, IdxRecompute<BF16>>(const void *, const IdxRecompute<BF16> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const GatherPlan &, hipStream_t);
 
 }  // namespace mp3d

@@ -19,30 +19,6 @@ namespace mp3d {
 
 namespace {
 
-// Taps of window o on one axis: tap j (0 <= j < n) sits at b + j*t; the taps
-// inside [0, X) are j0..j1 (j0 > j1: none).
-struct Taps {
-    int32_t b, t, n, j0, j1;
-};
-
-__device__ __forceinline__ Taps taps(const Axis &a, int32_t o)
-{
-    Taps r;
-    if (a.k) {
-        r.b = o * a.s - a.pad;
-        r.t = a.dil;
-        r.n = a.k;
-    } else {
-        r.b = a.start(o);
-        r.t = 1;
-        r.n = a.end(o) - r.b;
-    }
-    r.j0 = r.b >= 0 ? 0 : (r.t == 1 ? -r.b : (-r.b + r.t - 1) / r.t);
-    const int32_t room = a.X - 1 - r.b;                // last position minus the first tap's
-    r.j1 = room < 0 ? -1 : min(r.n - 1, r.t == 1 ? room : room / r.t);
-    return r;
-}
-
 __device__ __forceinline__ bool better(float v, float best)
 {
     return v > best || (v != v && best == best);     // strictly greater, or the first NaN
@@ -78,7 +54,7 @@ fwd_ex_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict
         const int32_t ow = (int32_t)(o - r * (uint32_t)OW);
         const uint32_t od = p.oh_div.div(r);
         const int32_t oh = (int32_t)(r - od * (uint32_t)OH);
-        const Taps td = taps(A, (int32_t)od), th = taps(B, oh), tw = taps(Cw, ow);
+        const Taps td = window_taps(A, (int32_t)od), th = window_taps(B, oh), tw = window_taps(Cw, ow);
         const R *xp = x + plane * (int64_t)p.g.in_plane;
         const bool empty = td.j0 > td.j1 || th.j0 > th.j1 || tw.j0 > tw.j1;
         int32_t pbest = -1;

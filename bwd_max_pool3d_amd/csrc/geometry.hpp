@@ -102,6 +102,31 @@ struct Axis {
     }
 };
 
+// Taps of window o on one axis: tap j (0 <= j < n) sits at b + j*t; the
+// taps inside [0, X) are j0..j1 (j0 > j1: none).
+struct Taps {
+    int32_t b, t, n, j0, j1;
+};
+
+__host__ __device__ inline Taps window_taps(const Axis &a, int32_t o)
+{
+    Taps r;
+    if (a.k) {
+        r.b = o * a.s - a.pad;
+        r.t = a.dil;
+        r.n = a.k;
+    } else {
+        r.b = a.start(o);
+        r.t = 1;
+        r.n = a.end(o) - r.b;
+    }
+    r.j0 = r.b >= 0 ? 0 : (r.t == 1 ? -r.b : (-r.b + r.t - 1) / r.t);
+    const int32_t room = a.X - 1 - r.b;                // last position minus the first tap's
+    const int32_t last = r.t == 1 ? room : room / r.t;
+    r.j1 = room < 0 ? -1 : (last < r.n - 1 ? last : r.n - 1);
+    return r;
+}
+
 // Splits a linear tile number into (plane, i0, i1, i2) for tiles counted
 // plane-major with n0 x n1 x n2 tiles per plane (i2 fastest).
 struct TileSplit {

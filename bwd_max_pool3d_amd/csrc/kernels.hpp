@@ -175,20 +175,20 @@ hipError_t launch_forward_direct(const void *x, void *y, int32_t *idx,
                                  const Geom &g, hipStream_t s);
 template <typename T, typename IT>
 hipError_t launch_forward_ex(const void *x, void *y, IT *idx, const ExPlan &p, hipStream_t s);
-template <typename T, typename IT>
-hipError_t launch_backward_tile(const void *gy, const IT *idx, void *gx, const BwdPlan &p,
+template <typename T, typename Src>
+hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const BwdPlan &p,
                                 hipStream_t s);
 template <typename T>
 hipError_t launch_forward_small(const void *x, void *y, int32_t *idx,
                                 const SmallPlan &p, hipStream_t s);
-template <typename T, typename IT>
-hipError_t launch_backward_small(const void *gy, const IT *idx, void *gx, const SmallPlan &p,
+template <typename T, typename Src>
+hipError_t launch_backward_small(const void *gy, const Src &src, void *gx, const SmallPlan &p,
                                  hipStream_t s);
-template <typename T, typename IT>
-hipError_t launch_backward_gather(const void *gy, const IT *idx, void *gx, const GatherPlan &p,
+template <typename T, typename Src>
+hipError_t launch_backward_gather(const void *gy, const Src &src, void *gx, const GatherPlan &p,
                                   hipStream_t s);
-template <typename T, typename IT>
-hipError_t launch_backward_ordered(const void *gy, const IT *idx, void *gx, const OrdPlan &p,
+template <typename T, typename Src>
+hipError_t launch_backward_ordered(const void *gy, const Src &src, void *gx, const OrdPlan &p,
                                    hipStream_t s);
 
 }  // namespace mp3d

@@ -12,6 +12,7 @@
 #include <algorithm>
 
 #include "dtype.hpp"
+#include "idxsrc.hpp"
 #include "kernels.hpp"
 
 namespace mp3d {
@@ -84,9 +85,9 @@ fwd_small_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
 // The (at most 8) windows are visited in ascending output order, so the
 // binary32 sum from +0 is the same fold the ordered definition gives, bit
 // for bit, and it is rounded once.
-template <typename T, typename IT>
+template <typename T, typename Src>
 __global__ void __launch_bounds__(kBlock)
-bwd_small_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
+bwd_small_kernel(const typename T::raw *__restrict__ gy, const Src src,
                  typename T::raw *__restrict__ gx, SmallPlan p)
 {
     using R = typename T::raw;
@@ -124,7 +125,7 @@ bwd_small_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ 
             c[a] = min(max(q, 0), O[a] - 1);          // in range even when unused
         }
         const int64_t o = obase + ((int64_t)c[0] * OH + c[1]) * OW + c[2];
-        ri[k] = ld_idx(idx, o);
+        ri[k] = src(o);
         rg[k] = gy[o];
         on[k] = valid;
     }
@@ -139,9 +140,9 @@ bwd_small_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ 
 // window containing it, in ascending output order, and keeps the elements
 // whose argmax it is: the ordered binary32 sum from +0, rounded once.  The
 // general fallback of the ordered backward; loads follow one another.
-template <typename T, typename IT>
+template <typename T, typename Src>
 __global__ void __launch_bounds__(kBlock)
-bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict__ idx,
+bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const Src src,
                    typename T::raw *__restrict__ gx, OrdPlan p)
 {
     const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
@@ -163,7 +164,7 @@ bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict_
             for (int32_t oh = h0; oh <= h1; ++oh)
                 for (int32_t ow = w0; ow <= w1; ++ow) {
                     const int64_t o = obase + ((int64_t)od * OH + oh) * OW + ow;
-                    const int32_t v = ld_idx(idx, o);
+                    const int32_t v = src(o);
                     const float g = T::widen(gy[o]);
                     if (v == i) acc = acc + g;
                 }
@@ -173,14 +174,14 @@ bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const IT *__restrict_
 
 }  // namespace
 
-template <typename T, typename IT>
-hipError_t launch_backward_ordered(const void *gy, const IT *idx, void *gx, const OrdPlan &p,
+template <typename T, typename Src>
+hipError_t launch_backward_ordered(const void *gy, const Src &src, void *gx, const OrdPlan &p,
                                    hipStream_t s)
 {
     using R = typename T::raw;
     const int64_t grid = std::min<int64_t>((p.total + kBlock - 1) / kBlock, (int64_t)1 << 20);
-    hipLaunchKernelGGL((bwd_ordered_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
-                       (const R *)gy, idx, (R *)gx, p);
+    hipLaunchKernelGGL((bwd_ordered_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
+                       (const R *)gy, src, (R *)gx, p);
     return hipGetLastError();
 }
 
@@ -194,13 +195,13 @@ hipError_t launch_forward_small(const void *x, void *y, int32_t *idx, const Smal
     return hipGetLastError();
 }
 
-template <typename T, typename IT>
-hipError_t launch_backward_small(const void *gy, const IT *idx, void *gx, const SmallPlan &p,
+template <typename T, typename Src>
+hipError_t launch_backward_small(const void *gy, const Src &src, void *gx, const SmallPlan &p,
                                  hipStream_t s)
 {
     using R = typename T::raw;
-    hipLaunchKernelGGL((bwd_small_kernel<T, IT>), dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
-                       s, (const R *)gy, idx, (R *)gx, p);
+    hipLaunchKernelGGL((bwd_small_kernel<T, Src>), dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
+                       s, (const R *)gy, src, (R *)gx, p);
     return hipGetLastError();
 }
 
@@ -208,17 +209,21 @@ template hipError_t launch_forward_small<F32>(const void *, void *, int32_t *, c
 template hipError_t launch_forward_small<F16>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
 template hipError_t launch_forward_small<BF16>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
 
-template hipError_t launch_backward_small<F32, int32_t>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_small<F32, int64_t>(const void *, const int64_t *, void *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_small<F16, int32_t>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_small<F16, int64_t>(const void *, const int64_t *, void *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_small<BF16, int32_t>(const void *, const int32_t *, void *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_small<BF16, int64_t>(const void *, const int64_t *, void *, const SmallPlan &, hipStream_t);
-template hipError_t launch_backward_ordered<F32, int32_t>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
-template hipError_t launch_backward_ordered<F32, int64_t>(const void *, const int64_t *, void *, const OrdPlan &, hipStream_t);
-template hipError_t launch_backward_ordered<F16, int32_t>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
-template hipError_t launch_backward_ordered<F16, int64_t>(const void *, const int64_t *, void *, const OrdPlan &, hipStream_t);
-template hipError_t launch_backward_ordered<BF16, int32_t>(const void *, const int32_t *, void *, const OrdPlan &, hipStream_t);
-template hipError_t launch_backward_ordered<BF16, int64_t>(const void *, const int64_t *, void *, const OrdPlan &, hipStream_t);
+
+template hipError_t launch_backward_ordered<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F32, IdxRecompute<F32>>(const void *, const IdxRecompute<F32> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_small<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_small<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F16, IdxRecompute<F16>>(const void *, const IdxRecompute<F16> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_small<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_small<F16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<BF16, IdxRecompute<BF16>>(const void *, const IdxRecompute<BF16> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_small<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_small<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
 
 }  // namespace mp3d

@@ -153,6 +153,27 @@ int mp3d_out_size(int64_t X, int32_t k, int32_t s, int64_t *out);
  * 2*pad <= k (as torch requires), and the span must fit the padded axis:
  * X + 2*pad >= (k-1)*dil + 1.  Otherwise MP3D_EINVAL. */
 
+/* Index-free backward: the same sums as mp3d_backward_ex, with each
+ * window's argmax recomputed from the forward's input x and output y
+ * instead of read from an index array, so that a caller can run the
+ * values-only forward (idx = NULL) and keep no index at all (the teenygrad
+ * kernel ABI passes no index buffer, "Struct Maxpool3dForward", Kernel
+ * trait; its backward receives the forward's inputs and output,
+ * RuntimeOp).  The argmax of window o is its first tap, in d, h, w scan
+ * order, whose element equals y[o] (the first NaN when y[o] is NaN): the
+ * forward's own argmax whenever y is what the forward wrote.  A window with
+ * no such tap contributes nothing.  x: (N, C, D, H, W); y and gy:
+ * (N, C, od, oh, ow); geometry arrays and overlap as for mp3d_backward_ex
+ * (overlap 0 and -1 take the accumulate kernels, which give the gather's
+ * result on tiling windows).  Reads x once per window that reaches a slab
+ * of gx: slower than the index path, and no index traffic. */
+int mp3d_backward_recompute(const void *x, const void *y, const void *gy, void *gx, int dtype,
+                            int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                            int32_t od, int32_t oh, int32_t ow,
+                            const int32_t *kernel, const int32_t *stride,
+                            const int32_t *pad, const int32_t *dilation,
+                            int overlap, void *stream);
+
 /* Output extent into *out.  ceil_mode 0: (X + 2*pad - span)/s + 1, rounded
  * down.  ceil_mode 1: rounded up, less one if that last window would start
  * at or beyond X + pad (so every window starts inside the input or the
