@@ -275,6 +275,10 @@ IdxRecompute<T> recompute_src(const void *x, const void *y, const Geom &g)
     r.y = (const typename T::raw *)y;
     r.g = g;
     r.fast32 = g.planes * (int64_t)g.out_plane < ((int64_t)1 << 31);
+    ExPlan ep;                                   // its tap-count test
+    plan_ex(g, &ep);
+    r.km3 = ep.km == 3;
+    r.w8 = max_taps(g.ax[2]) <= 8;
     r.plane_div = FastDiv((uint32_t)g.out_plane);
     r.ow_div = FastDiv((uint32_t)g.ax[2].O);
     r.oh_div = FastDiv((uint32_t)g.ax[1].O);

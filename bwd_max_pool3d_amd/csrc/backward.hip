@@ -294,7 +294,7 @@ hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const 
             hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kOrdThreads, true, kOrdRound>), dim3((uint32_t)grid),
                                dim3(kOrdThreads), p.lds_bytes, s, (const R *)gy, src, (R *)gx, p);
         else
-            hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kSlabBlock, false, kBwdRound>), dim3((uint32_t)grid),
+            hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kSlabBlock, false, Src::kSlots>), dim3((uint32_t)grid),
                                dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, src, (R *)gx, p);
     } else {
         hipLaunchKernelGGL((bwd_box_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,

@@ -160,6 +160,7 @@ bool plan_small_forward(const Geom &g, SmallPlan *p);
 bool plan_small_backward(const Geom &g, SmallPlan *p);
 void plan_ordered(const Geom &g, OrdPlan *p);
 void plan_ex(const Geom &g, ExPlan *p);
+int64_t max_taps(const Axis &a);         // most taps of one window on the axis
 
 template <typename T>
 hipError_t launch_forward_tile(const void *x, void *y, int32_t *idx,

@@ -334,15 +334,18 @@ bool plan_backward(const Geom &g, bool ordered, BwdPlan *p)
     return true;
 }
 
+int64_t max_taps(const Axis &a)
+{
+    return a.k ? (int64_t)a.k : axis_widest(a);
+}
+
 void plan_ex(const Geom &g, ExPlan *p)
 {
     p->g = g;
     p->total = g.planes * (int64_t)g.out_plane;
     p->km = 3;
-    for (int a = 0; a < 3; ++a) {
-        const Axis &ax = g.ax[a];
-        if ((ax.k ? (int64_t)ax.k : axis_widest(ax)) > 3) p->km = 0;
-    }
+    for (int a = 0; a < 3; ++a)
+        if (max_taps(g.ax[a]) > 3) p->km = 0;
     p->fast32 = p->total < ((int64_t)1 << 31);
     p->plane_div = FastDiv((uint32_t)g.out_plane);
     p->ow_div = FastDiv((uint32_t)g.ax[2].O);
