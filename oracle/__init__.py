@@ -8,9 +8,10 @@ the benchmark's CPU-baseline leg may import this package.  The product path
 two share no code: the oracle is plain C in ``mp3d_oracle.c`` (compiled with
 gcc) driven through ctypes with numpy arrays.
 
-Storage convention: float32 data are numpy float32 arrays; float16 and
-bfloat16 data are numpy uint16 arrays holding the raw bit patterns.
-dtype codes: 0 = float32, 1 = float16, 2 = bfloat16.
+Storage convention: float32 and float64 data are numpy float32 / float64
+arrays; float16 and bfloat16 data are numpy uint16 arrays holding the raw
+bit patterns.  dtype codes: 0 = float32, 1 = float16, 2 = bfloat16,
+3 = float64.
 
 The definitions followed (page titles and sections) are stated at the top
 of ``mp3d_oracle.c``.
@@ -23,7 +24,7 @@ import subprocess
 
 import numpy as np
 
-F32, F16, BF16 = 0, 1, 2
+F32, F16, BF16, F64 = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "mp3d_oracle.c")
@@ -109,7 +110,7 @@ class Oracle:
     # -- pooling -------------------------------------------------------
     @staticmethod
     def _check(x: np.ndarray, dtype: int):
-        want = np.float32 if dtype == F32 else np.uint16
+        want = {F32: np.float32, F64: np.float64}.get(dtype, np.uint16)
         if x.dtype != want or not x.flags.c_contiguous:
             raise TypeError("oracle expects contiguous %s storage" % np.dtype(want))
 

@@ -50,7 +50,7 @@
 #include <stdint.h>
 #include <string.h>
 
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_F64 = 3 };
 
 /* ---------------------------------------------------------------------- */
 /* 16-bit formats, from the IEEE 754 binary16 and the bfloat16 layouts.    */
@@ -154,6 +154,8 @@ uint16_t oracle_f32_to_bf16(float f)
  * exactly to binary64. */
 static double load_f64(const void *buf, int dtype, int64_t i)
 {
+    if (dtype == ORACLE_F64)
+        return ((const double *)buf)[i];
     if (dtype == ORACLE_F32)
         return (double)((const float *)buf)[i];
     if (dtype == ORACLE_F16)
@@ -163,7 +165,7 @@ static double load_f64(const void *buf, int dtype, int64_t i)
 
 static int dtype_size(int dtype)
 {
-    return dtype == ORACLE_F32 ? 4 : 2;
+    return dtype == ORACLE_F64 ? 8 : dtype == ORACLE_F32 ? 4 : 2;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -361,6 +363,8 @@ void oracle_forward_ex(const void *x, void *y, int64_t *idx, int dtype,
                     if (best_i >= 0) {
                         memcpy((char *)y + o * es,
                                (const char *)x + (p * plane_in + best_i) * es, es);
+                    } else if (dtype == ORACLE_F64) {
+                        ((double *)y)[o] = -INFINITY;
                     } else if (dtype == ORACLE_F32) {
                         ((float *)y)[o] = -INFINITY;
                     } else {
@@ -439,8 +443,11 @@ void oracle_argmax_from_output(const void *x, const void *y, int64_t *idx, int d
  * except idx (int32).  acc32 is a caller-provided binary32 scratch of
  * P*D*H*W that holds the accumulator before rounding on return.  ref64,
  * abs64 (binary64) and count (int32) are optional per-input side outputs
- * (NULL to skip): the exact sum, the sum of magnitudes and the number of
- * contributions. */
+ * (NULL to skip): the binary64 sum, the sum of magnitudes and the number of
+ * contributions.  float64 gradients (PR #308 page, Testing, leaves float64
+ * to a generic path; reading taken: the same ordered sum, in binary64) are
+ * added in binary64 from +0 in ascending output order straight into gx;
+ * acc32 then holds their binary32 roundings. */
 void oracle_backward(const void *gy, const int32_t *idx, void *gx, int dtype,
                      int64_t P, int64_t D, int64_t H, int64_t W,
                      int64_t OD, int64_t OH, int64_t OW,
@@ -452,6 +459,7 @@ void oracle_backward(const void *gy, const int32_t *idx, void *gx, int dtype,
     const int64_t n = P * plane_in;
     for (int64_t t = 0; t < n; ++t) {
         acc32[t] = 0.0f;
+        if (dtype == ORACLE_F64) ((double *)gx)[t] = 0.0;
         if (ref64) ref64[t] = 0.0;
         if (abs64) abs64[t] = 0.0;
         if (count) count[t] = 0;
@@ -462,17 +470,24 @@ void oracle_backward(const void *gy, const int32_t *idx, void *gx, int dtype,
             if (i < 0 || i >= plane_in)
                 continue;
             double gv = load_f64(gy, dtype, p * plane_out + o);
-            float g = (float)gv;                   /* exact: gy is <= 32 bit */
             int64_t t = p * plane_in + i;
-            float sum = acc32[t] + g;              /* one binary32 add, RNE */
-            acc32[t] = sum;
+            if (dtype == ORACLE_F64) {
+                double *g64 = (double *)gx;
+                g64[t] = g64[t] + gv;              /* one binary64 add, RNE */
+            } else {
+                float g = (float)gv;               /* exact: gy is <= 32 bit */
+                float sum = acc32[t] + g;          /* one binary32 add, RNE */
+                acc32[t] = sum;
+            }
             if (ref64) ref64[t] += gv;
             if (abs64) abs64[t] += fabs(gv);
             if (count) count[t] += 1;
         }
     }
     for (int64_t t = 0; t < n; ++t) {
-        if (dtype == ORACLE_F32)
+        if (dtype == ORACLE_F64)
+            acc32[t] = (float)((double *)gx)[t];
+        else if (dtype == ORACLE_F32)
             ((float *)gx)[t] = acc32[t];
         else if (dtype == ORACLE_F16)
             ((uint16_t *)gx)[t] = oracle_f32_to_f16(acc32[t]);

@@ -35,8 +35,8 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
-F32, F16, BF16 = 0, 1, 2
-TORCH_DT = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
+F32, F16, BF16, F64 = 0, 1, 2, 3
+TORCH_DT = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, F64: torch.float64}
 
 
 # ---------------------------------------------------------------------------
@@ -46,7 +46,7 @@ TORCH_DT = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
 def to_storage(t: torch.Tensor) -> np.ndarray:
     """CPU tensor -> the oracle's storage array (float32 or uint16 bits)."""
     t = t.contiguous()
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.float64):
         return t.numpy().copy()
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
@@ -54,6 +54,8 @@ def to_storage(t: torch.Tensor) -> np.ndarray:
 def from_storage(a: np.ndarray, dtype: int) -> torch.Tensor:
     if dtype == F32:
         return torch.from_numpy(np.ascontiguousarray(a, np.float32))
+    if dtype == F64:
+        return torch.from_numpy(np.ascontiguousarray(a, np.float64))
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(TORCH_DT[dtype])
 
 
@@ -63,10 +65,12 @@ def widen_torch(a: np.ndarray, dtype: int) -> np.ndarray:
 
 
 def draw(shape, dtype: int, kind: str, seed: int) -> np.ndarray:
+    """Seeded test data; float64 draws keep full binary64 precision."""
     g = torch.Generator().manual_seed(seed)
     n = int(np.prod(shape))
+    fd = torch.float64 if dtype == F64 else torch.float32
     if kind == "normal":
-        t = torch.randn(n, generator=g)
+        t = torch.randn(n, generator=g, dtype=fd)
     elif kind == "ties":
         t = torch.randint(-3, 4, (n,), generator=g).float()
     elif kind == "distinct":
@@ -77,13 +81,13 @@ def draw(shape, dtype: int, kind: str, seed: int) -> np.ndarray:
         t = torch.tensor([-2.0, -1.0, -0.0, 0.0])[torch.randint(0, 4, (n,), generator=g)]
     elif kind == "sparse_nan":
         # few NaN and infinities: most windows hold none
-        t = torch.randn(n, generator=g)
+        t = torch.randn(n, generator=g, dtype=fd)
         u = torch.rand(n, generator=g)
         t[u < 2e-3] = float("inf")
         t[(u >= 2e-3) & (u < 4e-3)] = -float("inf")
         t[u > 1 - 5e-4] = float("nan")
     elif kind == "special":
-        t = torch.randn(n, generator=g)
+        t = torch.randn(n, generator=g, dtype=fd)
         pick = torch.randint(0, 12, (n,), generator=g)
         t[pick == 0] = float("nan")
         t[pick == 1] = float("inf")
@@ -268,7 +272,7 @@ def pin_forward_brute(orc):
     seed = 11
     for shape, out, k, s in FORWARD_CASES:
         o3 = _out_of(orc, shape, out, k, s)
-        for dt in (F32, F16, BF16):
+        for dt in (F32, F16, BF16, F64):
             for kind in ("normal", "ties", "special"):
                 seed += 1
                 x = draw(shape, dt, kind, seed)
@@ -286,11 +290,12 @@ def pin_forward_torch(orc):
         if any(k) and not all(k):
             continue  # torch has no mixed fixed/adaptive form
         o3 = _out_of(orc, shape, out, k, s)
-        for dt in (F32, F16, BF16):
+        for dt in (F32, F16, BF16, F64):
             for kind in ("distinct", "ties"):
                 seed += 1
                 n = int(np.prod(shape))
-                if kind == "distinct" and n > {F32: 1 << 24, F16: 4096, BF16: 512}[dt]:
+                if kind == "distinct" and n > {F32: 1 << 24, F16: 4096, BF16: 512,
+                                               F64: 1 << 53}[dt]:
                     continue  # the format cannot hold that many distinct integers
                 x = draw(shape, dt, kind, seed)
                 y, idx = orc.forward(x, dt, o3, k, s)
@@ -365,7 +370,7 @@ def pin_backward(orc):
         o3 = _out_of(orc, shape, out, k, s)
         N, C, D, H, W = shape
         P, n = N * C, D * H * W
-        for dt in (F32, F16, BF16):
+        for dt in (F32, F16, BF16, F64):
             for kind in ("ties", "normal"):
                 seed += 1
                 x = draw(shape, dt, kind, seed)
@@ -383,6 +388,11 @@ def pin_backward(orc):
                     ab = np.zeros(n)
                     np.add.at(ab, ii[p], np.abs(g64[p]))
                     assert np.array_equal(r["abs64"].reshape(P, -1)[p], ab)
+                    if dt == F64:
+                        # float64: the binary64 fold in ascending order is gx itself
+                        got = r["gx"].reshape(P, -1)[p]
+                        assert np.array_equal(got.view(np.uint64), ref.view(np.uint64))
+                        continue
                     acc = np.zeros(n, np.float32)
                     np.add.at(acc, ii[p], g64[p].astype(np.float32))
                     got = r["acc32"].reshape(P, -1)[p]
@@ -391,8 +401,9 @@ def pin_backward(orc):
                     bound = m * 2.0**-24 * ab * 1.0001
                     assert (np.abs(got.astype(np.float64) - ref) <= bound).all()
                     assert (got[cnt == 0].view(np.uint32) == 0).all()
-                gx_ref = to_storage(torch.from_numpy(r["acc32"]).to(TORCH_DT[dt]))
-                assert np.array_equal(r["gx"], gx_ref)
+                if dt != F64:
+                    gx_ref = to_storage(torch.from_numpy(r["acc32"]).to(TORCH_DT[dt]))
+                    assert np.array_equal(r["gx"], gx_ref)
                 disjoint = all(
                     (k[a] and k[a] == s[a]) or (not k[a] and shape[2 + a] % o3[a] == 0)
                     for a in range(3))
@@ -486,11 +497,12 @@ def pin_forward_ex_torch(orc):
     seed = 1301
     for shape, k, s, pad, dil, cm in EX_CASES:
         o3 = ex_out(orc, shape, k, s, pad, dil, cm)
-        for dt in (F32, F16, BF16):
+        for dt in (F32, F16, BF16, F64):
             for kind in ("distinct", "ties"):
                 seed += 1
                 n = int(np.prod(shape))
-                if kind == "distinct" and n > {F32: 1 << 24, F16: 4096, BF16: 512}[dt]:
+                if kind == "distinct" and n > {F32: 1 << 24, F16: 4096, BF16: 512,
+                                               F64: 1 << 53}[dt]:
                     continue
                 x = draw(shape, dt, kind, seed)
                 y, idx = orc.forward_ex(x, dt, o3, k, s, pad, dil)
@@ -559,7 +571,7 @@ def pin_argmax_from_output(orc):
              ((1, 1, 2, 3, 4), (2, 2, 2), (1, 1, 1), (1, 1, 1), (3, 2, 2), False)]
     for shape, k, s, pad, dil, cm in cases:
         o3 = ex_out(orc, shape, k, s, pad, dil, cm)
-        for dt in (F32, F16, BF16):
+        for dt in (F32, F16, BF16, F64):
             for kind in ("ties", "zeros", "sparse_nan", "special"):
                 seed += 1
                 x = draw(shape, dt, kind, seed)

@@ -73,6 +73,10 @@ MUTANTS = {
         "for (int64_t jw = 0; jw < nt[2]; ++jw) {"),
     "argmax_from_output_nan_unmatched": (
         "if (isnan(want) ? isnan(v) : v == want)", "if (v == want)"),
+    "f64_backward_rounded_to_binary32": (
+        "g64[t] = g64[t] + gv;", "g64[t] = (float)(g64[t] + gv);"),
+    "f64_loaded_as_binary32": (
+        "return ((const double *)buf)[i];", "return (float)((const double *)buf)[i];"),
     "ex_empty_window_zero": (
         "((float *)y)[o] = -INFINITY;", "((float *)y)[o] = 0.0f;"),
 }
