@@ -24,8 +24,9 @@ the roofline of the dominant op (those events cost a few microseconds per
 op, so that pass is not the metric).  The values-only forward of each
 workload (no index written), the forward with int64 indices, the fixed
 workloads with padding k//2 (forward and backward), the ordered backward
-(overlap=2) and the index-free backward (argmax recomputed from x and y)
-are timed the same way, apart from the step, and reported on their own.
+(overlap=2), the index-free backward (argmax recomputed from x and y) and
+float64 forward and backward of the two large overlapping workloads are
+timed the same way, apart from the step, and reported on their own.
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (planes shard across GPUs with no communication, so more GPUs are not
@@ -150,6 +151,31 @@ def build_ops(torch, mp, workloads, variants=True):
                     g, i, wl.shape, wl.kernel, wl.stride, pad, out=gx))
                 exb_ops.append(Op(wl, "bwd_pad", bp, npo * es + npo * 4 + nin * es, nin,
                                   "backward, padding k//2"))
+    # float64 (x and gy widened exactly) on the two large overlapping workloads
+    for wl in workloads.WORKLOADS:
+        if not variants or not wl.backward or wl.shape[0] <= 4:
+            continue
+        x = wl.make_x().to(torch.float64).cuda()
+        if wl.adaptive:
+            o3 = tuple(wl.out)
+        else:
+            o3 = tuple(mp.mp3d_out_size(X, k, s) for X, k, s in zip(wl.shape[2:], wl.kernel, wl.stride))
+        oshape = wl.shape[:2] + o3
+        y = torch.empty(oshape, dtype=torch.float64, device="cuda")
+        idx = torch.empty(oshape, dtype=torch.int32, device="cuda")
+        gy = wl.make_gy(oshape).to(torch.float64).cuda()
+        gx = torch.empty_like(x)
+        nin, nout = x.numel(), y.numel()
+        if wl.adaptive:
+            f = (lambda x=x, o3=o3, y=y, idx=idx: mp.amp3d_forward(x, o3, out=(y, idx)))
+        else:
+            f = (lambda x=x, wl=wl, y=y, idx=idx: mp.mp3d_forward(x, wl.kernel, wl.stride,
+                                                                out=(y, idx)))
+        f()
+        b = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
+            gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, out=gx))
+        exf_ops.append(Op(wl, "fwd_f64", f, nin * 8 + nout * 12, nin, "forward, float64"))
+        exb_ops.append(Op(wl, "bwd_f64", b, nout * 12 + nin * 8, nin, "backward, float64"))
     # the variants run in the step's order: forwards, then backwards
     return fwd_ops + bwd_ops, (vo_ops + exf_ops + ord_ops + exb_ops) if variants else []
 
@@ -378,6 +404,7 @@ def main():
         "index_free_backward": [op_row(op) for op in vo_ops if op.kind == "bwd_recompute"],
         "int64_index_forward": [op_row(op) for op in vo_ops if op.kind == "fwd_i64"],
         "padded": [op_row(op) for op in vo_ops if op.kind in ("fwd_pad", "bwd_pad")],
+        "float64": [op_row(op) for op in vo_ops if op.kind in ("fwd_f64", "bwd_f64")],
     }
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)

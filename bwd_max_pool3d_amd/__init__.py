@@ -19,7 +19,7 @@ PyTorch fallback: if the library is missing every call raises ImportError.
   mp3d_backward_recompute(x, y, gy, kernel, stride, padding, dilation) -> gx
       index-free backward: the argmax recomputed from x and y
 
-x, y, gy and gx are float32, float16 or bfloat16; idx is int32 (int64 on
+x, y, gy and gx are float32, float16, bfloat16 or float64; idx is int32 (int64 on
 request: index_dtype=torch.int64), flat within each D*H*W plane.
 """
 from __future__ import annotations
@@ -38,7 +38,7 @@ __all__ = ["mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
 _IDX = {torch.int32: _lib.MP3D_IDX_I32, torch.int64: _lib.MP3D_IDX_I64}
 
 _DTYPE = {torch.float32: _lib.MP3D_F32, torch.float16: _lib.MP3D_F16,
-          torch.bfloat16: _lib.MP3D_BF16}
+          torch.bfloat16: _lib.MP3D_BF16, torch.float64: _lib.MP3D_F64}
 
 
 def _triple(v) -> tuple[int, int, int]:

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libmp3d.so")
 
 MP3D_OK, MP3D_EINVAL, MP3D_EDTYPE, MP3D_ENOTDIV, MP3D_EOVERFLOW, MP3D_EHIP = range(6)
-MP3D_F32, MP3D_F16, MP3D_BF16 = 0, 1, 2
+MP3D_F32, MP3D_F16, MP3D_BF16, MP3D_F64 = 0, 1, 2, 3
 
 MP3D_IDX_I32, MP3D_IDX_I64 = 0, 1
 

@@ -58,8 +58,9 @@ constexpr int64_t kInt32Max = 2147483647;
 // Shared checks of shapes and pointers; fills the per-plane sizes of g.
 int check_common(int dtype, int64_t N, int64_t C, int64_t D, int64_t H, int64_t W)
 {
-    if (dtype != MP3D_F32 && dtype != MP3D_F16 && dtype != MP3D_BF16)
-        return fail(MP3D_EDTYPE, "dtype %d is not MP3D_F32, MP3D_F16 or MP3D_BF16", dtype);
+    if (dtype != MP3D_F32 && dtype != MP3D_F16 && dtype != MP3D_BF16 && dtype != MP3D_F64)
+        return fail(MP3D_EDTYPE, "dtype %d is not MP3D_F32, MP3D_F16, MP3D_BF16 or MP3D_F64",
+                    dtype);
     if (N < 0 || C < 0)
         return fail(MP3D_EINVAL, "N=%lld and C=%lld must be >= 0", (long long)N, (long long)C);
     if (D <= 0 || H <= 0 || W <= 0)
@@ -208,8 +209,11 @@ template <typename T>
 int forward_t(const void *x, void *y, void *idx, int idx_type, const Geom &g, hipStream_t s)
 {
     if (idx_type == MP3D_IDX_I64) return run_forward_ex<T, int64_t>(x, y, (int64_t *)idx, g, s);
-    if (!g.plain()) return run_forward_ex<T, int32_t>(x, y, (int32_t *)idx, g, s);
-    return run_forward<T>(x, y, (int32_t *)idx, g, s);
+    // float64 takes the general kernel for every geometry
+    if (std::is_same<T, F64>::value || !g.plain())
+        return run_forward_ex<T, int32_t>(x, y, (int32_t *)idx, g, s);
+    if constexpr (!std::is_same<T, F64>::value) return run_forward<T>(x, y, (int32_t *)idx, g, s);
+    return MP3D_OK;
 }
 
 int forward(const void *x, void *y, void *idx, int idx_type, int dtype, const Geom &g,
@@ -220,6 +224,7 @@ int forward(const void *x, void *y, void *idx, int idx_type, int dtype, const Ge
     switch (dtype) {
     case MP3D_F32: return forward_t<F32>(x, y, idx, idx_type, g, s);
     case MP3D_F16: return forward_t<F16>(x, y, idx, idx_type, g, s);
+    case MP3D_F64: return forward_t<F64>(x, y, idx, idx_type, g, s);
     default: return forward_t<BF16>(x, y, idx, idx_type, g, s);
     }
 }
@@ -253,7 +258,7 @@ int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPat
     }
     const bool ordered = path == BwdPath::ordered;
     BwdPlan p;
-    if (plan_backward(g, ordered, &p)) {
+    if (plan_backward(g, ordered, (int)sizeof(typename T::acc), &p)) {
         if (log_enabled())
             fprintf(stderr, "[mp3d] backward %s%s dtype=%d box=(%d,%d,%d) tiles=%lld lds=%u phases=%d\n",
                     ordered ? "ordered slab" : "accumulate",
@@ -347,6 +352,7 @@ int backward(const void *gy, const void *idx, int idx_type, const void *x, const
         switch (dtype) {
         case MP3D_F32: return run_backward<F32>(gy, recompute_src<F32>(x, y, g), gx, g, rp, s);
         case MP3D_F16: return run_backward<F16>(gy, recompute_src<F16>(x, y, g), gx, g, rp, s);
+        case MP3D_F64: return run_backward<F64>(gy, recompute_src<F64>(x, y, g), gx, g, rp, s);
         default: return run_backward<BF16>(gy, recompute_src<BF16>(x, y, g), gx, g, rp, s);
         }
     }
@@ -355,6 +361,7 @@ int backward(const void *gy, const void *idx, int idx_type, const void *x, const
         switch (dtype) {
         case MP3D_F32: return run_backward<F32>(gy, ix, gx, g, path, s);
         case MP3D_F16: return run_backward<F16>(gy, ix, gx, g, path, s);
+        case MP3D_F64: return run_backward<F64>(gy, ix, gx, g, path, s);
         default: return run_backward<BF16>(gy, ix, gx, g, path, s);
         }
     }
@@ -362,6 +369,7 @@ int backward(const void *gy, const void *idx, int idx_type, const void *x, const
     switch (dtype) {
     case MP3D_F32: return run_backward<F32>(gy, ix, gx, g, path, s);
     case MP3D_F16: return run_backward<F16>(gy, ix, gx, g, path, s);
+    case MP3D_F64: return run_backward<F64>(gy, ix, gx, g, path, s);
     default: return run_backward<BF16>(gy, ix, gx, g, path, s);
     }
 }

@@ -64,6 +64,20 @@ __device__ __forceinline__ void lds_add(float *a, float v)
     }
 }
 
+// The same in binary64 (the float64 dtype), with a 64-bit compare-and-swap.
+__device__ __forceinline__ void lds_add(double *a, double v)
+{
+    unsigned long long *u = reinterpret_cast<unsigned long long *>(a);
+    unsigned long long old = *u;
+    for (;;) {
+        const unsigned long long want =
+            __builtin_bit_cast(unsigned long long, __builtin_bit_cast(double, old) + v);
+        const unsigned long long seen = atomicCAS(u, old, want);
+        if (seen == old) break;
+        old = seen;
+    }
+}
+
 constexpr int kSlabBlock = kSlabThreads;  // threads per slab workgroup
 
 // Round the accumulator a[0, n) into dst[0, n): 16-byte streaming stores for
@@ -215,7 +229,9 @@ bwd_box_kernel(const typename T::raw *__restrict__ gy, const Src src,
                typename T::raw *__restrict__ gx, BwdPlan p)
 {
     using R = typename T::raw;
-    extern __shared__ __align__(16) float acc[];
+    using Acc = typename T::acc;
+    extern __shared__ __align__(16) unsigned char smem[];
+    Acc *acc = reinterpret_cast<Acc *>(smem);
     const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
     const int32_t H = B.X, W = Cw.X;
     const int32_t tid = threadIdx.x;
@@ -234,7 +250,7 @@ bwd_box_kernel(const typename T::raw *__restrict__ gy, const Src src,
         const int32_t cw = max(Cw.last_starting(w1 - 1) + 1 - ow0, 0);
         const int64_t obase = plane * (int64_t)p.g.out_plane;
 
-        for (int32_t e = tid; e < n; e += kBlock) acc[e] = 0.0f;
+        for (int32_t e = tid; e < n; e += kBlock) acc[e] = Acc(0);
         __syncthreads();
         for (int32_t e = tid; e < cd * ch * cw; e += kBlock) {
             const int32_t owl = e % cw, r = e / cw, ohl = r % ch, odl = r / ch;
@@ -272,8 +288,9 @@ bwd_gather_kernel(const typename T::raw *__restrict__ gy, const Src src,
         const int32_t w = i % W, r = i / W, h = r % H, d = r / H;
         const int64_t o = plane * (int64_t)p.g.out_plane +
                           ((d / p.qd) * OH + h / p.qh) * OW + w / p.qw;
-        typename T::raw out = T::narrow(0.0f);
-        if (src(o) == i) out = T::narrow(0.0f + T::widen(gy[o]));
+        using Acc = typename T::acc;
+        typename T::raw out = T::narrow(Acc(0));
+        if (src(o) == i) out = T::narrow(Acc(0) + T::widen(gy[o]));
         gx[e] = out;
     }
 }
@@ -286,20 +303,24 @@ hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const 
 {
     using R = typename T::raw;
     int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)1 << 24);
-    if (p.slab) {
-        // one workgroup per slab; a multiple of 8 lets blocks map per XCD
-        // (the surplus blocks exit at once)
-        if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
-        if (p.nphase)
-            hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kOrdThreads, true, kOrdRound>), dim3((uint32_t)grid),
-                               dim3(kOrdThreads), p.lds_bytes, s, (const R *)gy, src, (R *)gx, p);
-        else
-            hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kSlabBlock, false, Src::kSlots>), dim3((uint32_t)grid),
-                               dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy, src, (R *)gx, p);
-    } else {
-        hipLaunchKernelGGL((bwd_box_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
-                           (const R *)gy, src, (R *)gx, p);
+    if constexpr (sizeof(typename T::acc) == 4) {   // the slab packs binary32 cells
+        if (p.slab) {
+            // one workgroup per slab; a multiple of 8 lets blocks map per XCD
+            // (the surplus blocks exit at once)
+            if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
+            if (p.nphase)
+                hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kOrdThreads, true, kOrdRound>),
+                                   dim3((uint32_t)grid), dim3(kOrdThreads), p.lds_bytes, s,
+                                   (const R *)gy, src, (R *)gx, p);
+            else
+                hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kSlabBlock, false, Src::kSlots>),
+                                   dim3((uint32_t)grid), dim3(kSlabBlock), p.lds_bytes, s,
+                                   (const R *)gy, src, (R *)gx, p);
+            return hipGetLastError();
+        }
     }
+    hipLaunchKernelGGL((bwd_box_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
+                       (const R *)gy, src, (R *)gx, p);
     return hipGetLastError();
 }
 
@@ -325,11 +346,16 @@ template hipError_t launch_backward_tile<F16, IdxRecompute<F16>>(const void *, c
 template hipError_t launch_backward_tile<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<BF16, IdxRecompute<BF16>>(const void *, const IdxRecompute<BF16> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F64, IdxRecompute<F64>>(const void *, const IdxRecompute<F64> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_gather<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);
 template hipError_t launch_backward_gather<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const GatherPlan &, hipStream_t);
 template hipError_t launch_backward_gather<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);
 template hipError_t launch_backward_gather<F16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const GatherPlan &, hipStream_t);
 template hipError_t launch_backward_gather<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);
 template hipError_t launch_backward_gather<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);
+template hipError_t launch_backward_gather<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const GatherPlan &, hipStream_t);
 
 }  // namespace mp3d

@@ -1,10 +1,11 @@
 // dtype.hpp -- storage types of the pooled tensors and their conversions
-// to and from binary32 on the device.
+// to and from the type the kernels compare and accumulate in (`acc`).
 //
 // float32 is stored as float; float16 and bfloat16 as their raw 16-bit
-// patterns.  Widening to binary32 is exact for all three.  Narrowing uses
-// gfx950's conversion instructions: round to nearest, ties to even (IEEE
-// 754 default), subnormals kept, overflow to infinity; NaN stays a NaN.
+// patterns; all three compare and accumulate in binary32, to which widening
+// is exact.  Narrowing uses gfx950's conversion instructions: round to
+// nearest, ties to even (IEEE 754 default), subnormals kept, overflow to
+// infinity; NaN stays a NaN.  float64 compares and accumulates in binary64.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,6 +26,7 @@ __device__ __forceinline__ void st_stream(V *p, V v) { __builtin_nontemporal_sto
 
 struct F32 {
     using raw = float;
+    using acc = float;
     static constexpr int code = 0;
     // narrowing a widened value gives back its exact bits, NaN included
     static constexpr bool exact_nan = true;
@@ -43,6 +45,7 @@ struct F32 {
 
 struct F16 {
     using raw = uint16_t;
+    using acc = float;
     static constexpr int code = 1;
     __device__ static inline float widen(uint16_t r) {
         return (float)__builtin_bit_cast(_Float16, r);   // v_cvt_f32_f16, exact
@@ -67,6 +70,7 @@ struct F16 {
 
 struct BF16 {
     using raw = uint16_t;
+    using acc = float;
     static constexpr int code = 2;
     __device__ static inline float widen(uint16_t r) {
         return __builtin_bit_cast(float, (uint32_t)r << 16);
@@ -87,6 +91,18 @@ struct BF16 {
             v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
         }
     }
+};
+
+// float64: compared and accumulated in binary64 (a binary32 accumulator
+// would round every double gradient).  Only the general kernels take it.
+struct F64 {
+    using raw = double;
+    using acc = double;
+    static constexpr int code = 3;
+    static constexpr bool exact_nan = true;
+    __device__ static inline double widen(double r) { return r; }
+    __device__ static inline double narrow(double f) { return f; }
+    __device__ static inline double back(double f) { return f; }
 };
 
 }  // namespace mp3d

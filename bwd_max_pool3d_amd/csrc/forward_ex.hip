@@ -19,7 +19,8 @@ namespace mp3d {
 
 namespace {
 
-__device__ __forceinline__ bool better(float v, float best)
+template <typename A>
+__device__ __forceinline__ bool better(A v, A best)
 {
     return v > best || (v != v && best == best);     // strictly greater, or the first NaN
 }
@@ -81,12 +82,12 @@ fwd_ex_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict
                         v[(a * 3 + b) * 3 + c] = xp[row + cw[c]];
                     }
                 }
-            float best = T::widen(v[0]);
+            typename T::acc best = T::widen(v[0]);
             pbest = pos[0];
             rbest = v[0];
 #pragma unroll
             for (int q = 1; q < 27; ++q) {
-                const float f = T::widen(v[q]);
+                const typename T::acc f = T::widen(v[q]);
                 if (better(f, best)) {
                     best = f;
                     pbest = pos[q];
@@ -99,7 +100,7 @@ fwd_ex_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict
             }
         } else {
             if (!empty) {
-                float best = 0.0f;
+                typename T::acc best = 0;
                 for (int32_t a = td.j0; a <= td.j1; ++a) {
                     const int32_t d = td.b + a * td.t;
                     for (int32_t b = th.j0; b <= th.j1; ++b) {
@@ -107,7 +108,7 @@ fwd_ex_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict
                         for (int32_t c = tw.j0; c <= tw.j1; ++c) {
                             const int32_t q = row + tw.b + c * tw.t;
                             const R v = xp[q];
-                            const float f = T::widen(v);
+                            const typename T::acc f = T::widen(v);
                             if (pbest < 0 || better(f, best)) {
                                 best = f;
                                 pbest = q;
@@ -145,5 +146,7 @@ template hipError_t launch_forward_ex<BF16, int32_t>(const void *, void *, int32
 template hipError_t launch_forward_ex<F32, int64_t>(const void *, void *, int64_t *, const ExPlan &, hipStream_t);
 template hipError_t launch_forward_ex<F16, int64_t>(const void *, void *, int64_t *, const ExPlan &, hipStream_t);
 template hipError_t launch_forward_ex<BF16, int64_t>(const void *, void *, int64_t *, const ExPlan &, hipStream_t);
+template hipError_t launch_forward_ex<F64, int32_t>(const void *, void *, int32_t *, const ExPlan &, hipStream_t);
+template hipError_t launch_forward_ex<F64, int64_t>(const void *, void *, int64_t *, const ExPlan &, hipStream_t);
 
 }  // namespace mp3d

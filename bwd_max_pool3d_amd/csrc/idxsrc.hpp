@@ -41,7 +41,8 @@ struct IdxRecompute {
     FastDiv plane_div;         // by out_plane
     FastDiv ow_div, oh_div;    // by OW, then by OH
 
-    __device__ __forceinline__ static bool hit(float v, float want, bool nan) {
+    using A = typename T::acc;
+    __device__ __forceinline__ static bool hit(A v, A want, bool nan) {
         return nan ? v != v : v == want;
     }
 
@@ -67,7 +68,7 @@ struct IdxRecompute {
         if (td.j0 > td.j1 || th.j0 > th.j1 || tw.j0 > tw.j1) return -1;
         const int32_t H = g.ax[1].X, W = g.ax[2].X;
         const R *xp = x + plane * (int64_t)g.in_plane;
-        const float want = T::widen(y[o]);
+        const A want = T::widen(y[o]);
         const bool nan = want != want;
         if (km3) {
             int32_t pos[27];

@@ -151,11 +151,13 @@ bool plan_fixed(const Geom &g, int elem_bytes, const void *x, const void *y,
 
 bool plan_forward(const Geom &g, int elem_bytes, FwdPlan *p);
 bool plan_col(const Geom &g, int elem_bytes, const void *x, ColPlan *p);
+// cell_bytes: the accumulator cell, 4 (binary32) or 8 (binary64: boxes, no
+// ordered slab).
 // plan_backward with ordered = false always succeeds; with ordered = true
 // it fails when the ordered slab cannot hold the geometry (slices larger
 // than the accumulator, a slab reached by more windows than one round
 // holds, or more than kMaxPhase phases): the ordered gather serves then.
-bool plan_backward(const Geom &g, bool ordered, BwdPlan *p);
+bool plan_backward(const Geom &g, bool ordered, int cell_bytes, BwdPlan *p);
 bool plan_small_forward(const Geom &g, SmallPlan *p);
 bool plan_small_backward(const Geom &g, SmallPlan *p);
 void plan_ordered(const Geom &g, OrdPlan *p);

@@ -269,12 +269,16 @@ static int64_t slab_reach(const Axis &a, int32_t td)
     return m;
 }
 
-bool plan_backward(const Geom &g, bool ordered, BwdPlan *p)
+bool plan_backward(const Geom &g, bool ordered, int cell_bytes, BwdPlan *p)
 {
     const int32_t D = g.ax[0].X, H = g.ax[1].X, W = g.ax[2].X;
     const int64_t budget = std::min<int64_t>(ordered ? kOrdBudget : kAccBudget,
                                              (int64_t)lds_limit() - 64);
-    const int64_t slice = (int64_t)H * W * 4;
+    const int64_t cb = cell_bytes;
+    // binary64 cells: boxes only (the slab kernel packs binary32 cells),
+    // and no ordered slab
+    if (cb != 4 && ordered) return false;
+    const int64_t slice = (int64_t)H * W * cb;
     p->g = g;
     if (slice <= budget) {
         int32_t td = (int32_t)std::min<int64_t>(D, budget / slice);
@@ -283,15 +287,15 @@ bool plan_backward(const Geom &g, bool ordered, BwdPlan *p)
         p->td = (int32_t)cdiv(D, cdiv(D, td));
         p->th = H;
         p->tw = W;
-    } else if ((int64_t)W * 4 <= budget) {
+    } else if ((int64_t)W * cb <= budget) {
         p->td = 1;
-        const int32_t th = (int32_t)std::min<int64_t>(H, budget / ((int64_t)W * 4));
+        const int32_t th = (int32_t)std::min<int64_t>(H, budget / ((int64_t)W * cb));
         p->th = (int32_t)cdiv(H, cdiv(H, th));
         p->tw = W;
     } else {
         p->td = 1;
         p->th = 1;
-        const int32_t tw = (int32_t)std::min<int64_t>(W, budget / 4);
+        const int32_t tw = (int32_t)std::min<int64_t>(W, budget / cb);
         p->tw = (int32_t)cdiv(W, cdiv(W, tw));
     }
     p->nphase = 0;
@@ -328,9 +332,9 @@ bool plan_backward(const Geom &g, bool ordered, BwdPlan *p)
     p->ntw = (int32_t)cdiv(W, p->tw);
     p->ntiles = g.planes * p->ntd * p->nth * p->ntw;
     p->split = TileSplit::make(g.planes, p->ntd, p->nth, p->ntw);
-    p->slab = p->th == H && p->tw == W;
+    p->slab = p->th == H && p->tw == W && cb == 4;
     // + alignment shift and the rounding of the zero fill to 16 bytes
-    p->lds_bytes = (uint32_t)(((int64_t)p->td * p->th * p->tw + 8) * 4);
+    p->lds_bytes = (uint32_t)(((int64_t)p->td * p->th * p->tw + 8) * cb);
     return true;
 }
 

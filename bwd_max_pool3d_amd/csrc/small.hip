@@ -129,7 +129,7 @@ bwd_small_kernel(const typename T::raw *__restrict__ gy, const Src src,
         rg[k] = gy[o];
         on[k] = valid;
     }
-    float acc = 0.0f;
+    typename T::acc acc = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
         if (on[k] && ri[k] == i) acc = acc + T::widen(rg[k]);
@@ -159,13 +159,13 @@ bwd_ordered_kernel(const typename T::raw *__restrict__ gy, const Src src,
         const int32_t h0 = B.first_reaching(h), h1 = B.last_starting(h);
         const int32_t w0 = Cw.first_reaching(w), w1 = Cw.last_starting(w);
         const int64_t obase = plane * p.g.out_plane;
-        float acc = 0.0f;
+        typename T::acc acc = 0;
         for (int32_t od = d0; od <= d1; ++od)
             for (int32_t oh = h0; oh <= h1; ++oh)
                 for (int32_t ow = w0; ow <= w1; ++ow) {
                     const int64_t o = obase + ((int64_t)od * OH + oh) * OW + ow;
                     const int32_t v = src(o);
-                    const float g = T::widen(gy[o]);
+                    const typename T::acc g = T::widen(gy[o]);
                     if (v == i) acc = acc + g;
                 }
         gx[e] = T::narrow(acc);
@@ -225,5 +225,11 @@ template hipError_t launch_backward_ordered<BF16, IdxArray<int64_t>>(const void 
 template hipError_t launch_backward_ordered<BF16, IdxRecompute<BF16>>(const void *, const IdxRecompute<BF16> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_small<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_small<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
+
+template hipError_t launch_backward_ordered<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F64, IdxRecompute<F64>>(const void *, const IdxRecompute<F64> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_small<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
+template hipError_t launch_backward_small<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
 
 }  // namespace mp3d

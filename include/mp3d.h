@@ -25,14 +25,16 @@
  *    than every number (the first NaN wins).  y holds that element's bits.
  *  - idx is int32, flat within one plane: (d*H + h)*W + w.
  *  - The backward accumulates in binary32 from +0 and rounds the sum once,
- *    to nearest-even, into the storage type.
+ *    to nearest-even, into the storage type (float64: in binary64, no
+ *    rounding).
  *
  * Layout and ownership: every tensor is contiguous NCDHW in device memory
  * owned by the caller; the library never allocates or frees.  x and gx
  * hold N*C*D*H*W elements; y, idx and gy hold N*C*OD*OH*OW.  Outputs must
  * not alias inputs, and each pointer is aligned to its element size.
  * dtype selects the storage type of x, y, gy and gx
- * (MP3D_F32, MP3D_F16, MP3D_BF16); idx is always int32.
+ * (MP3D_F32, MP3D_F16, MP3D_BF16, MP3D_F64); idx is int32 (int64 through
+ * the _ex entry points).
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Calls enqueue their kernels and return without synchronising;
@@ -58,7 +60,7 @@ enum mp3d_status {
     MP3D_EINVAL = 1,    /* null pointer with work to do, a size, kernel,
                            stride or output extent <= 0, a window larger
                            than its axis, or inconsistent shapes */
-    MP3D_EDTYPE = 2,    /* dtype is not one of MP3D_F32/F16/BF16, or idx_type
+    MP3D_EDTYPE = 2,    /* dtype is not one of MP3D_F32/F16/BF16/F64, or idx_type
                            not one of MP3D_IDX_I32/I64 */
     MP3D_ENOTDIV = 3,   /* overlap = 0 asked for, but the windows do not
                            tile every axis (see mp3d_backward) */
@@ -67,7 +69,11 @@ enum mp3d_status {
     MP3D_EHIP = 5       /* a HIP launch failed; the message names it */
 };
 
-enum mp3d_dtype { MP3D_F32 = 0, MP3D_F16 = 1, MP3D_BF16 = 2 };
+/* Storage types.  float16 and bfloat16 values are compared and gradients
+ * accumulated in binary32; float64 in binary64 (PR #308 page, Testing:
+ * that implementation leaves float64 to a generic fallback; here it is a
+ * dtype of its own, served by the general kernels). */
+enum mp3d_dtype { MP3D_F32 = 0, MP3D_F16 = 1, MP3D_BF16 = 2, MP3D_F64 = 3 };
 
 /* Index element type of the _ex entry points (the others use int32). */
 enum mp3d_index { MP3D_IDX_I32 = 0, MP3D_IDX_I64 = 1 };
@@ -94,8 +100,8 @@ int amp3d_forward(const void *x, void *y, int32_t *idx, int dtype,
                   int32_t od, int32_t oh, int32_t ow, void *stream);
 
 /* Backward (PR #308, Summary): gx[p] = sum of gy[o] over the outputs o
- * whose idx[o] == p, in binary32 from +0, rounded once to dtype; +0 where
- * no output points.  Every element of gx is written.
+ * whose idx[o] == p, in binary32 from +0, rounded once to dtype (float64:
+ * binary64); +0 where no output points.  Every element of gx is written.
  *
  * (N, C, D, H, W) is the input shape; (od, oh, ow) the shape of gy and
  * idx.  The window rule is given per axis so that the library knows which

@@ -129,7 +129,7 @@ def test_ex_empty_batch_is_a_no_op():
 
 
 @pytest.mark.parametrize("call,code", [
-    (lambda: fwd(dtype=3), _lib.MP3D_EDTYPE),
+    (lambda: fwd(dtype=4), _lib.MP3D_EDTYPE),
     (lambda: fwd(dtype=-1), _lib.MP3D_EDTYPE),
     (lambda: fwd(x=None), _lib.MP3D_EINVAL),
     (lambda: fwd(y=None), _lib.MP3D_EINVAL),            # idx NULL is allowed: values only

@@ -15,8 +15,8 @@ import bwd_max_pool3d_amd as mp
 
 pytestmark = pytest.mark.gpu
 
-DTYPES = [torch.float32, torch.float16, torch.bfloat16]
-DT_ID = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+DTYPES = [torch.float32, torch.float16, torch.bfloat16, torch.float64]
+DT_ID = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.float64: "f64"}
 
 # (shape, kernel, stride, pad, dilation, ceil_mode)
 CASES = [

@@ -19,8 +19,8 @@ from bwd_max_pool3d_amd import workloads
 
 pytestmark = pytest.mark.gpu
 
-DTYPES = [torch.float32, torch.float16, torch.bfloat16]
-DT_ID = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+DTYPES = [torch.float32, torch.float16, torch.bfloat16, torch.float64]
+DT_ID = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.float64: "f64"}
 
 # (shape, adaptive out or None, kernel, stride)
 CASES = [
@@ -208,8 +208,10 @@ def test_subnormal_gradients(orc, dtype):
     code = _gpu.CODE[dtype]
     x = _pins.from_storage(_pins.draw(shape, code, "ties", 8), code)
     y, idx = _gpu.gpu_forward(x, (8, 8, 8))
-    scale = {torch.float32: 1e-39, torch.float16: 1e-6, torch.bfloat16: 1e-39}[dtype]
-    g = (torch.randn(y.shape, generator=torch.Generator().manual_seed(9)) * scale).to(dtype)
+    scale = {torch.float32: 1e-39, torch.float16: 1e-6, torch.bfloat16: 1e-39,
+             torch.float64: 1e-310}[dtype]
+    g = (torch.randn(y.shape, generator=torch.Generator().manual_seed(9), dtype=torch.float64)
+         * scale).to(dtype)
     assert (g != 0).float().mean() > 0.5
     gx = _gpu.gpu_backward(g, idx.cpu(), shape)
     _gpu.check_backward(orc, g, idx.cpu(), shape, gx, exact=False, what="subnormal")
@@ -394,3 +396,32 @@ def test_workload_full_size(orc, wl):
         _gpu.check_backward(orc, gy[sl].contiguous(), idx[sl].cpu().contiguous(),
                             (1, 1, D, H, W), gx2[sl], exact=True,
                             what="%s ordered plane %d" % (wl.name, p))
+
+
+@pytest.mark.parametrize("wl", [w for w in workloads.WORKLOADS if w.backward and w.shape[0] > 4],
+                         ids=lambda w: w.name)
+def test_float64_full_size(orc, wl):
+    """The two large overlapping workloads with x and gy widened exactly to
+    float64: forward and the ordered backward bit-exact with the oracle on
+    sampled planes, the accumulate backward within the binary64 bound."""
+    N, C, D, H, W = wl.shape
+    P = N * C
+    x = wl.make_x().to(torch.float64)
+    xd = x.cuda()
+    out, k, s = wl.out, wl.kernel, wl.stride
+    y, idx = _gpu.gpu_forward(xd, out, k, s)
+    gy = wl.make_gy(tuple(y.shape)).to(torch.float64)
+    gyd = gy.cuda()
+    gx1 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s)
+    gx2 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=2)
+    torch.cuda.synchronize()
+    for p in _sample_planes(P):
+        n_, c_ = divmod(p, C)
+        sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
+        yo, io = _gpu.oracle_forward(orc, x[sl].contiguous(), out, k, s)
+        _gpu.assert_forward_match(y[sl], idx[sl], yo, io, "%s f64 plane %d" % (wl.name, p))
+        for gx, exact in ((gx1, False), (gx2, True)):
+            _gpu.check_backward(orc, gy[sl].contiguous(), idx[sl].cpu().contiguous(),
+                                (1, 1, D, H, W), gx[sl], exact=exact,
+                                what="%s f64 plane %d" % (wl.name, p))
+
