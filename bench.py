@@ -26,7 +26,8 @@ workload (no index written), the forward with int64 indices, the fixed
 workloads with padding k//2 (forward and backward), the ordered backward
 (overlap=2), the index-free backward (argmax recomputed from x and y) and
 float64 forward and backward of the two large overlapping workloads are
-timed the same way, apart from the step, and reported on their own.
+timed the same way, apart from the step, and reported on their own (median
+per op: launched one op at a time, an event pair can catch a host stall).
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (planes shard across GPUs with no communication, so more GPUs are not
@@ -364,12 +365,19 @@ def main():
     ms_step_ev = (t3 - t2) * 1e3 / args.steps
     step_bytes = sum(op.nbytes for op in ops)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    def op_row(op):
+    def op_row(op, median=False):
+        # step ops: the mean (it matches the profiler's average per launch);
+        # variants, timed one op at a time: the median, since a host stall
+        # while the queue is empty can land inside one event pair
         avg = sum(op.ms) / len(op.ms)
-        return {"op": op.name, "ms": round(avg, 5), "bytes": op.nbytes,
-                "GB_s": round(op.nbytes / (avg * 1e-3) / 1e9, 1),
-                "elems_per_s": round(op.elems / (avg * 1e-3), 1),
-                "frac_of_peak": round(op.nbytes / (avg * 1e-3) / 1e9 / PEAK_GBS, 4)}
+        srt = sorted(op.ms)
+        med = srt[len(srt) // 2]
+        t = med if median else avg
+        return {"op": op.name, "ms": round(t, 5), "ms_mean": round(avg, 5),
+                "ms_min": round(srt[0], 5), "ms_median": round(med, 5), "bytes": op.nbytes,
+                "GB_s": round(op.nbytes / (t * 1e-3) / 1e9, 1),
+                "elems_per_s": round(op.elems / (t * 1e-3), 1),
+                "frac_of_peak": round(op.nbytes / (t * 1e-3) / 1e9 / PEAK_GBS, 4)}
 
     per_op = [op_row(op) for op in ops]
     dom = max(per_op, key=lambda r: r["ms"])
@@ -399,12 +407,12 @@ def main():
         "copy_GB_s": round(copy_gbs, 1),
         "roofline": roofline,
         "per_op": per_op,
-        "values_only_forward": [op_row(op) for op in vo_ops if op.kind == "fwd_values"],
-        "ordered_backward": [op_row(op) for op in vo_ops if op.kind == "bwd_ordered"],
-        "index_free_backward": [op_row(op) for op in vo_ops if op.kind == "bwd_recompute"],
-        "int64_index_forward": [op_row(op) for op in vo_ops if op.kind == "fwd_i64"],
-        "padded": [op_row(op) for op in vo_ops if op.kind in ("fwd_pad", "bwd_pad")],
-        "float64": [op_row(op) for op in vo_ops if op.kind in ("fwd_f64", "bwd_f64")],
+        "values_only_forward": [op_row(op, True) for op in vo_ops if op.kind == "fwd_values"],
+        "ordered_backward": [op_row(op, True) for op in vo_ops if op.kind == "bwd_ordered"],
+        "index_free_backward": [op_row(op, True) for op in vo_ops if op.kind == "bwd_recompute"],
+        "int64_index_forward": [op_row(op, True) for op in vo_ops if op.kind == "fwd_i64"],
+        "padded": [op_row(op, True) for op in vo_ops if op.kind in ("fwd_pad", "bwd_pad")],
+        "float64": [op_row(op, True) for op in vo_ops if op.kind in ("fwd_f64", "bwd_f64")],
     }
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)

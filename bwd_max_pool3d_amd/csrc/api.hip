@@ -161,37 +161,37 @@ int hip_status(hipError_t e, const char *what)
     return fail(MP3D_EHIP, "%s: %s (hipError %d)", what, hipGetErrorString(e), (int)e);
 }
 
-template <typename T>
-int run_forward(const void *x, void *y, int32_t *idx, const Geom &g, hipStream_t s)
+template <typename T, typename IT>
+int run_forward(const void *x, void *y, IT *idx, const Geom &g, hipStream_t s)
 {
     FixedPlan fp;
     if (plan_fixed(g, (int)sizeof(typename T::raw), x, y, idx, &fp)) {
         if (log_enabled())
             fprintf(stderr, "[mp3d] forward fixed dtype=%d k=%d s=%d threads=%u vec_store=%d\n",
                     T::code, g.ax[0].k, g.ax[0].s, fp.nthreads, fp.vec_store);
-        return hip_status(launch_forward_fixed<T>(x, y, idx, fp, s), "forward fixed launch");
+        return hip_status(launch_forward_fixed<T, IT>(x, y, idx, fp, s), "forward fixed launch");
     }
     ColPlan cp;
     if (plan_col(g, (int)sizeof(typename T::raw), x, &cp)) {
         if (log_enabled())
             fprintf(stderr, "[mp3d] forward column dtype=%d tod=%d tiles=%u maxkd=%d lds=%u\n",
                     T::code, cp.tod, cp.ntiles, cp.maxkd, cp.lds_bytes);
-        return hip_status(launch_forward_col<T>(x, y, idx, cp, s), "forward column launch");
+        return hip_status(launch_forward_col<T, IT>(x, y, idx, cp, s), "forward column launch");
     }
     SmallPlan sp;
     if (small_enabled() && plan_small_forward(g, &sp)) {
         if (log_enabled()) fprintf(stderr, "[mp3d] forward small dtype=%d outputs=%u\n", T::code, sp.total);
-        return hip_status(launch_forward_small<T>(x, y, idx, sp, s), "forward small launch");
+        return hip_status(launch_forward_small<T, IT>(x, y, idx, sp, s), "forward small launch");
     }
     FwdPlan p;
     if (plan_forward(g, (int)sizeof(typename T::raw), &p)) {
         if (log_enabled())
             fprintf(stderr, "[mp3d] forward tile dtype=%d tile=(%d,%d,%d) tiles=%lld lds=%u\n",
                     T::code, p.tod, p.toh, p.tow, (long long)p.ntiles, p.lds_bytes);
-        return hip_status(launch_forward_tile<T>(x, y, idx, p, s), "forward tile launch");
+        return hip_status(launch_forward_tile<T, IT>(x, y, idx, p, s), "forward tile launch");
     }
     if (log_enabled()) fprintf(stderr, "[mp3d] forward direct dtype=%d\n", T::code);
-    return hip_status(launch_forward_direct<T>(x, y, idx, g, s), "forward direct launch");
+    return hip_status(launch_forward_direct<T, IT>(x, y, idx, g, s), "forward direct launch");
 }
 
 template <typename T, typename IT>
@@ -205,15 +205,23 @@ int run_forward_ex(const void *x, void *y, IT *idx, const Geom &g, hipStream_t s
     return hip_status(launch_forward_ex<T, IT>(x, y, idx, p, s), "forward general launch");
 }
 
+template <typename T, typename IT>
+int forward_it(const void *x, void *y, IT *idx, const Geom &g, hipStream_t s)
+{
+    // float64 and padded / dilated windows take the general kernel
+    if constexpr (std::is_same<T, F64>::value) {
+        return run_forward_ex<T, IT>(x, y, idx, g, s);
+    } else {
+        if (!g.plain()) return run_forward_ex<T, IT>(x, y, idx, g, s);
+        return run_forward<T, IT>(x, y, idx, g, s);
+    }
+}
+
 template <typename T>
 int forward_t(const void *x, void *y, void *idx, int idx_type, const Geom &g, hipStream_t s)
 {
-    if (idx_type == MP3D_IDX_I64) return run_forward_ex<T, int64_t>(x, y, (int64_t *)idx, g, s);
-    // float64 takes the general kernel for every geometry
-    if (std::is_same<T, F64>::value || !g.plain())
-        return run_forward_ex<T, int32_t>(x, y, (int32_t *)idx, g, s);
-    if constexpr (!std::is_same<T, F64>::value) return run_forward<T>(x, y, (int32_t *)idx, g, s);
-    return MP3D_OK;
+    if (idx_type == MP3D_IDX_I64) return forward_it<T, int64_t>(x, y, (int64_t *)idx, g, s);
+    return forward_it<T, int32_t>(x, y, (int32_t *)idx, g, s);
 }
 
 int forward(const void *x, void *y, void *idx, int idx_type, int dtype, const Geom &g,

@@ -18,6 +18,7 @@ namespace mp3d {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
 // Streaming (non-temporal) stores: data written once is not kept in the
 // caches.  Output streams measured markedly faster this way.

@@ -133,10 +133,10 @@ __device__ __forceinline__ void write_table(int2 *tab, const FwdPlan &p, const T
 //  stage C: every output combines the row partials of its window's (d, h)
 //           rows in ascending order, then stores y (the element's own
 //           bits, read back from the box) and idx.
-template <typename T>
+template <typename T, typename IT>
 __device__ __forceinline__ void reduce_tile(const FwdPlan &p, const Tile &tl, const int2 *tab,
                                    const typename T::raw *box, float *pv, int32_t *pw,
-                                   typename T::raw *__restrict__ y, int32_t *__restrict__ idx)
+                                   typename T::raw *__restrict__ y, IT *__restrict__ idx)
 {
     const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X, OH = p.g.ax[1].O, OW = p.g.ax[2].O;
     const int32_t tid = threadIdx.x;
@@ -200,10 +200,10 @@ __device__ __forceinline__ void reduce_tile(const FwdPlan &p, const Tile &tl, co
     }
 }
 
-template <typename T>
+template <typename T, typename IT>
 __global__ void __launch_bounds__(kBlock)
 fwd_tile_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict__ y,
-                int32_t *__restrict__ idx, FwdPlan p)
+                IT *__restrict__ idx, FwdPlan p)
 {
     using R = typename T::raw;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -237,7 +237,7 @@ fwd_tile_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restri
                 const R *ns = x + nx.plane * (int64_t)p.g.in_plane + nx.bd0 * H * W;
                 span_fetch(regs, ns, span_shape(ns, (nx.bd1 - nx.bd0) * H * W));
             }
-            reduce_tile<T>(p, tl, tab, box, pv, pw, y, idx);
+            reduce_tile<T, IT>(p, tl, tab, box, pv, pw, y, idx);
             __syncthreads();   // LDS is reused by the next tile
         }
     } else {
@@ -253,16 +253,16 @@ fwd_tile_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restri
             }
             write_table(tab, p, tl);
             __syncthreads();
-            reduce_tile<T>(p, tl, tab, box, pv, pw, y, idx);
+            reduce_tile<T, IT>(p, tl, tab, box, pv, pw, y, idx);
             __syncthreads();
         }
     }
 }
 
-template <typename T>
+template <typename T, typename IT>
 __global__ void __launch_bounds__(kBlock)
 fwd_direct_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict__ y,
-                  int32_t *__restrict__ idx, Geom g)
+                  IT *__restrict__ idx, Geom g)
 {
     using R = typename T::raw;
     const Axis A = g.ax[0], B = g.ax[1], Cw = g.ax[2];
@@ -300,41 +300,45 @@ fwd_direct_kernel(const typename T::raw *__restrict__ x, typename T::raw *__rest
 
 }  // namespace
 
-template <typename T>
-hipError_t launch_forward_tile(const void *x, void *y, int32_t *idx,
-                               const FwdPlan &p, hipStream_t s)
+template <typename T, typename IT>
+hipError_t launch_forward_tile(const void *x, void *y, IT *idx, const FwdPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
     // persistent: as many workgroups as can be resident at once
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd_tile_kernel<T>, kBlock,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd_tile_kernel<T, IT>, kBlock,
                                                      p.lds_bytes) != hipSuccess || per_cu < 1)
         per_cu = 1;
     int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)per_cu * device_cus());
     if (grid >= 64) grid &= ~(int64_t)7;    // a multiple of 8 lets blocks map per XCD
-    hipLaunchKernelGGL(fwd_tile_kernel<T>, dim3((uint32_t)grid), dim3(kBlock),
+    hipLaunchKernelGGL((fwd_tile_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock),
                        p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_forward_direct(const void *x, void *y, int32_t *idx,
-                                 const Geom &g, hipStream_t s)
+template <typename T, typename IT>
+hipError_t launch_forward_direct(const void *x, void *y, IT *idx, const Geom &g, hipStream_t s)
 {
     using R = typename T::raw;
     const int64_t total = g.planes * (int64_t)g.out_plane;
     int64_t grid = (total + kBlock - 1) / kBlock;
     if (grid > (1 << 20)) grid = 1 << 20;
-    hipLaunchKernelGGL(fwd_direct_kernel<T>, dim3((uint32_t)grid), dim3(kBlock), 0, s,
+    hipLaunchKernelGGL((fwd_direct_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
                        (const R *)x, (R *)y, idx, g);
     return hipGetLastError();
 }
 
-template hipError_t launch_forward_tile<F32>(const void *, void *, int32_t *, const FwdPlan &, hipStream_t);
-template hipError_t launch_forward_tile<F16>(const void *, void *, int32_t *, const FwdPlan &, hipStream_t);
-template hipError_t launch_forward_tile<BF16>(const void *, void *, int32_t *, const FwdPlan &, hipStream_t);
-template hipError_t launch_forward_direct<F32>(const void *, void *, int32_t *, const Geom &, hipStream_t);
-template hipError_t launch_forward_direct<F16>(const void *, void *, int32_t *, const Geom &, hipStream_t);
-template hipError_t launch_forward_direct<BF16>(const void *, void *, int32_t *, const Geom &, hipStream_t);
+template hipError_t launch_forward_tile<F32, int32_t>(const void *, void *, int32_t *, const FwdPlan &, hipStream_t);
+template hipError_t launch_forward_tile<F16, int32_t>(const void *, void *, int32_t *, const FwdPlan &, hipStream_t);
+template hipError_t launch_forward_tile<BF16, int32_t>(const void *, void *, int32_t *, const FwdPlan &, hipStream_t);
+template hipError_t launch_forward_tile<F32, int64_t>(const void *, void *, int64_t *, const FwdPlan &, hipStream_t);
+template hipError_t launch_forward_tile<F16, int64_t>(const void *, void *, int64_t *, const FwdPlan &, hipStream_t);
+template hipError_t launch_forward_tile<BF16, int64_t>(const void *, void *, int64_t *, const FwdPlan &, hipStream_t);
+template hipError_t launch_forward_direct<F32, int32_t>(const void *, void *, int32_t *, const Geom &, hipStream_t);
+template hipError_t launch_forward_direct<F16, int32_t>(const void *, void *, int32_t *, const Geom &, hipStream_t);
+template hipError_t launch_forward_direct<BF16, int32_t>(const void *, void *, int32_t *, const Geom &, hipStream_t);
+template hipError_t launch_forward_direct<F32, int64_t>(const void *, void *, int64_t *, const Geom &, hipStream_t);
+template hipError_t launch_forward_direct<F16, int64_t>(const void *, void *, int64_t *, const Geom &, hipStream_t);
+template hipError_t launch_forward_direct<BF16, int64_t>(const void *, void *, int64_t *, const Geom &, hipStream_t);
 
 }  // namespace mp3d

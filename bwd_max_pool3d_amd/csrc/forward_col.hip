@@ -86,10 +86,10 @@ __device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, float *pv, ui
     }
 }
 
-template <typename T, int MAXKD>
+template <typename T, typename IT, int MAXKD>
 __global__ void __launch_bounds__(kBlock)
 fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict__ y,
-               int32_t *__restrict__ idx, ColPlan p)
+               IT *__restrict__ idx, ColPlan p)
 {
     using R = typename T::raw;
     constexpr int VE = 16 / (int)sizeof(R);
@@ -181,32 +181,34 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         else
             raw = xp[pos];                // NaN: copy the element's own bits
         st_stream(y + obase + e, raw);
-        if (idx) st_stream(idx + obase + e, pos);
+        if (idx) st_stream(idx + obase + e, (IT)pos);
     }
 }
 
-template <typename T, int MAXKD>
-hipError_t launch_col(const void *x, void *y, int32_t *idx, const ColPlan &p, hipStream_t s)
+template <typename T, typename IT, int MAXKD>
+hipError_t launch_col(const void *x, void *y, IT *idx, const ColPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
     int64_t grid = p.ntiles;
-    hipLaunchKernelGGL((fwd_col_kernel<T, MAXKD>), dim3((uint32_t)grid), dim3(kBlock),
+    hipLaunchKernelGGL((fwd_col_kernel<T, IT, MAXKD>), dim3((uint32_t)grid), dim3(kBlock),
                        p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-template <typename T>
-hipError_t launch_forward_col(const void *x, void *y, int32_t *idx, const ColPlan &p,
-                              hipStream_t s)
+template <typename T, typename IT>
+hipError_t launch_forward_col(const void *x, void *y, IT *idx, const ColPlan &p, hipStream_t s)
 {
-    if (p.maxkd <= 4) return launch_col<T, 4>(x, y, idx, p, s);
-    return launch_col<T, 8>(x, y, idx, p, s);
+    if (p.maxkd <= 4) return launch_col<T, IT, 4>(x, y, idx, p, s);
+    return launch_col<T, IT, 8>(x, y, idx, p, s);
 }
 
-template hipError_t launch_forward_col<F32>(const void *, void *, int32_t *, const ColPlan &, hipStream_t);
-template hipError_t launch_forward_col<F16>(const void *, void *, int32_t *, const ColPlan &, hipStream_t);
-template hipError_t launch_forward_col<BF16>(const void *, void *, int32_t *, const ColPlan &, hipStream_t);
+template hipError_t launch_forward_col<F32, int32_t>(const void *, void *, int32_t *, const ColPlan &, hipStream_t);
+template hipError_t launch_forward_col<F16, int32_t>(const void *, void *, int32_t *, const ColPlan &, hipStream_t);
+template hipError_t launch_forward_col<BF16, int32_t>(const void *, void *, int32_t *, const ColPlan &, hipStream_t);
+template hipError_t launch_forward_col<F32, int64_t>(const void *, void *, int64_t *, const ColPlan &, hipStream_t);
+template hipError_t launch_forward_col<F16, int64_t>(const void *, void *, int64_t *, const ColPlan &, hipStream_t);
+template hipError_t launch_forward_col<BF16, int64_t>(const void *, void *, int64_t *, const ColPlan &, hipStream_t);
 
 }  // namespace mp3d

@@ -113,10 +113,10 @@ __device__ __forceinline__ float scan_window(El el, int o, int &code)
 // Outputs are written with streaming stores: they leave the caches clean
 // for the kernels that follow (measured about 1 % faster over the whole
 // forward + backward sequence than cached stores).
-template <typename T, int KD, int KH, int KW, int SD, int SH, int SW, int V>
+template <typename T, typename IT, int KD, int KH, int KW, int SD, int SH, int SW, int V>
 __global__ void __launch_bounds__(kBlock)
 fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict__ y,
-                 int32_t *__restrict__ idx, FixedPlan p)
+                 IT *__restrict__ idx, FixedPlan p)
 {
     using R = typename T::raw;
     constexpr int SPAN = (V - 1) * SW + KW;      // input columns per thread
@@ -274,15 +274,20 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
         const int32_t nrow = row0 < p.nrows ? (int32_t)min((uint32_t)p.rpw, p.nrows - row0) : 0;
         const int32_t cnt = nrow * OW;
         const int64_t first = (int64_t)row0 * OW;
-        // idx: 4 per vector
+        // idx: IVE per 16-byte vector
         if (idx) {
-            const int32_t head = min((int32_t)((4 - first % 4) % 4), cnt);
-            const int32_t nvec = (cnt - head) / 4, tail0 = head + nvec * 4;
+            constexpr int IVE = 16 / (int)sizeof(IT);
+            const int32_t head = min((int32_t)((IVE - first % IVE) % IVE), cnt);
+            const int32_t nvec = (cnt - head) / IVE, tail0 = head + nvec * IVE;
             if (lane < head) idx[first + lane] = s_idx[wv][lane];
             for (int32_t i = lane; i < nvec; i += 64) {
-                const int32_t k = head + 4 * i;
-                st_stream(reinterpret_cast<i32x4 *>(idx + first + k),
-                          i32x4{s_idx[wv][k], s_idx[wv][k + 1], s_idx[wv][k + 2], s_idx[wv][k + 3]});
+                const int32_t k = head + IVE * i;
+                if constexpr (sizeof(IT) == 4)
+                    st_stream(reinterpret_cast<i32x4 *>(idx + first + k),
+                              i32x4{s_idx[wv][k], s_idx[wv][k + 1], s_idx[wv][k + 2], s_idx[wv][k + 3]});
+                else
+                    st_stream(reinterpret_cast<i64x2 *>(idx + first + k),
+                              i64x2{s_idx[wv][k], s_idx[wv][k + 1]});
             }
             if (lane < cnt - tail0) idx[first + tail0 + lane] = s_idx[wv][tail0 + lane];
         }
@@ -308,7 +313,14 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
     } else if (active) {
         if (p.vec_store && ow0 + V <= OW) {
             static_assert(V == 4, "vector store assumes four outputs");
-            if (idx) st_stream(reinterpret_cast<i32x4 *>(idx + obase), i32x4{io[0], io[1], io[2], io[3]});
+            if (idx) {
+                if constexpr (sizeof(IT) == 4) {
+                    st_stream(reinterpret_cast<i32x4 *>(idx + obase), i32x4{io[0], io[1], io[2], io[3]});
+                } else {
+                    st_stream(reinterpret_cast<i64x2 *>(idx + obase), i64x2{io[0], io[1]});
+                    st_stream(reinterpret_cast<i64x2 *>(idx + obase + 2), i64x2{io[2], io[3]});
+                }
+            }
             if constexpr (sizeof(R) == 4) {
                 st_stream(reinterpret_cast<u32x4 *>(y + obase),
                           u32x4{__builtin_bit_cast(uint32_t, yo[0]), __builtin_bit_cast(uint32_t, yo[1]),
@@ -330,8 +342,8 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
     }
 }
 
-template <typename T, int KD, int KH, int KW, int SD, int SH, int SW>
-hipError_t launch_fixed(const void *x, void *y, int32_t *idx, const FixedPlan &p, hipStream_t s)
+template <typename T, typename IT, int KD, int KH, int KW, int SD, int SH, int SW>
+hipError_t launch_fixed(const void *x, void *y, IT *idx, const FixedPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
     uint32_t grid;
@@ -342,7 +354,7 @@ hipError_t launch_fixed(const void *x, void *y, int32_t *idx, const FixedPlan &p
         grid = (uint32_t)((p.nthreads + kBlock - 1) / kBlock);
     }
     grid = (grid + 7u) & ~7u;
-    hipLaunchKernelGGL((fwd_fixed_kernel<T, KD, KH, KW, SD, SH, SW, FixedPlan::V>), dim3(grid),
+    hipLaunchKernelGGL((fwd_fixed_kernel<T, IT, KD, KH, KW, SD, SH, SW, FixedPlan::V>), dim3(grid),
                        dim3(kBlock), 0, s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
@@ -358,16 +370,19 @@ bool fixed_shape_supported(const Geom &g)
     return (a.k == 2 && a.s == 2) || (a.k == 3 && a.s == 2);
 }
 
-template <typename T>
-hipError_t launch_forward_fixed(const void *x, void *y, int32_t *idx, const FixedPlan &p,
+template <typename T, typename IT>
+hipError_t launch_forward_fixed(const void *x, void *y, IT *idx, const FixedPlan &p,
                                 hipStream_t s)
 {
-    if (p.g.ax[0].k == 2) return launch_fixed<T, 2, 2, 2, 2, 2, 2>(x, y, idx, p, s);
-    return launch_fixed<T, 3, 3, 3, 2, 2, 2>(x, y, idx, p, s);
+    if (p.g.ax[0].k == 2) return launch_fixed<T, IT, 2, 2, 2, 2, 2, 2>(x, y, idx, p, s);
+    return launch_fixed<T, IT, 3, 3, 3, 2, 2, 2>(x, y, idx, p, s);
 }
 
-template hipError_t launch_forward_fixed<F32>(const void *, void *, int32_t *, const FixedPlan &, hipStream_t);
-template hipError_t launch_forward_fixed<F16>(const void *, void *, int32_t *, const FixedPlan &, hipStream_t);
-template hipError_t launch_forward_fixed<BF16>(const void *, void *, int32_t *, const FixedPlan &, hipStream_t);
+template hipError_t launch_forward_fixed<F32, int32_t>(const void *, void *, int32_t *, const FixedPlan &, hipStream_t);
+template hipError_t launch_forward_fixed<F16, int32_t>(const void *, void *, int32_t *, const FixedPlan &, hipStream_t);
+template hipError_t launch_forward_fixed<BF16, int32_t>(const void *, void *, int32_t *, const FixedPlan &, hipStream_t);
+template hipError_t launch_forward_fixed<F32, int64_t>(const void *, void *, int64_t *, const FixedPlan &, hipStream_t);
+template hipError_t launch_forward_fixed<F16, int64_t>(const void *, void *, int64_t *, const FixedPlan &, hipStream_t);
+template hipError_t launch_forward_fixed<BF16, int64_t>(const void *, void *, int64_t *, const FixedPlan &, hipStream_t);
 
 }  // namespace mp3d

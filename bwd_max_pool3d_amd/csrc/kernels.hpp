@@ -164,26 +164,21 @@ void plan_ordered(const Geom &g, OrdPlan *p);
 void plan_ex(const Geom &g, ExPlan *p);
 int64_t max_taps(const Axis &a);         // most taps of one window on the axis
 
-template <typename T>
-hipError_t launch_forward_tile(const void *x, void *y, int32_t *idx,
-                               const FwdPlan &p, hipStream_t s);
-template <typename T>
-hipError_t launch_forward_fixed(const void *x, void *y, int32_t *idx,
-                                const FixedPlan &p, hipStream_t s);
-template <typename T>
-hipError_t launch_forward_col(const void *x, void *y, int32_t *idx,
-                              const ColPlan &p, hipStream_t s);
-template <typename T>
-hipError_t launch_forward_direct(const void *x, void *y, int32_t *idx,
-                                 const Geom &g, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_forward_tile(const void *x, void *y, IT *idx, const FwdPlan &p, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_forward_fixed(const void *x, void *y, IT *idx, const FixedPlan &p, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_forward_col(const void *x, void *y, IT *idx, const ColPlan &p, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_forward_direct(const void *x, void *y, IT *idx, const Geom &p, hipStream_t s);
 template <typename T, typename IT>
 hipError_t launch_forward_ex(const void *x, void *y, IT *idx, const ExPlan &p, hipStream_t s);
 template <typename T, typename Src>
 hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const BwdPlan &p,
                                 hipStream_t s);
-template <typename T>
-hipError_t launch_forward_small(const void *x, void *y, int32_t *idx,
-                                const SmallPlan &p, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_forward_small(const void *x, void *y, IT *idx, const SmallPlan &p, hipStream_t s);
 template <typename T, typename Src>
 hipError_t launch_backward_small(const void *gy, const Src &src, void *gx, const SmallPlan &p,
                                  hipStream_t s);

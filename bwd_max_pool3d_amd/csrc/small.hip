@@ -28,10 +28,10 @@ __device__ __forceinline__ bool better(float v, float best)
 // the thread loads a kSmallK^3 block whose slots past the window's end
 // repeat its last element, so that a repeat comes after the element it
 // copies in scan order and never wins.
-template <typename T>
+template <typename T, typename IT>
 __global__ void __launch_bounds__(kBlock)
 fwd_small_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict__ y,
-                 int32_t *__restrict__ idx, SmallPlan p)
+                 IT *__restrict__ idx, SmallPlan p)
 {
     using R = typename T::raw;
     constexpr int K = kSmallK;
@@ -185,12 +185,12 @@ hipError_t launch_backward_ordered(const void *gy, const Src &src, void *gx, con
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_forward_small(const void *x, void *y, int32_t *idx, const SmallPlan &p,
+template <typename T, typename IT>
+hipError_t launch_forward_small(const void *x, void *y, IT *idx, const SmallPlan &p,
                                 hipStream_t s)
 {
     using R = typename T::raw;
-    hipLaunchKernelGGL(fwd_small_kernel<T>, dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
+    hipLaunchKernelGGL((fwd_small_kernel<T, IT>), dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
                        s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
@@ -205,9 +205,6 @@ hipError_t launch_backward_small(const void *gy, const Src &src, void *gx, const
     return hipGetLastError();
 }
 
-template hipError_t launch_forward_small<F32>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
-template hipError_t launch_forward_small<F16>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
-template hipError_t launch_forward_small<BF16>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
 
 
 template hipError_t launch_backward_ordered<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const OrdPlan &, hipStream_t);
@@ -231,5 +228,12 @@ template hipError_t launch_backward_ordered<F64, IdxArray<int64_t>>(const void *
 template hipError_t launch_backward_ordered<F64, IdxRecompute<F64>>(const void *, const IdxRecompute<F64> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_small<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_small<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
+
+template hipError_t launch_forward_small<F32, int32_t>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
+template hipError_t launch_forward_small<F16, int32_t>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
+template hipError_t launch_forward_small<BF16, int32_t>(const void *, void *, int32_t *, const SmallPlan &, hipStream_t);
+template hipError_t launch_forward_small<F32, int64_t>(const void *, void *, int64_t *, const SmallPlan &, hipStream_t);
+template hipError_t launch_forward_small<F16, int64_t>(const void *, void *, int64_t *, const SmallPlan &, hipStream_t);
+template hipError_t launch_forward_small<BF16, int64_t>(const void *, void *, int64_t *, const SmallPlan &, hipStream_t);
 
 }  // namespace mp3d

@@ -363,6 +363,15 @@ def test_workload_full_size(orc, wl):
         _gpu.assert_forward_match(y[n_:n_ + 1, c_:c_ + 1], idx[n_:n_ + 1, c_:c_ + 1], yo, io,
                                   "%s plane %d" % (wl.name, p))
     _full_properties(orc, wl, xd, y, idx)
+    # int64 indices: the same positions and the same y
+    if k is None:
+        y64, i64 = mp.amp3d_forward(xd, out, index_dtype=torch.int64)
+    else:
+        y64, i64 = mp.mp3d_forward(xd, k, s, index_dtype=torch.int64)
+    assert torch.equal(i64, idx.to(torch.int64)), "%s int64 idx differs" % wl.name
+    assert torch.equal(y64.view(torch.int16 if y64.element_size() == 2 else torch.int32),
+                       y.view(torch.int16 if y.element_size() == 2 else torch.int32))
+    del y64, i64
     # values-only forward (idx NULL): the same y, bit for bit
     yv = _gpu.gpu_forward(xd, out, k, s, indices=False)
     assert torch.equal(yv.view(torch.int16 if yv.element_size() == 2 else torch.int32),
