@@ -208,11 +208,14 @@ int run_forward_ex(const void *x, void *y, IT *idx, const Geom &g, hipStream_t s
 template <typename T, typename IT>
 int forward_it(const void *x, void *y, IT *idx, const Geom &g, hipStream_t s)
 {
-    // float64 and padded / dilated windows take the general kernel
+    // float64 and dilated windows take the general kernel; padded and
+    // ceil-mode windows of dilation 1 are clipped spans, which the column,
+    // tile, small and direct kernels scan as they are (the fixed kernel
+    // takes plain windows only)
     if constexpr (std::is_same<T, F64>::value) {
         return run_forward_ex<T, IT>(x, y, idx, g, s);
     } else {
-        if (!g.plain()) return run_forward_ex<T, IT>(x, y, idx, g, s);
+        if (!g.contiguous()) return run_forward_ex<T, IT>(x, y, idx, g, s);
         return run_forward<T, IT>(x, y, idx, g, s);
     }
 }

@@ -86,8 +86,8 @@ __device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, float *pv, ui
     }
 }
 
-template <typename T, typename IT, int MAXKD>
-__global__ void __launch_bounds__(kBlock)
+template <typename T, typename IT, int MAXKD, int NT>
+__global__ void __launch_bounds__(NT)
 fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict__ y,
                IT *__restrict__ idx, ColPlan p)
 {
@@ -110,14 +110,14 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
     const int32_t cd = od1 - od0;
     const R *xp = x + (int64_t)plane * p.g.in_plane;
 
-    for (int32_t j = tid; j < B.O + Cw.O; j += kBlock)
+    for (int32_t j = tid; j < B.O + Cw.O; j += NT)
         tab[j] = j < B.O ? make_int2(B.start(j), B.end(j))
                          : make_int2(Cw.start(j - B.O), Cw.end(j - B.O));
 
     // stage D: the loads of two windows in flight while the previous one
     // is reduced
     const int32_t ngroups = HW / VE;
-    for (int32_t gi = tid; gi < ngroups; gi += kBlock) {
+    for (int32_t gi = tid; gi < ngroups; gi += NT) {
         const R *col = xp + gi * VE;
         ColWin<MAXKD> wa, wb;
         int32_t ds = A.start(od0);
@@ -142,7 +142,7 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
     const int32_t per_slice = B.O * Cw.O;
     const int32_t nout = cd * per_slice;
     const int64_t obase = (int64_t)plane * p.g.out_plane + (int64_t)od0 * per_slice;
-    for (int32_t e = tid; e < nout; e += kBlock) {
+    for (int32_t e = tid; e < nout; e += NT) {
         const uint32_t q = p.ow_div.div((uint32_t)e);
         const int32_t ow = e - (int32_t)q * Cw.O;
         const uint32_t odl = p.oh_div.div(q);
@@ -190,8 +190,12 @@ hipError_t launch_col(const void *x, void *y, IT *idx, const ColPlan &p, hipStre
 {
     using R = typename T::raw;
     int64_t grid = p.ntiles;
-    hipLaunchKernelGGL((fwd_col_kernel<T, IT, MAXKD>), dim3((uint32_t)grid), dim3(kBlock),
-                       p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
+    if (p.lds_bytes > kColBigLds)
+        hipLaunchKernelGGL((fwd_col_kernel<T, IT, MAXKD, kColBigThreads>), dim3((uint32_t)grid),
+                           dim3(kColBigThreads), p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
+    else
+        hipLaunchKernelGGL((fwd_col_kernel<T, IT, MAXKD, kBlock>), dim3((uint32_t)grid),
+                           dim3(kBlock), p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
 

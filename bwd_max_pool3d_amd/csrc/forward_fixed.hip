@@ -366,6 +366,7 @@ hipError_t launch_fixed(const void *x, void *y, IT *idx, const FixedPlan &p, hip
 bool fixed_shape_supported(const Geom &g)
 {
     const Axis &a = g.ax[0], &b = g.ax[1], &c = g.ax[2];
+    if (!g.plain()) return false;          // no padding, every window inside the axes
     if (!a.k || a.k != b.k || a.k != c.k || a.s != b.s || a.s != c.s) return false;
     return (a.k == 2 && a.s == 2) || (a.k == 3 && a.s == 2);
 }

@@ -46,10 +46,10 @@ struct FastDiv {
 // One spatial axis: extent X split into O windows; k > 0 selects fixed
 // windows, k == 0 adaptive windows.  A fixed window o has k taps at
 // o*s - pad + j*dil (j < k), spanning ext = (k-1)*dil + 1 positions; taps
-// outside [0, X) are padding and never taken.  With pad = 0 and dil = 1
-// (`plain`) window o is [o*s, o*s + k).  When every numerator below fits 31
-// bits (`fast`), the divisions by O, X and s use precomputed multiply-high
-// constants instead of 64-bit division.
+// outside [0, X) are padding and never taken.  `plain`: no padding,
+// dilation 1 and no window past the axis end (window o is [o*s, o*s + k)).
+// When every numerator below fits 31 bits (`fast`), the divisions by O, X
+// and s use precomputed multiply-high constants instead of 64-bit division.
 struct Axis {
     int32_t X, O, k, s;
     int32_t pad, dil, ext;
@@ -71,17 +71,23 @@ struct Axis {
         return a;
     }
 
-    __host__ __device__ inline bool plain() const { return pad == 0 && dil == 1; }
+    __host__ __device__ inline bool plain() const {
+        return k == 0 || (pad == 0 && dil == 1 && (int64_t)(O - 1) * s + k <= X);
+    }
+    // taps are every position of the span: dilation 1
+    __host__ __device__ inline bool contiguous() const { return dil == 1; }
 
-    // Span [start, end) of window o; for fixed windows it may reach into
-    // the padding (start < 0 or end > X).
+    // Span [start, end) of window o, clipped to the axis.  With dilation 1
+    // these are exactly the window's taps inside the input, so a kernel
+    // that scans [start, end) serves padded and ceil-mode windows as they
+    // are; with dilation > 1 the span also holds positions between taps.
     __host__ __device__ inline int32_t start(int32_t o) const {
-        if (k) return o * s - pad;
+        if (k) { const int32_t b = o * s - pad; return b > 0 ? b : 0; }
         if (fast) return (int32_t)dO.div((uint32_t)(o * X));
         return (int32_t)(((int64_t)o * X) / O);
     }
     __host__ __device__ inline int32_t end(int32_t o) const {
-        if (k) return o * s - pad + ext;
+        if (k) { const int32_t e = o * s - pad + ext; return e < X ? e : X; }
         if (fast) return (int32_t)dO.div((uint32_t)((o + 1) * X + O - 1));
         return (int32_t)((((int64_t)o + 1) * X + O - 1) / O);
     }
@@ -170,6 +176,9 @@ struct Geom {
 
     __host__ __device__ inline bool plain() const {
         return ax[0].plain() && ax[1].plain() && ax[2].plain();
+    }
+    __host__ __device__ inline bool contiguous() const {
+        return ax[0].contiguous() && ax[1].contiguous() && ax[2].contiguous();
     }
 };
 

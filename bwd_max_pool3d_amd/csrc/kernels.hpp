@@ -68,6 +68,11 @@ struct BwdPlan {
 };
 constexpr int kBwdRound = 8;               // slab: windows per thread fetched per round
 constexpr int kOrdThreads = 256;           // threads per ordered slab workgroup
+// Column forward: a workgroup whose slice partials take more LDS than this
+// runs with more threads (fewer workgroups fit on a CU, so each needs more
+// waves to keep loads in flight).
+constexpr uint32_t kColBigLds = 40 * 1024;
+constexpr int kColBigThreads = 512;
 constexpr int kOrdRound = 8;               // ordered slab: windows per thread (one round)
 constexpr int kMaxPhase = 64;              // ordered slab: at most this many phases
 

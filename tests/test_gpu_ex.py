@@ -31,6 +31,10 @@ CASES = [
     ((1, 1, 2, 3, 4), (2, 2, 2), (1, 1, 1), (1, 1, 1), (3, 2, 2), False),      # all-padding windows
     ((1, 1, 3, 200, 300), (3, 3, 3), (1, 2, 2), (1, 1, 1), (1, 1, 1), False),  # slices beyond LDS
     ((1, 3, 16, 32, 32), (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), False),   # stride 1, overlap 3
+    ((1, 2, 5, 7, 9), (2, 2, 2), (2, 2, 2), (0, 0, 0), (1, 1, 1), True),        # last window past the end
+    ((2, 1, 7, 9, 10), (3, 3, 3), (2, 2, 2), (0, 0, 0), (1, 1, 1), True),
+    ((1, 2, 9, 17, 40), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), True),      # column kernel width
+    ((1, 1, 6, 60, 64), (2, 2, 2), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),
 ]
 
 
@@ -52,10 +56,18 @@ def _check_forward(y, idx, yo, io, what):
     assert np.array_equal(_gpu.storage(y).view(np.uint8), yo.view(np.uint8)), "%s: y bits differ" % what
 
 
+@pytest.fixture(params=["any", "general"])
+def kernels(request, monkeypatch):
+    """'general' turns the small-tensor kernels off (MP3D_SMALL=0)."""
+    if request.param == "general":
+        monkeypatch.setenv("MP3D_SMALL", "0")
+    return request.param
+
+
 @pytest.mark.parametrize("index_dtype", [torch.int32, torch.int64], ids=["i32", "i64"])
 @pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
 @pytest.mark.parametrize("case", CASES, ids=_cid)
-def test_forward_backward_ex(orc, case, dtype, index_dtype):
+def test_forward_backward_ex(orc, case, dtype, index_dtype, kernels):
     shape, k, s, p, d, cm = case
     code = _gpu.CODE[dtype]
     base = abs(hash(case)) % 10000
