@@ -11,6 +11,14 @@
 // and no barrier: input rows shared by neighbouring output rows are re-read
 // from L1/L2, and blocks are mapped so that neighbouring blocks run on the
 // same XCD and share its L2.
+//
+// Padding of one position per side (PAD): a row index past an axis end is
+// clamped to the nearest row, which repeats that row next to itself in scan
+// order; along w the thread's span starts one column left of its vectors
+// (PW = 1) -- the left neighbour lane's last column, or at a row start a
+// copy of column 0.  A copy is equal to the element beside it and comes
+// first, so the first maximum is the same and, with its coordinates clamped
+// back into the axes, so is its position.
 #include "dtype.hpp"
 #include "kernels.hpp"
 
@@ -28,10 +36,10 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // half of a dword directly.  The scan carries the code dd << 4 | hh << 2 |
 // ww, small enough to be an inline constant of the select.  Returns false,
 // computing nothing, when a window holds a NaN.
-template <int KD, int KH, int KW, int SW, int SPAN, int V, int NQ, typename Rel>
-__device__ __forceinline__ bool f16_first_max(const uint32_t (&q)[KD][KH][NQ], Rel rel,
-                                              const uint16_t *__restrict__ xp, int32_t at0,
-                                              bool active, int32_t (&io)[V], uint16_t (&yo)[V])
+template <int KD, int KH, int KW, int SW, int SPAN, int V, int NQ, typename Pos>
+__device__ __forceinline__ bool f16_first_max(const uint32_t (&q)[KD][KH][NQ], Pos pos,
+                                              const uint16_t *__restrict__ xp, bool active,
+                                              int32_t (&io)[V], uint16_t (&yo)[V])
 {
     static_assert(KD <= 4 && KH <= 4 && KW <= 4, "window code fields are 2 bits");
     constexpr int KN = KD * KH * KW;
@@ -77,7 +85,7 @@ __device__ __forceinline__ bool f16_first_max(const uint32_t (&q)[KD][KH][NQ], R
     }
 #pragma unroll
     for (int o = 0; o < V; ++o) {
-        io[o] = at0 + o * SW + rel(c4[o] >> 4, (c4[o] >> 2) & 3, c4[o] & 3);
+        io[o] = pos(o, c4[o] >> 4, (c4[o] >> 2) & 3, c4[o] & 3);
         yo[o] = __builtin_bit_cast(uint16_t, mx[o]);
         // -0 and +0 compare equal, so c4 names the first zero; its sign comes
         // from the element itself (an L1/L2 hit)
@@ -113,20 +121,26 @@ __device__ __forceinline__ float scan_window(El el, int o, int &code)
 // Outputs are written with streaming stores: they leave the caches clean
 // for the kernels that follow (measured about 1 % faster over the whole
 // forward + backward sequence than cached stores).
-template <typename T, typename IT, int KD, int KH, int KW, int SD, int SH, int SW, int V>
+template <typename T, typename IT, int KD, int KH, int KW, int SD, int SH, int SW, int V, bool PAD,
+          int PW>
 __global__ void __launch_bounds__(kBlock)
 fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict__ y,
                  IT *__restrict__ idx, FixedPlan p)
 {
     using R = typename T::raw;
-    constexpr int SPAN = (V - 1) * SW + KW;      // input columns per thread
+    constexpr int SPAN = (V - 1) * SW + KW;      // input columns per thread (taps' span)
     constexpr int VE = 16 / (int)sizeof(R);      // elements per 16-byte vector
-    constexpr int NV = SPAN / VE;                // whole vectors per row
-    constexpr int NX = SPAN - NV * VE;           // columns past the last vector
+    constexpr int OWNC = SPAN - PW;              // span columns from the thread's own vectors
+    // PW = 1: whole vectors cover the own columns (no spill past them)
+    constexpr int NV = PW ? (OWNC + VE - 1) / VE : SPAN / VE;  // vectors per row
+    constexpr int NX = PW ? 0 : SPAN - NV * VE;  // columns past the last vector
     constexpr int NWAVE = kBlock / 64;
+    static_assert(PW == 0 || PW == 1, "one column of padding at most");
+    static_assert(PW == 0 || PAD, "column padding is padding");
+    static_assert(PW == 0 || NV * VE == V * SW, "the left lane's vectors end at its last column");
     static_assert(NX == 0 || V * SW == NV * VE, "the next group must hold the spill columns");
     static_assert(NX <= 4 / (int)sizeof(R), "the spill columns fit one dword");
-    const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X;
+    const int32_t D = p.g.ax[0].X, H = p.g.ax[1].X, W = p.g.ax[2].X;
     const int32_t OD = p.g.ax[0].O, OH = p.g.ax[1].O, OW = p.g.ax[2].O;
     const int32_t G = p.G;
     const int32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -154,14 +168,31 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
     const uint32_t plane = p.od.div(r2);
     const int32_t od = (int32_t)(r2 - plane * (uint32_t)OD);
     const int32_t ow0 = g * V;
-    const int32_t d0 = od * SD, h0 = oh * SH, w0 = ow0 * SW;
+    // first window's first tap row / column; w0 is where the thread's
+    // vectors start (16-byte aligned), PW columns right of its span start
+    const int32_t d0 = od * SD - (PAD ? p.pd : 0), h0 = oh * SH - (PAD ? p.ph : 0);
+    const int32_t w0 = ow0 * SW;
     const R *xp = x + (int64_t)plane * p.g.in_plane;
-    const R *base = xp + (d0 * H + h0) * W + w0;
+    // offsets of the KD*KH rows (clamped into the axes under padding)
+    int32_t roff[KD][KH];
+#pragma unroll
+    for (int dd = 0; dd < KD; ++dd)
+#pragma unroll
+        for (int hh = 0; hh < KH; ++hh) {
+            int32_t d = d0 + dd, h = h0 + hh;
+            if constexpr (PAD) {
+                d = min(max(d, 0), D - 1);
+                h = min(max(h, 0), H - 1);
+            }
+            roff[dd][hh] = (d * H + h) * W + w0;
+        }
 
-    // The thread's input rows as raw dwords, NQ per row; with NX > 0 the
-    // last dword of a row holds the spill columns.
+    // The thread's span as raw dwords, NQ per row: element j of a row is
+    // column w0 - PW + j.  With NX > 0 the last dword of a row holds the
+    // spill columns.
     constexpr int EPD = 4 / (int)sizeof(R);      // elements per dword
-    constexpr int NQ = NV * 4 + (NX > 0 ? 1 : 0);
+    constexpr int NQO = NV * 4;                  // dwords of the own vectors
+    constexpr int NQ = NQO + (PW || NX > 0 ? 1 : 0);
     uint32_t q[KD][KH][NQ];
     // every row's vector loads first, so that all of them are in flight
     // together (the spill handling below waits for them)
@@ -179,8 +210,9 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
             for (int hh = 0; hh < KH; ++hh)
 #pragma unroll
                 for (int j = 0; j < NV; ++j)
-                    vq[dd][hh][j] = *reinterpret_cast<const u32x4 *>(base + (dd * H + hh) * W + j * VE);
+                    vq[dd][hh][j] = *reinterpret_cast<const u32x4 *>(xp + roff[dd][hh] + j * VE);
     }
+    uint32_t own[KD][KH][NQO];
 #pragma unroll
     for (int dd = 0; dd < KD; ++dd) {
 #pragma unroll
@@ -188,10 +220,53 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const u32x4 t = vq[dd][hh][j];
-                q[dd][hh][4 * j] = t.x;
-                q[dd][hh][4 * j + 1] = t.y;
-                q[dd][hh][4 * j + 2] = t.z;
-                q[dd][hh][4 * j + 3] = t.w;
+                own[dd][hh][4 * j] = t.x;
+                own[dd][hh][4 * j + 1] = t.y;
+                own[dd][hh][4 * j + 2] = t.z;
+                own[dd][hh][4 * j + 3] = t.w;
+            }
+        }
+    }
+    if constexpr (PW == 0) {
+#pragma unroll
+        for (int dd = 0; dd < KD; ++dd)
+#pragma unroll
+            for (int hh = 0; hh < KH; ++hh)
+#pragma unroll
+                for (int j = 0; j < NQO; ++j) q[dd][hh][j] = own[dd][hh][j];
+    } else {
+        // column w0 - 1: the left lane's last column (the previous group of
+        // the same row), from memory when that group is in another wave,
+        // and padding -- a copy of column 0 -- at a row start
+        const bool row_start = g == 0;
+        const bool left_lane = !row_start && (p.rpw > 0 || lane != 0);
+        const bool left_mem = !row_start && !left_lane && active;
+#pragma unroll
+        for (int dd = 0; dd < KD; ++dd) {
+#pragma unroll
+            for (int hh = 0; hh < KH; ++hh) {
+                const uint32_t nb = __shfl_up(own[dd][hh][NQO - 1], 1);
+                uint32_t lw;                       // the left column in the top element of a dword
+                if constexpr (EPD == 1) {
+                    lw = left_lane ? nb : own[dd][hh][0];
+                    if (left_mem) lw = __builtin_bit_cast(uint32_t, xp[roff[dd][hh] - 1]);
+                } else {
+                    lw = left_lane ? nb : own[dd][hh][0] << 16;
+                    if (left_mem) lw = (uint32_t)xp[roff[dd][hh] - 1] << 16;
+                }
+                if constexpr (EPD == 1) {
+                    q[dd][hh][0] = lw;
+#pragma unroll
+                    for (int j = 0; j < NQO; ++j) q[dd][hh][j + 1] = own[dd][hh][j];
+                } else {
+                    // re-pair the columns one element later: dword i holds
+                    // span elements 2i, 2i + 1 = columns w0 - 1 + 2i, w0 + 2i
+                    q[dd][hh][0] = (own[dd][hh][0] << 16) | (lw >> 16);
+#pragma unroll
+                    for (int j = 1; j < NQO; ++j)
+                        q[dd][hh][j] = (own[dd][hh][j] << 16) | (own[dd][hh][j - 1] >> 16);
+                    q[dd][hh][NQO] = own[dd][hh][NQO - 1] >> 16;
+                }
             }
         }
     }
@@ -207,7 +282,7 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
                 const uint32_t nb = __shfl_down(q[dd][hh][0], 1);
                 uint32_t sp = from_lane ? nb : 0u;
                 if (from_mem) {
-                    const R *row_p = base + (dd * H + hh) * W;
+                    const R *row_p = xp + roff[dd][hh];
 #pragma unroll
                     for (int j = 0; j < NX; ++j) {
                         if (w0 + NV * VE + j < W) {
@@ -229,20 +304,29 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
         else return (R)(q[dd][hh][j / 2] >> (16 * (j % 2)));
     };
 
-    // offset of window element (dd, hh, ww) from the window's first element
-    auto rel = [&](int dd, int hh, int ww) { return (dd * H + hh) * W + ww; };
-    const int32_t at0 = (d0 * H + h0) * W + w0;
+    // plane position of element (dd, hh, ww) of output o's window, its
+    // coordinates clamped into the axes (a copy stands for the element it
+    // repeats)
+    auto pos = [&](int o, int dd, int hh, int ww) -> int32_t {
+        int32_t d = d0 + dd, h = h0 + hh, w = w0 - PW + o * SW + ww;
+        if constexpr (PAD) {
+            d = min(max(d, 0), D - 1);
+            h = min(max(h, 0), H - 1);
+            w = max(w, 0);
+        }
+        return (d * H + h) * W + w;
+    };
 
     R yo[V];
     int32_t io[V];
     bool done = false;
-    if constexpr (T::code == F16::code) done = f16_first_max<KD, KH, KW, SW, SPAN, V, NQ>(q, rel, xp, at0, active, io, yo);
+    if constexpr (T::code == F16::code) done = f16_first_max<KD, KH, KW, SW, SPAN, V, NQ>(q, pos, xp, active, io, yo);
     if (!done) {
 #pragma unroll
         for (int o = 0; o < V; ++o) {
             int code;
             const float best = scan_window<T, KD, KH, KW, SW>(el, o, code);
-            io[o] = at0 + o * SW + rel(code / (KH * KW), (code / KW) % KH, code % KW);
+            io[o] = pos(o, code / (KH * KW), (code / KW) % KH, code % KW);
             if (T::exact_nan || best == best || !active)
                 yo[o] = T::back(best);
             else
@@ -342,7 +426,7 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
     }
 }
 
-template <typename T, typename IT, int KD, int KH, int KW, int SD, int SH, int SW>
+template <typename T, typename IT, int KD, int KH, int KW, int SD, int SH, int SW, bool PAD, int PW>
 hipError_t launch_fixed(const void *x, void *y, IT *idx, const FixedPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
@@ -354,7 +438,7 @@ hipError_t launch_fixed(const void *x, void *y, IT *idx, const FixedPlan &p, hip
         grid = (uint32_t)((p.nthreads + kBlock - 1) / kBlock);
     }
     grid = (grid + 7u) & ~7u;
-    hipLaunchKernelGGL((fwd_fixed_kernel<T, IT, KD, KH, KW, SD, SH, SW, FixedPlan::V>), dim3(grid),
+    hipLaunchKernelGGL((fwd_fixed_kernel<T, IT, KD, KH, KW, SD, SH, SW, FixedPlan::V, PAD, PW>), dim3(grid),
                        dim3(kBlock), 0, s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
@@ -362,21 +446,35 @@ hipError_t launch_fixed(const void *x, void *y, IT *idx, const FixedPlan &p, hip
 }  // namespace
 
 // The window shapes with a compiled kernel: 2x2x2 / stride 2 and
-// 3x3x3 / stride 2, the two fixed-window workloads' shapes.
+// 3x3x3 / stride 2, the two fixed-window workloads' shapes, with no padding
+// or one position of padding per side (dilation 1).  Along w no tap of an
+// output may fall past the end (the kernel copies only the left padding);
+// along d and h the row clamp covers both ends.
 bool fixed_shape_supported(const Geom &g)
 {
     const Axis &a = g.ax[0], &b = g.ax[1], &c = g.ax[2];
-    if (!g.plain()) return false;          // no padding, every window inside the axes
     if (!a.k || a.k != b.k || a.k != c.k || a.s != b.s || a.s != c.s) return false;
-    return (a.k == 2 && a.s == 2) || (a.k == 3 && a.s == 2);
+    if (!((a.k == 2 && a.s == 2) || (a.k == 3 && a.s == 2))) return false;
+    for (int i = 0; i < 3; ++i)
+        if (g.ax[i].dil != 1 || g.ax[i].pad > 1) return false;
+    if (g.plain()) return true;
+    return (int64_t)(c.O - 1) * c.s - c.pad + c.k <= c.X;
+}
+
+template <typename T, typename IT, int K>
+hipError_t launch_fixed_k(const void *x, void *y, IT *idx, const FixedPlan &p, hipStream_t s)
+{
+    if (p.pw) return launch_fixed<T, IT, K, K, K, 2, 2, 2, true, 1>(x, y, idx, p, s);
+    if (p.pd || p.ph) return launch_fixed<T, IT, K, K, K, 2, 2, 2, true, 0>(x, y, idx, p, s);
+    return launch_fixed<T, IT, K, K, K, 2, 2, 2, false, 0>(x, y, idx, p, s);
 }
 
 template <typename T, typename IT>
 hipError_t launch_forward_fixed(const void *x, void *y, IT *idx, const FixedPlan &p,
                                 hipStream_t s)
 {
-    if (p.g.ax[0].k == 2) return launch_fixed<T, IT, 2, 2, 2, 2, 2, 2>(x, y, idx, p, s);
-    return launch_fixed<T, IT, 3, 3, 3, 2, 2, 2>(x, y, idx, p, s);
+    if (p.g.ax[0].k == 2) return launch_fixed_k<T, IT, 2>(x, y, idx, p, s);
+    return launch_fixed_k<T, IT, 3>(x, y, idx, p, s);
 }
 
 template hipError_t launch_forward_fixed<F32, int32_t>(const void *, void *, int32_t *, const FixedPlan &, hipStream_t);

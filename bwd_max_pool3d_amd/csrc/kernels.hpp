@@ -124,6 +124,7 @@ struct FixedPlan {
     int32_t rpw;               // whole rows per wave (0: rows may straddle waves)
     int32_t spill_load;        // some group loads its spill columns itself
     int32_t vec_store;         // outputs may be stored as 4-wide vectors
+    int32_t pd, ph, pw;        // padding per axis (0 or 1)
 };
 
 // Forward by axis: D-reduce in registers from coalesced column loads, then

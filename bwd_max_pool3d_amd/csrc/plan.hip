@@ -126,8 +126,13 @@ bool plan_fixed(const Geom &g, int es, const void *x, const void *y, const void 
     const int64_t ve = 16 / es;                     // elements per 16-byte vector
     const int64_t span = (V - 1) * c.s + c.k;       // input columns per thread
     const int64_t G = cdiv(c.O, V);
+    const int64_t pw = c.pad;
+    // vectors per row: with a left padding column the own vectors cover the
+    // rest of the span and end where the next group's start
+    const int64_t nv = pw ? cdiv(span - pw, ve) : span / ve;
     if ((W * es) % 16 || (uintptr_t)x % 16 || (V * c.s * es) % 16) return false;
-    if ((G - 1) * V * c.s + (span / ve) * ve > W) return false;   // vectors stay in the row
+    if (pw && nv * ve != V * c.s) return false;
+    if ((G - 1) * V * c.s + nv * ve > W) return false;   // vectors stay in the row
     const int64_t n = g.planes * g.ax[0].O * g.ax[1].O * G;
     if (n >= ((int64_t)1 << 31)) return false;
     p->g = g;
@@ -138,11 +143,15 @@ bool plan_fixed(const Geom &g, int es, const void *x, const void *y, const void 
     p->nthreads = (uint32_t)n;
     p->nrows = (uint32_t)(g.planes * g.ax[0].O * g.ax[1].O);
     p->vec_store = (c.O % V == 0) && ((uintptr_t)y % (V * es) == 0) && ((uintptr_t)idx % 16 == 0);
-    const bool spill = span % ve != 0;          // columns beyond the thread's vectors
-    // Windows that spill read the next group's columns across lanes: give
-    // each wave whole rows so that lane is in the same wave, and stage the
-    // wave's outputs to write them as vectors.
-    p->rpw = (spill && G <= 64 && (uintptr_t)y % 16 == 0 && (uintptr_t)idx % 16 == 0)
+    const bool spill = !pw && span % ve != 0;   // columns beyond the thread's vectors
+    p->pd = g.ax[0].pad;
+    p->ph = g.ax[1].pad;
+    p->pw = (int32_t)pw;
+    // Windows that spill read the next group's columns across lanes, and a
+    // left padding column the previous group's: give each wave whole rows
+    // so that lane is in the same wave, and stage the wave's outputs to
+    // write them as vectors.
+    p->rpw = ((spill || pw) && G <= 64 && (uintptr_t)y % 16 == 0 && (uintptr_t)idx % 16 == 0)
                  ? (int32_t)(64 / G) : 0;
     // the last group of a row needs its spill columns when its last output
     // exists; without whole rows per wave, lane 63 needs them too

@@ -35,6 +35,13 @@ CASES = [
     ((2, 1, 7, 9, 10), (3, 3, 3), (2, 2, 2), (0, 0, 0), (1, 1, 1), True),
     ((1, 2, 9, 17, 40), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), True),      # column kernel width
     ((1, 1, 6, 60, 64), (2, 2, 2), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),
+    # the row-vector kernel with padding: W a multiple of 8 and no tap past the row end
+    ((2, 3, 9, 12, 56), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),
+    ((1, 2, 10, 9, 40), (3, 3, 3), (2, 2, 2), (1, 0, 1), (1, 1, 1), False),
+    ((1, 2, 8, 10, 24), (3, 3, 3), (2, 2, 2), (1, 1, 0), (1, 1, 1), False),
+    ((1, 1, 6, 7, 48), (3, 3, 3), (2, 2, 2), (0, 1, 1), (1, 1, 1), True),
+    ((2, 1, 5, 6, 200), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),    # rows wider than a wave
+    ((1, 1, 5, 5, 16), (2, 2, 2), (2, 2, 2), (1, 1, 0), (1, 1, 1), True),
 ]
 
 
@@ -138,3 +145,36 @@ def test_int64_idx_out_of_range_ignored(orc):
         gx = mp.mp3d_backward_ex(gy, bad, shape, k, s, p, d, overlap=overlap)
         _gpu.check_backward(orc, gy.cpu(), torch.from_numpy(ref), shape, gx, exact=overlap == 2,
                             what="out-of-range int64 overlap=%d" % overlap)
+
+
+@pytest.mark.parametrize("name", ["fixed_bf16_k2s2", "fixed_f16_k3s2"])
+def test_padded_full_size(orc, name):
+    """The two fixed workloads with padding k // 2 on every axis, at full
+    size: y and idx against the oracle on sampled planes, and the backward
+    (accumulate and ordered) on the same planes."""
+    from bwd_max_pool3d_amd import workloads
+    wl = [w for w in workloads.WORKLOADS if w.name == name][0]
+    N, C, D, H, W = wl.shape
+    pad = tuple(k // 2 for k in wl.kernel)
+    x = wl.make_x()
+    xd = x.cuda()
+    y, idx = mp.mp3d_forward_ex(xd, wl.kernel, wl.stride, pad)
+    o3 = tuple(y.shape[2:])
+    gy = wl.make_gy(tuple(y.shape))
+    gyd = gy.cuda()
+    gx1 = mp.mp3d_backward_ex(gyd, idx, wl.shape, wl.kernel, wl.stride, pad)
+    gx2 = mp.mp3d_backward_ex(gyd, idx, wl.shape, wl.kernel, wl.stride, pad, overlap=2)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    P = N * C
+    for p in sorted({0, P - 1} | set(int(v) for v in rng.integers(0, P, size=6))):
+        n_, c_ = divmod(p, C)
+        sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
+        xs = _gpu.storage(x[sl].contiguous())
+        yo, io = orc.forward_ex(xs, _gpu.CODE[x.dtype], o3, wl.kernel, wl.stride, pad)
+        _check_forward(y[sl], idx[sl], yo, io, "%s padded plane %d" % (name, p))
+        i32 = idx[sl].cpu().contiguous()
+        for gx, exact in ((gx1, False), (gx2, True)):
+            _gpu.check_backward(orc, gy[sl].contiguous(), i32, (1, 1, D, H, W), gx[sl],
+                                exact=exact, what="%s padded plane %d" % (name, p))
+
