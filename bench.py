@@ -55,8 +55,9 @@ def kernel_source_hash() -> str:
     while it matches the hash they were measured at."""
     from bwd_max_pool3d_amd import _build
     h = hashlib.sha256()
-    for path in _build.sources() + [os.path.join(_build.CSRC, f) for f in
-                                    ("geometry.hpp", "dtype.hpp", "kernels.hpp")]:
+    headers = sorted(os.path.join(_build.CSRC, f) for f in os.listdir(_build.CSRC)
+                     if f.endswith(".hpp"))
+    for path in _build.sources() + headers:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
