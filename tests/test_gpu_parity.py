@@ -434,3 +434,67 @@ def test_float64_full_size(orc, wl):
                                 (1, 1, D, H, W), gx[sl], exact=exact,
                                 what="%s f64 plane %d" % (wl.name, p))
 
+
+def test_maximum_sizes(orc):
+    """Planes of 1026 x 1026 x 2040 = 2 147 459 040 elements, just under the
+    int32 index limit, three of them (6.4 G elements, past 2^31 in all),
+    bfloat16, 2 x 2 x 2 / 2 windows: the forward (int32 and int64 idx) on
+    sampled windows against the oracle, including the last windows of each
+    plane, with every element's idx checked to lie in its window and y to
+    be x there; the backward (gather, accumulate, ordered) exact on the same
+    windows and in total."""
+    shape = (3, 1, 1026, 1026, 2040)
+    N, C, D, H, W = shape
+    plane = D * H * W
+    assert plane < 2**31 and N * C * plane > 2**31
+    g = torch.Generator(device="cuda").manual_seed(41)
+    xd = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    y, idx = mp.mp3d_forward(xd, 2, 2)
+    y64, i64 = mp.mp3d_forward(xd, 2, 2, index_dtype=torch.int64)
+    OD, OH, OW = y.shape[2:]
+    assert torch.equal(i64, idx.to(torch.int64))
+    assert torch.equal(y64.view(torch.int16), y.view(torch.int16))
+    del y64, i64
+    # every output: idx inside its window, y the element there (a plane at a time)
+    o = torch.arange(OD * OH * OW, device="cuda", dtype=torch.int64)
+    od, oh, ow = o // (OH * OW), (o // OW) % OH, o % OW
+    for n in range(N):
+        ii = idx[n].reshape(-1).to(torch.int64)
+        d, h, w = ii // (H * W), (ii // W) % H, ii % W
+        assert bool(((d // 2 == od) & (h // 2 == oh) & (w // 2 == ow)).all()), n
+        xv = xd[n].reshape(-1).view(torch.int16)
+        assert torch.equal(xv[ii], y[n].reshape(-1).view(torch.int16)), n
+        del ii, d, h, w
+    del o, od, oh, ow
+    # sampled windows (with the last ones) against the oracle
+    rng = np.random.default_rng(42)
+    picks = [(n, OD - 1, OH - 1, OW - 1) for n in range(N)] + [
+        (int(rng.integers(N)), int(rng.integers(OD)), int(rng.integers(OH)), int(rng.integers(OW)))
+        for _ in range(60)]
+    gy = torch.randn(y.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    gxs = {ov: mp.mp3d_backward(gy, idx, shape, kernel=2, stride=2, overlap=ov) for ov in (0, 1, 2)}
+    for n, a, b, c in picks:
+        blk = xd[n:n + 1, :, 2 * a:2 * a + 2, 2 * b:2 * b + 2, 2 * c:2 * c + 2].contiguous().cpu()
+        yo, io = orc.forward(_gpu.storage(blk), 2, (1, 1, 1), (2, 2, 2), (2, 2, 2))
+        bd, brem = divmod(int(io.reshape(-1)[0]), 4)
+        bh, bw = divmod(brem, 2)
+        want = ((2 * a + bd) * H + 2 * b + bh) * W + 2 * c + bw
+        assert int(idx[n, 0, a, b, c]) == want, (n, a, b, c)
+        assert _gpu.storage(y[n:n + 1, :, a:a + 1, b:b + 1, c:c + 1]).view(np.uint16)[0, 0, 0, 0, 0] \
+            == yo.view(np.uint16).reshape(-1)[0]
+        gblk = gy[n:n + 1, :, a:a + 1, b:b + 1, c:c + 1].contiguous().cpu()
+        r = orc.backward(_gpu.storage(gblk), io, 2, (1, 1, 2, 2, 2))
+        for ov, gx in gxs.items():
+            got = _gpu.storage(gx[n:n + 1, :, 2 * a:2 * a + 2, 2 * b:2 * b + 2, 2 * c:2 * c + 2]
+                               .contiguous())
+            assert np.array_equal(got.view(np.uint16), r["gx"].view(np.uint16)), (ov, n, a, b, c)
+    # windows tile: gx is +0 + gy at each argmax and +0 elsewhere, on every path
+    for n in range(N):
+        want = (gy[n].float() + 0.0).to(torch.bfloat16).reshape(-1).view(torch.int16)
+        ii = idx[n].reshape(-1).to(torch.int64)
+        for ov, gx in gxs.items():
+            gv = gx[n].reshape(-1).view(torch.int16)
+            assert torch.equal(gv[ii], want), (ov, n)
+            assert int(gv.ne(0).sum()) == int(want.ne(0).sum()), (ov, n)
+        del want, ii
+
