@@ -18,9 +18,10 @@
 //    h, w window, then the smallest key d << 24 | (h * W + w) among the
 //    partials equal to it: the smallest d, then the first (h, w) in scan
 //    order, which is the first maximum in (d, h, w) order.
-// Both stages find a maximum first (IEEE 754-2019 maximum, NaN when an
-// operand is NaN) and its first position second; windows holding a NaN take
-// the first NaN instead, on a path of their own.
+// Stage D finds a maximum first (IEEE 754-2019 maximum, NaN when an operand
+// is NaN) and its first slot second; stage HW keeps the running maximum and
+// the smallest key among the elements equal to it in one pass, and the
+// smallest key among NaNs apart (a window holding a NaN takes its first NaN).
 #include "dtype.hpp"
 #include "kernels.hpp"
 
@@ -150,28 +151,23 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         const int2 wh = tab[oh], ww = tab[B.O + ow];
         const float *sv = pv + odl * HW;
         const uint8_t *sd = pd + odl * HW;
+        // one pass: the running maximum and the smallest key among the
+        // elements equal to it; NaNs tracked apart (the first NaN wins)
         float m = sv[wh.x * W + ww.x];
+        uint32_t bk = 0xffffffffu, nk = 0xffffffffu;
         for (int32_t h = wh.x; h < wh.y; ++h) {
 #pragma unroll 4
-            for (int32_t w = ww.x; w < ww.y; ++w) m = __builtin_elementwise_maximum(m, sv[h * W + w]);
-        }
-        uint32_t bk = 0xffffffffu;
-        if (m == m) {
-            for (int32_t h = wh.x; h < wh.y; ++h) {
-#pragma unroll 4
-                for (int32_t w = ww.x; w < ww.y; ++w) {
-                    const int32_t i = h * W + w;
-                    bk = min(bk, sv[i] == m ? ((uint32_t)sd[i] << 24) | (uint32_t)i : 0xffffffffu);
-                }
-            }
-        } else {
-            for (int32_t h = wh.x; h < wh.y; ++h) {
-                for (int32_t w = ww.x; w < ww.y; ++w) {
-                    const int32_t i = h * W + w;
-                    bk = min(bk, sv[i] != sv[i] ? ((uint32_t)sd[i] << 24) | (uint32_t)i : 0xffffffffu);
-                }
+            for (int32_t w = ww.x; w < ww.y; ++w) {
+                const int32_t i = h * W + w;
+                const float v = sv[i];
+                const uint32_t k = ((uint32_t)sd[i] << 24) | (uint32_t)i;
+                const bool gt = v > m;
+                bk = gt ? k : (v == m ? min(bk, k) : bk);
+                m = gt ? v : m;
+                nk = v != v ? min(nk, k) : nk;
             }
         }
+        if (nk != 0xffffffffu) bk = nk;
         const int32_t bi = (int32_t)(bk & 0xffffffu);
         const int32_t pos = (A.start(od0 + (int32_t)odl) + (int32_t)(bk >> 24)) * HW + bi;
         const float best = sv[bi];        // the element itself: keeps the sign of a zero
