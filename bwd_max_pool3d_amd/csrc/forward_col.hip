@@ -9,15 +9,16 @@
 // A workgroup owns one plane and a run of output slices od.  The reduction
 // is split by axis so that every memory access is coalesced:
 //  stage D (registers): thread i owns the 16-byte column groups i,
-//    i + 256, ... of the H*W slice.  For each od it loads the window's
+//    i + NT, ... of the H*W slice (NT threads: 256, or 512 when the tile's
+//    D-partials need much LDS and few workgroups fit on a CU).  For each od it loads the window's
 //    slices of its column (the next window's loads are issued before the
 //    current window is reduced; a slice shared by two windows is read
 //    twice, the second time from L2), and reduces them element-wise to the
 //    first maximum over d, written to LDS as the value and its d offset.
-//  stage HW (LDS): each output takes the maximum of the D-partials over its
-//    h, w window, then the smallest key d << 24 | (h * W + w) among the
-//    partials equal to it: the smallest d, then the first (h, w) in scan
-//    order, which is the first maximum in (d, h, w) order.
+//  stage HW (LDS): each output scans the D-partials of its h, w window once,
+//    keeping the running maximum and the smallest key d << 24 | (h * W + w)
+//    among the partials equal to it: the smallest d, then the first (h, w)
+//    in scan order, which is the first maximum in (d, h, w) order.
 // Stage D finds a maximum first (IEEE 754-2019 maximum, NaN when an operand
 // is NaN) and its first slot second; stage HW keeps the running maximum and
 // the smallest key among the elements equal to it in one pass, and the
