@@ -26,8 +26,14 @@ workload (no index written), the forward with int64 indices, the fixed
 workloads with padding k//2 (forward and backward), the ordered backward
 (overlap=2), the index-free backward (argmax recomputed from x and y) and
 float64 forward and backward of the two large overlapping workloads are
-timed the same way, apart from the step, and reported on their own (median
-per op: launched one op at a time, an event pair can catch a host stall).
+timed the same way, apart from the step, each launch after an untimed read
+of a 512 MiB buffer that leaves the caches clean, and reported on their own
+(median per op: launched one op at a time, an event pair can catch a host
+stall).
+
+Beside the GPU figures, the CPU oracle is timed on the same workloads
+(``cpu_baseline``: one thread; ``cpu_baseline_threads``: the host's CPUs, up
+to 16, each thread running the unchanged oracle on a range of planes).
 
 Prints ONE JSON line.  ``--gpus`` above 1 is refused: this path runs on one
 GPU (planes shard across GPUs with no communication, so more GPUs are not
@@ -182,10 +188,27 @@ def build_ops(torch, mp, workloads, variants=True):
     return fwd_ops + bwd_ops, (vo_ops + exf_ops + ord_ops + exb_ops) if variants else []
 
 
-def cpu_baseline(target_s: float):
-    """The CPU oracle, single-threaded, on the same fraction of every
-    workload's planes (so the byte mix matches the GPU step), sized to
-    about ``target_s`` seconds."""
+_CPU_INPUTS: dict = {}     # seeded workload tensors, drawn once for both oracle runs
+
+
+def host_threads() -> int:
+    """Host threads for the multi-threaded oracle run: the CPUs this process
+    may use, at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(target_s: float, threads: int = 1):
+    """The CPU oracle on the same fraction of every workload's planes (so
+    the byte mix matches the GPU step), sized to about ``target_s`` seconds.
+    With ``threads`` > 1 the planes are split into that many contiguous
+    ranges, each run by the unchanged oracle on a thread of its own (the
+    ctypes call releases the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
     import oracle
@@ -193,6 +216,7 @@ def cpu_baseline(target_s: float):
 
     orc = oracle.get()
     code = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    pool = ThreadPoolExecutor(threads) if threads > 1 else None
 
     def storage(t):
         t = t.contiguous()
@@ -200,12 +224,21 @@ def cpu_baseline(target_s: float):
             return t.numpy()
         return t.view(torch.int16).numpy().view(np.uint16)
 
-    cache = {}
+    cache = _CPU_INPUTS
 
     def draw(wl, kind, shape=None):
         if (wl.name, kind) not in cache:
             cache[(wl.name, kind)] = wl.make_x() if kind == "x" else wl.make_gy(shape)
         return cache[(wl.name, kind)]
+
+    def ranges(n):
+        cuts = np.linspace(0, n, min(threads, n) + 1).astype(int)
+        return [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:])]
+
+    def each(fn, parts):
+        if pool is None:
+            return [fn(*q) for q in parts]
+        return list(pool.map(lambda q: fn(*q), parts))
 
     def run(frac):
         total_bytes = 0
@@ -225,28 +258,34 @@ def cpu_baseline(target_s: float):
                 o3 = tuple(orc.fixed_out(X, ka, sa) for X, ka, sa in zip(wl.shape[2:], k, s))
             es = x.element_size()
             xs = storage(x)
+            parts = ranges(np_)
             t0 = time.perf_counter()
-            y, idx = orc.forward(xs, c, o3, k, s)
+            fw = each(lambda a, b: orc.forward(xs[a:b], c, o3, k, s), parts)
             elapsed += time.perf_counter() - t0
-            nin, nout = xs.size, y.size
+            nin, nout = xs.size, sum(y.size for y, _ in fw)
             total_bytes += nin * es + nout * (es + 4)
             if wl.backward:
                 gy = draw(wl, "gy", (P, 1) + o3)[:np_].contiguous()
                 gys = storage(gy)
+                jobs = [(a, b, fw[j][1]) for j, (a, b) in enumerate(parts)]
                 t0 = time.perf_counter()
-                orc.backward(gys, idx, c, (np_, 1, D, H, W), side=False)
+                each(lambda a, b, idx: orc.backward(gys[a:b], idx, c, (b - a, 1, D, H, W),
+                                                    side=False), jobs)
                 elapsed += time.perf_counter() - t0
                 total_bytes += nout * (es + 4) + nin * es
         return total_bytes, elapsed, planes_used
 
-    probe = 1.0 / 512
+    probe = 1.0 / 512 * threads
     b, t, _ = run(probe)
     frac = min(1.0, probe * target_s / max(t, 1e-3))
     b, t, used = run(frac)
-    return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "plain C oracle, one thread, forward+backward on %.4f of each "
+    if pool is not None:
+        pool.shutdown()
+    who = "one thread" if threads == 1 else "%d threads over contiguous plane ranges" % threads
+    return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "plain C oracle, %s, forward+backward on %.4f of each "
                       "workload's planes (%s): %.3g GB of algorithmic bytes in %.1f s"
-                      % (frac, ", ".join(used), b / 1e9, t)}
+                      % (who, frac, ", ".join(used), b / 1e9, t)}
 
 
 def main():
@@ -346,7 +385,12 @@ def main():
             op.ms.append(e0.elapsed_time(e1))
     print("[bench] timed %d steps with per-op events" % args.steps, file=sys.stderr, flush=True)
 
-    # Variants (not part of the step): same events, K times each.
+    # Variants (not part of the step): same events, K times each.  Each
+    # launch is preceded by an untimed read of a 512 MiB buffer: it writes
+    # back whatever the previous variant left dirty in L2 and the 256 MB
+    # memory-side cache and leaves clean lines, so a variant's time does not
+    # depend on which variant ran before it.
+    flush_buf = torch.ones(1 << 27, dtype=torch.float32, device="cuda") if vo_ops else None
     for op in vo_ops:
         op.fn()
     vo_evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -354,10 +398,12 @@ def main():
     torch.cuda.synchronize()
     for step in range(args.steps):
         for op, (e0, e1) in zip(vo_ops, vo_evs[step]):
+            flush_buf.sum()
             e0.record(stream)
             op.fn()
             e1.record(stream)
     torch.cuda.synchronize()
+    del flush_buf
     for step in range(args.steps):
         for op, (e0, e1) in zip(vo_ops, vo_evs[step]):
             op.ms.append(e0.elapsed_time(e1))
@@ -418,8 +464,12 @@ def main():
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        nt = host_threads()
+        result["cpu_baseline_threads"] = (cpu_baseline(args.cpu_seconds / 2, nt)
+                                          if nt > 1 else None)
     else:
         result["cpu_baseline"] = None
+        result["cpu_baseline_threads"] = None
     print(json.dumps(result), flush=True)
 
 
