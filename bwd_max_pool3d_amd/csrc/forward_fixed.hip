@@ -16,9 +16,13 @@
 // clamped to the nearest row, which repeats that row next to itself in scan
 // order; along w the thread's span starts one column left of its vectors
 // (PW = 1) -- the left neighbour lane's last column, or at a row start a
-// copy of column 0.  A copy is equal to the element beside it and comes
-// first, so the first maximum is the same and, with its coordinates clamped
-// back into the axes, so is its position.
+// copy of column 0.  When the last windows of a row reach past its end, the
+// row's last group has its vectors wholly past the row (the plan admits no
+// other case): it loads nothing and its span holds copies of the row's last
+// column, its left column.  A copy is equal to the element it repeats and
+// sits beside it on the far side from the window's first tap, so the first
+// maximum is the same and, with its coordinates clamped back into the axes,
+// so is its position.
 #include "dtype.hpp"
 #include "kernels.hpp"
 
@@ -203,7 +207,10 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
         for (int hh = 0; hh < KH; ++hh)
 #pragma unroll
             for (int j = 0; j < NV; ++j) vq[dd][hh][j] = u32x4{0u, 0u, 0u, 0u};
-    if (active) {                         // idle lanes load nothing and scan zeros
+    // idle lanes, and a group whose vectors lie past the row end, load
+    // nothing (the latter's columns are filled in below)
+    const bool own_in = w0 < W;
+    if (active && own_in) {
 #pragma unroll
         for (int dd = 0; dd < KD; ++dd)
 #pragma unroll
@@ -253,6 +260,13 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
                 } else {
                     lw = left_lane ? nb : own[dd][hh][0] << 16;
                     if (left_mem) lw = (uint32_t)xp[roff[dd][hh] - 1] << 16;
+                }
+                if (!own_in) {
+                    // right padding: every own column is a copy of the left
+                    // column, the row's last
+                    const uint32_t c = EPD == 1 ? lw : ((lw & 0xffff0000u) | (lw >> 16));
+#pragma unroll
+                    for (int j = 0; j < NQO; ++j) own[dd][hh][j] = c;
                 }
                 if constexpr (EPD == 1) {
                     q[dd][hh][0] = lw;
@@ -312,7 +326,7 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
         if constexpr (PAD) {
             d = min(max(d, 0), D - 1);
             h = min(max(h, 0), H - 1);
-            w = max(w, 0);
+            w = min(max(w, 0), W - 1);
         }
         return (d * H + h) * W + w;
     };
@@ -447,9 +461,10 @@ hipError_t launch_fixed(const void *x, void *y, IT *idx, const FixedPlan &p, hip
 
 // The window shapes with a compiled kernel: 2x2x2 / stride 2 and
 // 3x3x3 / stride 2, the two fixed-window workloads' shapes, with no padding
-// or one position of padding per side (dilation 1).  Along w no tap of an
-// output may fall past the end (the kernel copies only the left padding);
-// along d and h the row clamp covers both ends.
+// or one position of padding per side (dilation 1).  Along w a tap past the
+// end needs the padding column of that axis (the plan then checks that the
+// row's last group lies wholly past the end); along d and h the row clamp
+// covers both ends.
 bool fixed_shape_supported(const Geom &g)
 {
     const Axis &a = g.ax[0], &b = g.ax[1], &c = g.ax[2];
@@ -458,14 +473,17 @@ bool fixed_shape_supported(const Geom &g)
     for (int i = 0; i < 3; ++i)
         if (g.ax[i].dil != 1 || g.ax[i].pad > 1) return false;
     if (g.plain()) return true;
-    return (int64_t)(c.O - 1) * c.s - c.pad + c.k <= c.X;
+    return c.pad == 1 || (int64_t)(c.O - 1) * c.s - c.pad + c.k <= c.X;
 }
 
 template <typename T, typename IT, int K>
 hipError_t launch_fixed_k(const void *x, void *y, IT *idx, const FixedPlan &p, hipStream_t s)
 {
     if (p.pw) return launch_fixed<T, IT, K, K, K, 2, 2, 2, true, 1>(x, y, idx, p, s);
-    if (p.pd || p.ph) return launch_fixed<T, IT, K, K, K, 2, 2, 2, true, 0>(x, y, idx, p, s);
+    // the row clamp serves padding on d or h, and also a last window past
+    // the end of d or h without padding (ceil-mode extents)
+    if (p.pd || p.ph || !p.g.plain())
+        return launch_fixed<T, IT, K, K, K, 2, 2, 2, true, 0>(x, y, idx, p, s);
     return launch_fixed<T, IT, K, K, K, 2, 2, 2, false, 0>(x, y, idx, p, s);
 }
 

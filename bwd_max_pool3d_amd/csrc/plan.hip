@@ -132,7 +132,12 @@ bool plan_fixed(const Geom &g, int es, const void *x, const void *y, const void 
     const int64_t nv = pw ? cdiv(span - pw, ve) : span / ve;
     if ((W * es) % 16 || (uintptr_t)x % 16 || (V * c.s * es) % 16) return false;
     if (pw && nv * ve != V * c.s) return false;
-    if ((G - 1) * V * c.s + nv * ve > W) return false;   // vectors stay in the row
+    // vectors stay in the row, but for the last group under a padding column
+    // when it starts exactly at the row end (its columns are all padding)
+    const int64_t last = (G - 1) * V * c.s;
+    if (last + nv * ve > W && !(pw && last == W)) return false;
+    // without the padding column no tap may fall past the row end
+    if (!pw && (c.O - 1) * c.s - c.pad + c.k > W) return false;
     const int64_t n = g.planes * g.ax[0].O * g.ax[1].O * G;
     if (n >= ((int64_t)1 << 31)) return false;
     p->g = g;

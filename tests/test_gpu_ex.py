@@ -42,6 +42,16 @@ CASES = [
     ((1, 1, 6, 7, 48), (3, 3, 3), (2, 2, 2), (0, 1, 1), (1, 1, 1), True),
     ((2, 1, 5, 6, 200), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),    # rows wider than a wave
     ((1, 1, 5, 5, 16), (2, 2, 2), (2, 2, 2), (1, 1, 0), (1, 1, 1), True),
+    # the row-vector kernel, no padding, a last window past the end of d or h
+    # (ceil mode): rows clamped
+    ((1, 1, 7, 8, 16), (2, 2, 2), (2, 2, 2), (0, 0, 0), (1, 1, 1), True),
+    ((1, 2, 6, 7, 24), (2, 2, 2), (2, 2, 2), (0, 0, 0), (1, 1, 1), True),
+    # the row-vector kernel with taps in the right padding of w: the row's
+    # last group lies past the row end
+    ((2, 2, 6, 5, 16), (2, 2, 2), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),
+    ((1, 2, 5, 6, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), True),      # two columns past
+    ((1, 2, 4, 6, 200), (2, 2, 2), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),    # two rows per wave
+    ((1, 1, 3, 4, 520), (2, 2, 2), (2, 2, 2), (1, 1, 1), (1, 1, 1), False),    # rows across waves
 ]
 
 
