@@ -11,7 +11,8 @@
 //    coalesced store per element.
 //  * bwd_slab / bwd_box: when windows overlap several outputs may land on
 //    one input.  Each workgroup owns a box of one plane's gx (whole slices
-//    when they fit), zero-fills a binary32 accumulator for it in LDS, adds
+//    when they fit), zero-fills an accumulator for it in LDS (binary32;
+//    binary64 for the float64 dtype), adds
 //    every gy whose idx falls in the box with an LDS compare-and-swap loop,
 //    then rounds and stores the box once.  The zero fill, the atomic
 //    scatter and the cast of the page's scheme all happen on-chip, so HBM
@@ -30,11 +31,12 @@ namespace mp3d {
 
 namespace {
 
-// Pack VE rounded accumulator values into one 16-byte store.
+// Pack VE rounded accumulator values into one 16-byte store (binary32 and
+// binary64 cells are stored as they are).
 template <typename T>
-__device__ __forceinline__ u32x4 pack16(const float *a)
+__device__ __forceinline__ u32x4 pack16(const typename T::acc *a)
 {
-    if constexpr (sizeof(typename T::raw) == 4) {
+    if constexpr (sizeof(typename T::raw) == sizeof(typename T::acc)) {
         return *reinterpret_cast<const u32x4 *>(a);
     } else {
         const float4 u = *reinterpret_cast<const float4 *>(a);
@@ -85,7 +87,7 @@ constexpr int kSlabBlock = kSlabThreads;  // threads per slab workgroup
 // for the unaligned head and tail.  a[e] and dst[e] share their alignment
 // modulo one 16-byte vector.
 template <typename T, int NT>
-__device__ __forceinline__ void store_span(typename T::raw *dst, const float *a, int32_t n,
+__device__ __forceinline__ void store_span(typename T::raw *dst, const typename T::acc *a, int32_t n,
                                            int32_t head)
 {
     constexpr int VE = 16 / (int)sizeof(typename T::raw);
@@ -127,8 +129,11 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
                 typename T::raw *__restrict__ gx, BwdPlan p)
 {
     using R = typename T::raw;
+    using Acc = typename T::acc;
     constexpr int VE = 16 / (int)sizeof(R);
-    extern __shared__ __align__(16) float acc[];
+    constexpr int AE = 16 / (int)sizeof(Acc);   // accumulator cells per 16 bytes
+    extern __shared__ __align__(16) unsigned char smem[];
+    Acc *acc = reinterpret_cast<Acc *>(smem);
     const Axis A = p.g.ax[0];
     const int32_t HW = p.g.ax[1].X * p.g.ax[2].X;
     const int32_t OHW = p.g.ax[1].O * p.g.ax[2].O;
@@ -150,8 +155,8 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
     // the accumulator is shifted so that a[e] and dst[e] share alignment
     const int32_t mis = (int32_t)(((uintptr_t)dst / sizeof(R)) % VE);
     const int32_t head = min((VE - mis) % VE, n);
-    const int32_t shift = (4 - head % 4) % 4;
-    float *a = acc + shift;
+    const int32_t shift = (AE - head % AE) % AE;
+    Acc *a = acc + shift;
 
     int32_t ri[kRound];
     R rg[kRound];
@@ -167,7 +172,7 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
         }
     };
     fetch(0);                                   // in flight during the zero fill
-    for (int32_t e = tid; e < (n + shift + 3) / 4; e += NT)
+    for (int32_t e = tid; e < (n + shift + AE - 1) / AE; e += NT)
         reinterpret_cast<u32x4 *>(acc)[e] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     if constexpr (ORD) {
@@ -303,21 +308,23 @@ hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const 
 {
     using R = typename T::raw;
     int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)1 << 24);
-    if constexpr (sizeof(typename T::acc) == 4) {   // the slab packs binary32 cells
-        if (p.slab) {
-            // one workgroup per slab; a multiple of 8 lets blocks map per XCD
-            // (the surplus blocks exit at once)
-            if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
-            if (p.nphase)
+    if (p.slab) {
+        // one workgroup per slab; a multiple of 8 lets blocks map per XCD
+        // (the surplus blocks exit at once).  The ordered slab is binary32
+        // only (the plan gives binary64 cells no phases).
+        if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
+        if constexpr (sizeof(typename T::acc) == 4) {
+            if (p.nphase) {
                 hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kOrdThreads, true, kOrdRound>),
                                    dim3((uint32_t)grid), dim3(kOrdThreads), p.lds_bytes, s,
                                    (const R *)gy, src, (R *)gx, p);
-            else
-                hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kSlabBlock, false, Src::kSlots>),
-                                   dim3((uint32_t)grid), dim3(kSlabBlock), p.lds_bytes, s,
-                                   (const R *)gy, src, (R *)gx, p);
-            return hipGetLastError();
+                return hipGetLastError();
+            }
         }
+        hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kSlabBlock, false, Src::kSlots>),
+                           dim3((uint32_t)grid), dim3(kSlabBlock), p.lds_bytes, s,
+                           (const R *)gy, src, (R *)gx, p);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((bwd_box_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
                        (const R *)gy, src, (R *)gx, p);

@@ -104,6 +104,11 @@ struct F64 {
     __device__ static inline double widen(double r) { return r; }
     __device__ static inline double narrow(double f) { return f; }
     __device__ static inline double back(double f) { return f; }
+    // the two elements of a 16-byte vector
+    __device__ static inline void unpack(u32x4 q, double *v) {
+        v[0] = __builtin_bit_cast(double, (uint64_t)q.x | ((uint64_t)q.y << 32));
+        v[1] = __builtin_bit_cast(double, (uint64_t)q.z | ((uint64_t)q.w << 32));
+    }
 };
 
 }  // namespace mp3d

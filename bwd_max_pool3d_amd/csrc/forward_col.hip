@@ -52,22 +52,23 @@ __device__ __forceinline__ void col_load(ColWin<MAXKD> &w, const R *__restrict__
 // Element-wise first maximum over the window's slots: writes the values and
 // the winning slot (the d offset in the window) to LDS.
 template <typename T, int MAXKD>
-__device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, float *pv, uint8_t *pd)
+__device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, typename T::acc *pv, uint8_t *pd)
 {
+    using A = typename T::acc;
     constexpr int VE = 16 / (int)sizeof(typename T::raw);
-    float v[MAXKD][VE];
+    A v[MAXKD][VE];
 #pragma unroll
     for (int j = 0; j < MAXKD; ++j) T::unpack(w.q[j], v[j]);
 #pragma unroll
     for (int i = 0; i < VE; ++i) {
-        float m = v[0][i];
+        A m = v[0][i];
 #pragma unroll
         for (int j = 1; j < MAXKD; ++j) m = __builtin_elementwise_maximum(m, v[j][i]);
         // the first slot equal to the maximum (the first NaN when it is
         // NaN), found from the last slot back; the value is taken from the
         // slot itself, which keeps the sign of a zero and a NaN's bits
         int32_t jd = MAXKD - 1;
-        float val = v[MAXKD - 1][i];
+        A val = v[MAXKD - 1][i];
         if (m == m) {
 #pragma unroll
             for (int j = MAXKD - 2; j >= 0; --j) {
@@ -94,6 +95,7 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
                IT *__restrict__ idx, ColPlan p)
 {
     using R = typename T::raw;
+    using Acc = typename T::acc;
     constexpr int VE = 16 / (int)sizeof(R);
     extern __shared__ __align__(16) unsigned char smem[];
     const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
@@ -102,7 +104,7 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
 
     // LDS: window table (oh then ow) | D-partial values | D-partial d offsets
     int2 *tab = reinterpret_cast<int2 *>(smem);
-    float *pv = reinterpret_cast<float *>(smem + p.tab_bytes);
+    Acc *pv = reinterpret_cast<Acc *>(smem + p.tab_bytes);
     uint8_t *pd = reinterpret_cast<uint8_t *>(smem + p.tab_bytes + p.pv_bytes);
 
     const uint32_t t = xcd_local_block(blockIdx.x, gridDim.x);
@@ -150,17 +152,17 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         const uint32_t odl = p.oh_div.div(q);
         const int32_t oh = (int32_t)(q - odl * (uint32_t)B.O);
         const int2 wh = tab[oh], ww = tab[B.O + ow];
-        const float *sv = pv + odl * HW;
+        const Acc *sv = pv + odl * HW;
         const uint8_t *sd = pd + odl * HW;
         // one pass: the running maximum and the smallest key among the
         // elements equal to it; NaNs tracked apart (the first NaN wins)
-        float m = sv[wh.x * W + ww.x];
+        Acc m = sv[wh.x * W + ww.x];
         uint32_t bk = 0xffffffffu, nk = 0xffffffffu;
         for (int32_t h = wh.x; h < wh.y; ++h) {
 #pragma unroll 4
             for (int32_t w = ww.x; w < ww.y; ++w) {
                 const int32_t i = h * W + w;
-                const float v = sv[i];
+                const Acc v = sv[i];
                 const uint32_t k = ((uint32_t)sd[i] << 24) | (uint32_t)i;
                 const bool gt = v > m;
                 bk = gt ? k : (v == m ? min(bk, k) : bk);
@@ -171,7 +173,7 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         if (nk != 0xffffffffu) bk = nk;
         const int32_t bi = (int32_t)(bk & 0xffffffu);
         const int32_t pos = (A.start(od0 + (int32_t)odl) + (int32_t)(bk >> 24)) * HW + bi;
-        const float best = sv[bi];        // the element itself: keeps the sign of a zero
+        const Acc best = sv[bi];          // the element itself: keeps the sign of a zero
         R raw;
         if (T::exact_nan || best == best)
             raw = T::back(best);
@@ -211,5 +213,7 @@ template hipError_t launch_forward_col<BF16, int32_t>(const void *, void *, int3
 template hipError_t launch_forward_col<F32, int64_t>(const void *, void *, int64_t *, const ColPlan &, hipStream_t);
 template hipError_t launch_forward_col<F16, int64_t>(const void *, void *, int64_t *, const ColPlan &, hipStream_t);
 template hipError_t launch_forward_col<BF16, int64_t>(const void *, void *, int64_t *, const ColPlan &, hipStream_t);
+template hipError_t launch_forward_col<F64, int32_t>(const void *, void *, int32_t *, const ColPlan &, hipStream_t);
+template hipError_t launch_forward_col<F64, int64_t>(const void *, void *, int64_t *, const ColPlan &, hipStream_t);
 
 }  // namespace mp3d

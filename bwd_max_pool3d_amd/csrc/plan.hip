@@ -181,8 +181,10 @@ bool plan_col(const Geom &g, int es, const void *x, ColPlan *p)
     const int64_t cap = std::min<int64_t>(kLdsCap, (int64_t)lds_limit());
     const int64_t tab = ((int64_t)(B.O + Cw.O) * 8 + 15) & ~(int64_t)15;
     if (tab > 16 * 1024) return false;
-    // per output slice: D-partial value + d offset
-    const int64_t per_slice = HW * 5 + 16;
+    // per output slice: D-partial value (binary32, or binary64 for float64)
+    // + d offset
+    const int64_t ab = es == 8 ? 8 : 4;
+    const int64_t per_slice = HW * (ab + 1) + 16;
     int32_t tod = (int32_t)std::min<int64_t>(A.O, (cap - tab) / per_slice);
     if (tod < 1) return false;
     const int64_t per_plane = cdiv(kWantTiles, std::max<int64_t>(g.planes, 1));
@@ -201,7 +203,7 @@ bool plan_col(const Geom &g, int es, const void *x, ColPlan *p)
     p->ntiles = (uint32_t)ntiles;
     p->maxkd = (int32_t)maxkd;
     p->tab_bytes = (uint32_t)tab;
-    p->pv_bytes = (uint32_t)(((int64_t)tod * HW * 4 + 15) & ~(int64_t)15);
+    p->pv_bytes = (uint32_t)(((int64_t)tod * HW * ab + 15) & ~(int64_t)15);
     p->lds_bytes = (uint32_t)(tab + p->pv_bytes + (int64_t)tod * HW);
     return true;
 }
@@ -289,8 +291,7 @@ bool plan_backward(const Geom &g, bool ordered, int cell_bytes, BwdPlan *p)
     const int64_t budget = std::min<int64_t>(ordered ? kOrdBudget : kAccBudget,
                                              (int64_t)lds_limit() - 64);
     const int64_t cb = cell_bytes;
-    // binary64 cells: boxes only (the slab kernel packs binary32 cells),
-    // and no ordered slab
+    // binary64 cells: no ordered slab (its phases add binary32 cells)
     if (cb != 4 && ordered) return false;
     const int64_t slice = (int64_t)H * W * cb;
     p->g = g;
@@ -346,7 +347,7 @@ bool plan_backward(const Geom &g, bool ordered, int cell_bytes, BwdPlan *p)
     p->ntw = (int32_t)cdiv(W, p->tw);
     p->ntiles = g.planes * p->ntd * p->nth * p->ntw;
     p->split = TileSplit::make(g.planes, p->ntd, p->nth, p->ntw);
-    p->slab = p->th == H && p->tw == W && cb == 4;
+    p->slab = p->th == H && p->tw == W;
     // + alignment shift and the rounding of the zero fill to 16 bytes
     p->lds_bytes = (uint32_t)(((int64_t)p->td * p->th * p->tw + 8) * cb);
     return true;
