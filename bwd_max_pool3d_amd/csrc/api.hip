@@ -279,6 +279,17 @@ int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPat
         }
     }
     const bool ordered = path == BwdPath::ordered;
+    if constexpr (!is_array_src<Src>::value) {
+        // index-free, any order: the column stages recompute the argmax
+        RcPlan rp;
+        if (!ordered && plan_rc(g, (int)sizeof(typename T::raw), (int)sizeof(typename T::acc),
+                                src.x, &rp)) {
+            if (log_enabled())
+                fprintf(stderr, "[mp3d] backward index-free column dtype=%d slab=%d tiles=%u lds=%u\n",
+                        T::code, rp.td, rp.ntiles, rp.lds_bytes);
+            return hip_status(launch_backward_rc<T>(gy, gx, rp, src, s), "backward index-free launch");
+        }
+    }
     BwdPlan p;
     if (plan_backward(g, ordered, (int)sizeof(typename T::acc), &p)) {
         if (log_enabled())

@@ -23,6 +23,7 @@
 #include <algorithm>
 #include <climits>
 
+#include "colstage.hpp"
 #include "dtype.hpp"
 #include "idxsrc.hpp"
 #include "kernels.hpp"
@@ -227,6 +228,128 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
     store_span<T, NT>(dst, a, n, head);
 }
 
+// Index-free backward by column stages: a slab [d0, d1) of whole slices of
+// one plane.  The argmax of window o is the first tap equal to y[o] (the
+// first NaN when y[o] is NaN).  The column forward's two stages give every
+// window reaching the slab its first maximum (the first NaN when it holds
+// one); where that element equals y[o], every tap equal to y[o] is a
+// maximum, so the first of them is that element.  Elsewhere -- y not the
+// window's maximum -- the window is scanned in memory (fb).  The LDS that
+// held the D-partials then becomes the slab's accumulator, as in the slab
+// kernel.
+//
+// The fallback scan is a plain loop over the window's in-range taps (one
+// load at a time): it runs only where y is not the window's maximum, and
+// adds few registers to those of the common path.
+template <typename T>
+__device__ __forceinline__ int32_t rc_scan(const typename T::raw *xp, const Geom &g,
+                                                     int32_t od, int32_t oh, int32_t ow,
+                                                     typename T::acc want)
+{
+    const Taps td = window_taps(g.ax[0], od), th = window_taps(g.ax[1], oh);
+    const Taps tw = window_taps(g.ax[2], ow);
+    const int32_t H = g.ax[1].X, W = g.ax[2].X;
+    const bool nan = want != want;
+    for (int32_t a = td.j0; a <= td.j1; ++a)
+        for (int32_t b = th.j0; b <= th.j1; ++b) {
+            const int32_t row = ((td.b + a * td.t) * H + th.b + b * th.t) * W + tw.b;
+            for (int32_t c = tw.j0; c <= tw.j1; ++c) {
+                const typename T::acc v = T::widen(xp[row + c * tw.t]);
+                if (nan ? v != v : v == want) return row + c * tw.t;
+            }
+        }
+    return -1;
+}
+
+template <typename T, int MAXKD, int NT, int KS>
+__global__ void __launch_bounds__(NT)
+bwd_rc_kernel(const typename T::raw *__restrict__ gy, typename T::raw *__restrict__ gx, RcPlan p,
+              IdxRecompute<T> fb)
+{
+    using R = typename T::raw;
+    using Acc = typename T::acc;
+    constexpr int VE = 16 / (int)sizeof(R);
+    constexpr int AE = 16 / (int)sizeof(Acc);
+    extern __shared__ __align__(16) unsigned char smem[];
+    const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
+    const int32_t W = Cw.X, HW = B.X * W, OHW = B.O * Cw.O;
+    const int32_t tid = threadIdx.x;
+    int2 *tab = reinterpret_cast<int2 *>(smem);          // window spans: oh, then ow
+    unsigned char *region = smem + p.tab_bytes;          // D-partials, then the accumulator
+
+    const uint32_t t = xcd_local_block(blockIdx.x, gridDim.x);
+    if (t >= p.ntiles) return;                           // whole workgroup: no barrier skipped
+    const uint32_t plane = p.ntd_div.div(t);
+    const int32_t sd = (int32_t)(t - plane * (uint32_t)p.ntd);
+    const int32_t d0 = sd * p.td, d1 = min(d0 + p.td, A.X);
+    const int32_t n = (d1 - d0) * HW;
+    const int32_t od0 = A.first_reaching(d0);
+    const int32_t cd = max(A.last_starting(d1 - 1) + 1 - od0, 0);
+    const int32_t nwin = cd * OHW;                       // <= KS * NT (the plan)
+    const int64_t obase = (int64_t)plane * p.g.out_plane + (int64_t)od0 * OHW;
+    const R *xp = fb.x + (int64_t)plane * p.g.in_plane;
+
+    // y and gy of the windows, in flight during stage D
+    R ry[KS], rg[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int32_t e = k * NT + tid;
+        ry[k] = R{};
+        rg[k] = R{};
+        if (e < nwin) {
+            ry[k] = fb.y[obase + e];
+            rg[k] = gy[obase + e];
+        }
+    }
+    for (int32_t j = tid; j < B.O + Cw.O; j += NT)
+        tab[j] = j < B.O ? make_int2(B.start(j), B.end(j))
+                         : make_int2(Cw.start(j - B.O), Cw.end(j - B.O));
+    Acc *pv = reinterpret_cast<Acc *>(region);
+    uint8_t *pd = region + (((int64_t)cd * HW * (int64_t)sizeof(Acc) + 15) & ~(int64_t)15);
+    col_stage_d<T, MAXKD, NT>(xp, A, HW, od0, cd, pv, pd);
+    __syncthreads();
+
+    int32_t ri[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int32_t e = k * NT + tid;
+        ri[k] = -1;
+        if (e < nwin) {
+            const uint32_t q = p.ow_div.div((uint32_t)e);
+            const int32_t ow = e - (int32_t)q * Cw.O;
+            const uint32_t odl = p.oh_div.div(q);
+            const int32_t oh = (int32_t)(q - odl * (uint32_t)B.O);
+            Acc m;
+            const uint32_t bk = col_scan(pv + odl * HW, pd + odl * HW, W, tab[oh], tab[B.O + ow], m);
+            const int32_t bi = (int32_t)(bk & 0xffffffu);
+            const Acc best = pv[odl * HW + bi];          // NaN exactly when bk names a NaN
+            const Acc want = T::widen(ry[k]);
+            const bool same = want != want ? best != best : best == want;
+            ri[k] = same ? (A.start(od0 + (int32_t)odl) + (int32_t)(bk >> 24)) * HW + bi
+                         : rc_scan<T>(xp, p.g, od0 + (int32_t)odl, oh, ow, want);
+        }
+    }
+    __syncthreads();                                     // the D-partials are consumed
+
+    R *dst = gx + (int64_t)plane * p.g.in_plane + (int64_t)d0 * HW;
+    // the accumulator is shifted so that a[e] and dst[e] share alignment
+    const int32_t mis = (int32_t)(((uintptr_t)dst / sizeof(R)) % VE);
+    const int32_t head = min((VE - mis) % VE, n);
+    const int32_t shift = (AE - head % AE) % AE;
+    Acc *a = reinterpret_cast<Acc *>(region) + shift;
+    for (int32_t e = tid; e < (n + shift + AE - 1) / AE; e += NT)
+        reinterpret_cast<u32x4 *>(region)[e] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    const uint32_t ibase = (uint32_t)d0 * (uint32_t)HW;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const uint32_t l = (uint32_t)ri[k] - ibase;
+        if (ri[k] >= 0 && l < (uint32_t)n) lds_add(&a[l], T::widen(rg[k]));
+    }
+    __syncthreads();
+    store_span<T, NT>(dst, a, n, head);
+}
+
 // General boxes [d0,d1) x [h0,h1) x [w0,w1) (a slice does not fit in LDS).
 template <typename T, typename Src>
 __global__ void __launch_bounds__(kBlock)
@@ -331,6 +454,33 @@ hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const 
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_backward_rc(const void *gy, void *gx, const RcPlan &p, const IdxRecompute<T> &fb,
+                              hipStream_t s)
+{
+    using R = typename T::raw;
+    uint32_t grid = p.ntiles;
+    if (grid >= 64) grid = (grid + 7u) & ~7u;            // blocks map per XCD; the surplus exits
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), p.lds_bytes, s, (const R *)gy, (R *)gx,
+                           p, fb);
+    };
+    // window slots per thread: the fewest of 1, 2, 4, 8 that hold the
+    // windows reaching a slab
+    if (p.maxkd <= 4) {
+        if (p.slots <= 1) go(bwd_rc_kernel<T, 4, kBlock, 1>);
+        else if (p.slots <= 2) go(bwd_rc_kernel<T, 4, kBlock, 2>);
+        else if (p.slots <= 4) go(bwd_rc_kernel<T, 4, kBlock, 4>);
+        else go(bwd_rc_kernel<T, 4, kBlock, 8>);
+    } else {
+        if (p.slots <= 1) go(bwd_rc_kernel<T, 8, kBlock, 1>);
+        else if (p.slots <= 2) go(bwd_rc_kernel<T, 8, kBlock, 2>);
+        else if (p.slots <= 4) go(bwd_rc_kernel<T, 8, kBlock, 4>);
+        else go(bwd_rc_kernel<T, 8, kBlock, 8>);
+    }
+    return hipGetLastError();
+}
+
 template <typename T, typename Src>
 hipError_t launch_backward_gather(const void *gy, const Src &src, void *gx, const GatherPlan &p,
                                   hipStream_t s)
@@ -356,6 +506,10 @@ template hipError_t launch_backward_tile<BF16, IdxRecompute<BF16>>(const void *,
 template hipError_t launch_backward_tile<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F64, IdxRecompute<F64>>(const void *, const IdxRecompute<F64> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_rc<F32>(const void *, void *, const RcPlan &, const IdxRecompute<F32> &, hipStream_t);
+template hipError_t launch_backward_rc<F16>(const void *, void *, const RcPlan &, const IdxRecompute<F16> &, hipStream_t);
+template hipError_t launch_backward_rc<BF16>(const void *, void *, const RcPlan &, const IdxRecompute<BF16> &, hipStream_t);
+template hipError_t launch_backward_rc<F64>(const void *, void *, const RcPlan &, const IdxRecompute<F64> &, hipStream_t);
 template hipError_t launch_backward_gather<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);
 template hipError_t launch_backward_gather<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const GatherPlan &, hipStream_t);
 template hipError_t launch_backward_gather<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);

@@ -1,0 +1,142 @@
+// colstage.hpp -- the two stages of the column forward, shared by the
+// forward (forward_col.hip) and the index-free backward, which recomputes
+// each window's first maximum the same way (backward.hip).
+//
+// Definition ("Struct Maxpool3dForward", teenygrad, description; PR #308
+// page, Summary): per window, the first maximum in d, h, w scan order, NaN
+// ranking above every number.
+//  stage D (registers): a thread owns 16-byte column groups of an H*W
+//    slice; for each output slice od it loads the window's slices of its
+//    column group and reduces them element-wise to the first maximum over d
+//    (IEEE 754-2019 maximum first, NaN when an operand is NaN, then its
+//    first slot), written to LDS as the value and its d offset.
+//  stage HW (LDS): a window scans the D-partials of its h, w span once,
+//    keeping the running maximum and the smallest key d << 24 | (h * W + w)
+//    among the partials equal to it (the smallest d, then the first (h, w):
+//    the first maximum in d, h, w order), and the smallest key among NaNs
+//    apart (a window holding a NaN takes its first NaN).
+#pragma once
+
+#include "dtype.hpp"
+#include "kernels.hpp"
+
+namespace mp3d {
+
+// One window's slices of one column group: slot j holds slice ds + j for
+// j < n and repeats slice ds + n - 1 beyond.  The loads carry no branch, so
+// that every load of a tile is in flight at once; a repeated slice never
+// comes first among equal values.  Plain (cached) loads: a slice shared by
+// two neighbouring windows is served from L2 the second time.
+template <int MAXKD>
+struct ColWin {
+    u32x4 q[MAXKD];
+};
+
+template <typename R, int MAXKD>
+__device__ __forceinline__ void col_load(ColWin<MAXKD> &w, const R *__restrict__ col, int32_t hw,
+                                         int32_t n)
+{
+#pragma unroll
+    for (int j = 0; j < MAXKD; ++j)
+        w.q[j] = *reinterpret_cast<const u32x4 *>(col + (int64_t)min(j, n - 1) * hw);
+}
+
+// Element-wise first maximum over the window's slots: writes the values and
+// the winning slot (the d offset in the window) to LDS.
+template <typename T, int MAXKD>
+__device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, typename T::acc *pv, uint8_t *pd)
+{
+    using A = typename T::acc;
+    constexpr int VE = 16 / (int)sizeof(typename T::raw);
+    A v[MAXKD][VE];
+#pragma unroll
+    for (int j = 0; j < MAXKD; ++j) T::unpack(w.q[j], v[j]);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) {
+        A m = v[0][i];
+#pragma unroll
+        for (int j = 1; j < MAXKD; ++j) m = __builtin_elementwise_maximum(m, v[j][i]);
+        // the first slot equal to the maximum (the first NaN when it is
+        // NaN), found from the last slot back; the value is taken from the
+        // slot itself, which keeps the sign of a zero and a NaN's bits
+        int32_t jd = MAXKD - 1;
+        A val = v[MAXKD - 1][i];
+        if (m == m) {
+#pragma unroll
+            for (int j = MAXKD - 2; j >= 0; --j) {
+                const bool hit = v[j][i] == m;
+                jd = hit ? j : jd;
+                val = hit ? v[j][i] : val;
+            }
+        } else {
+#pragma unroll
+            for (int j = MAXKD - 2; j >= 0; --j) {
+                const bool hit = v[j][i] != v[j][i];
+                jd = hit ? j : jd;
+                val = hit ? v[j][i] : val;
+            }
+        }
+        pv[i] = val;
+        pd[i] = (uint8_t)jd;
+    }
+}
+
+// Stage D for output slices [od0, od0 + cd) of one plane (xp): the
+// D-partials of slice odl go to pv / pd + odl * HW.  The loads of two
+// windows are in flight while the previous one is reduced; a slice shared
+// by two windows is read twice, the second time from L2.
+template <typename T, int MAXKD, int NT>
+__device__ __forceinline__ void col_stage_d(const typename T::raw *__restrict__ xp, const Axis &A,
+                                            int32_t HW, int32_t od0, int32_t cd,
+                                            typename T::acc *pv, uint8_t *pd)
+{
+    using R = typename T::raw;
+    constexpr int VE = 16 / (int)sizeof(R);
+    const int32_t ngroups = HW / VE;
+    for (int32_t gi = (int32_t)threadIdx.x; gi < ngroups; gi += NT) {
+        const R *col = xp + gi * VE;
+        ColWin<MAXKD> wa, wb;
+        int32_t ds = A.start(od0);
+        col_load<R, MAXKD>(wa, col + (int64_t)ds * HW, HW, A.end(od0) - ds);
+        for (int32_t odl = 0; odl < cd; odl += 2) {
+            if (odl + 1 < cd) {
+                ds = A.start(od0 + odl + 1);
+                col_load<R, MAXKD>(wb, col + (int64_t)ds * HW, HW, A.end(od0 + odl + 1) - ds);
+            }
+            col_reduce<T, MAXKD>(wa, pv + odl * HW + gi * VE, pd + odl * HW + gi * VE);
+            if (odl + 2 < cd) {
+                ds = A.start(od0 + odl + 2);
+                col_load<R, MAXKD>(wa, col + (int64_t)ds * HW, HW, A.end(od0 + odl + 2) - ds);
+            }
+            if (odl + 1 < cd)
+                col_reduce<T, MAXKD>(wb, pv + (odl + 1) * HW + gi * VE, pd + (odl + 1) * HW + gi * VE);
+        }
+    }
+}
+
+// Stage HW for one window: rows [wh.x, wh.y), columns [ww.x, ww.y) of one
+// slice's D-partials (sv values, sd d offsets).  Returns the key of the
+// first maximum (the first NaN when there is one) and sets m to the
+// maximum.
+template <typename Acc>
+__device__ __forceinline__ uint32_t col_scan(const Acc *sv, const uint8_t *sd, int32_t W, int2 wh,
+                                             int2 ww, Acc &m)
+{
+    m = sv[wh.x * W + ww.x];
+    uint32_t bk = 0xffffffffu, nk = 0xffffffffu;
+    for (int32_t h = wh.x; h < wh.y; ++h) {
+#pragma unroll 4
+        for (int32_t w = ww.x; w < ww.y; ++w) {
+            const int32_t i = h * W + w;
+            const Acc v = sv[i];
+            const uint32_t k = ((uint32_t)sd[i] << 24) | (uint32_t)i;
+            const bool gt = v > m;
+            bk = gt ? k : (v == m ? min(bk, k) : bk);
+            m = gt ? v : m;
+            nk = v != v ? min(nk, k) : nk;
+        }
+    }
+    return nk != 0xffffffffu ? nk : bk;
+}
+
+}  // namespace mp3d

@@ -6,88 +6,18 @@
 // teenygrad, description; PR #308 page, Summary): per window, the first
 // maximum in d, h, w scan order, NaN ranking above every number.
 //
-// A workgroup owns one plane and a run of output slices od.  The reduction
-// is split by axis so that every memory access is coalesced:
-//  stage D (registers): thread i owns the 16-byte column groups i,
-//    i + NT, ... of the H*W slice (NT threads: 256, or 512 when the tile's
-//    D-partials need much LDS and few workgroups fit on a CU).  For each od it loads the window's
-//    slices of its column (the next window's loads are issued before the
-//    current window is reduced; a slice shared by two windows is read
-//    twice, the second time from L2), and reduces them element-wise to the
-//    first maximum over d, written to LDS as the value and its d offset.
-//  stage HW (LDS): each output scans the D-partials of its h, w window once,
-//    keeping the running maximum and the smallest key d << 24 | (h * W + w)
-//    among the partials equal to it: the smallest d, then the first (h, w)
-//    in scan order, which is the first maximum in (d, h, w) order.
-// Stage D finds a maximum first (IEEE 754-2019 maximum, NaN when an operand
-// is NaN) and its first slot second; stage HW keeps the running maximum and
-// the smallest key among the elements equal to it in one pass, and the
-// smallest key among NaNs apart (a window holding a NaN takes its first NaN).
+// A workgroup owns one plane and a run of output slices od, and computes
+// every window's first maximum with the two stages of colstage.hpp: the
+// D-reduce in registers from coalesced 16-byte column loads, then one scan
+// per window over the D-partials in LDS.  NT threads: 256, or 512 when the
+// tile's D-partials need much LDS and few workgroups fit on a CU.
+#include "colstage.hpp"
 #include "dtype.hpp"
 #include "kernels.hpp"
 
 namespace mp3d {
 
 namespace {
-
-// One window's slices of one column group: slot j holds slice ds + j for
-// j < n and repeats slice ds + n - 1 beyond.  The loads carry no branch, so
-// that every load of a tile is in flight at once; a repeated slice never
-// comes first among equal values.  Plain (cached) loads: a slice shared by
-// two neighbouring windows is served from L2 the second time.
-template <int MAXKD>
-struct ColWin {
-    u32x4 q[MAXKD];
-};
-
-template <typename R, int MAXKD>
-__device__ __forceinline__ void col_load(ColWin<MAXKD> &w, const R *__restrict__ col, int32_t hw,
-                                         int32_t n)
-{
-#pragma unroll
-    for (int j = 0; j < MAXKD; ++j)
-        w.q[j] = *reinterpret_cast<const u32x4 *>(col + (int64_t)min(j, n - 1) * hw);
-}
-
-// Element-wise first maximum over the window's slots: writes the values and
-// the winning slot (the d offset in the window) to LDS.
-template <typename T, int MAXKD>
-__device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, typename T::acc *pv, uint8_t *pd)
-{
-    using A = typename T::acc;
-    constexpr int VE = 16 / (int)sizeof(typename T::raw);
-    A v[MAXKD][VE];
-#pragma unroll
-    for (int j = 0; j < MAXKD; ++j) T::unpack(w.q[j], v[j]);
-#pragma unroll
-    for (int i = 0; i < VE; ++i) {
-        A m = v[0][i];
-#pragma unroll
-        for (int j = 1; j < MAXKD; ++j) m = __builtin_elementwise_maximum(m, v[j][i]);
-        // the first slot equal to the maximum (the first NaN when it is
-        // NaN), found from the last slot back; the value is taken from the
-        // slot itself, which keeps the sign of a zero and a NaN's bits
-        int32_t jd = MAXKD - 1;
-        A val = v[MAXKD - 1][i];
-        if (m == m) {
-#pragma unroll
-            for (int j = MAXKD - 2; j >= 0; --j) {
-                const bool hit = v[j][i] == m;
-                jd = hit ? j : jd;
-                val = hit ? v[j][i] : val;
-            }
-        } else {
-#pragma unroll
-            for (int j = MAXKD - 2; j >= 0; --j) {
-                const bool hit = v[j][i] != v[j][i];
-                jd = hit ? j : jd;
-                val = hit ? v[j][i] : val;
-            }
-        }
-        pv[i] = val;
-        pd[i] = (uint8_t)jd;
-    }
-}
 
 template <typename T, typename IT, int MAXKD, int NT>
 __global__ void __launch_bounds__(NT)
@@ -96,7 +26,6 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
 {
     using R = typename T::raw;
     using Acc = typename T::acc;
-    constexpr int VE = 16 / (int)sizeof(R);
     extern __shared__ __align__(16) unsigned char smem[];
     const Axis A = p.g.ax[0], B = p.g.ax[1], Cw = p.g.ax[2];
     const int32_t H = B.X, W = Cw.X, HW = H * W;
@@ -118,28 +47,7 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         tab[j] = j < B.O ? make_int2(B.start(j), B.end(j))
                          : make_int2(Cw.start(j - B.O), Cw.end(j - B.O));
 
-    // stage D: the loads of two windows in flight while the previous one
-    // is reduced
-    const int32_t ngroups = HW / VE;
-    for (int32_t gi = tid; gi < ngroups; gi += NT) {
-        const R *col = xp + gi * VE;
-        ColWin<MAXKD> wa, wb;
-        int32_t ds = A.start(od0);
-        col_load<R, MAXKD>(wa, col + (int64_t)ds * HW, HW, A.end(od0) - ds);
-        for (int32_t odl = 0; odl < cd; odl += 2) {
-            if (odl + 1 < cd) {
-                ds = A.start(od0 + odl + 1);
-                col_load<R, MAXKD>(wb, col + (int64_t)ds * HW, HW, A.end(od0 + odl + 1) - ds);
-            }
-            col_reduce<T, MAXKD>(wa, pv + odl * HW + gi * VE, pd + odl * HW + gi * VE);
-            if (odl + 2 < cd) {
-                ds = A.start(od0 + odl + 2);
-                col_load<R, MAXKD>(wa, col + (int64_t)ds * HW, HW, A.end(od0 + odl + 2) - ds);
-            }
-            if (odl + 1 < cd)
-                col_reduce<T, MAXKD>(wb, pv + (odl + 1) * HW + gi * VE, pd + (odl + 1) * HW + gi * VE);
-        }
-    }
+    col_stage_d<T, MAXKD, NT>(xp, A, HW, od0, cd, pv, pd);
     __syncthreads();
 
     // stage HW
@@ -151,26 +59,9 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         const int32_t ow = e - (int32_t)q * Cw.O;
         const uint32_t odl = p.oh_div.div(q);
         const int32_t oh = (int32_t)(q - odl * (uint32_t)B.O);
-        const int2 wh = tab[oh], ww = tab[B.O + ow];
         const Acc *sv = pv + odl * HW;
-        const uint8_t *sd = pd + odl * HW;
-        // one pass: the running maximum and the smallest key among the
-        // elements equal to it; NaNs tracked apart (the first NaN wins)
-        Acc m = sv[wh.x * W + ww.x];
-        uint32_t bk = 0xffffffffu, nk = 0xffffffffu;
-        for (int32_t h = wh.x; h < wh.y; ++h) {
-#pragma unroll 4
-            for (int32_t w = ww.x; w < ww.y; ++w) {
-                const int32_t i = h * W + w;
-                const Acc v = sv[i];
-                const uint32_t k = ((uint32_t)sd[i] << 24) | (uint32_t)i;
-                const bool gt = v > m;
-                bk = gt ? k : (v == m ? min(bk, k) : bk);
-                m = gt ? v : m;
-                nk = v != v ? min(nk, k) : nk;
-            }
-        }
-        if (nk != 0xffffffffu) bk = nk;
+        Acc m;
+        const uint32_t bk = col_scan(sv, pd + odl * HW, W, tab[oh], tab[B.O + ow], m);
         const int32_t bi = (int32_t)(bk & 0xffffffu);
         const int32_t pos = (A.start(od0 + (int32_t)odl) + (int32_t)(bk >> 24)) * HW + bi;
         const Acc best = sv[bi];          // the element itself: keeps the sign of a zero

@@ -76,6 +76,24 @@ constexpr int kColBigThreads = 512;
 constexpr int kOrdRound = 8;               // ordered slab: windows per thread (one round)
 constexpr int kMaxPhase = 64;              // ordered slab: at most this many phases
 
+// Index-free backward by column stages (backward.hip): each workgroup owns
+// a slab of whole slices [d0, d0 + td) of one plane's gx.  It recomputes the
+// first maximum of every window reaching the slab with the column forward's
+// two stages, takes it as the argmax where it equals y[o] (else scans the
+// window in memory), then reuses the same LDS as the slab's accumulator.
+constexpr int kRcSlots = 8;                // at most this many windows per thread (one round)
+struct RcPlan {
+    Geom g;
+    int32_t td, ntd;           // slices per slab, slabs per plane
+    FastDiv ntd_div;
+    uint32_t ntiles;           // planes * ntd
+    int32_t maxkd;             // widest window along D
+    FastDiv ow_div, oh_div;    // window number in the slab -> (odl, oh, ow)
+    uint32_t tab_bytes;        // LDS: window table, 16-byte aligned
+    uint32_t lds_bytes;        // table + the larger of D-partials and accumulator
+    int32_t slots;             // windows per thread: most windows reaching a slab / threads
+};
+
 // General forward (forward_ex.hip): one thread per output, any geometry.
 struct ExPlan {
     Geom g;
@@ -167,6 +185,8 @@ bool plan_backward(const Geom &g, bool ordered, int cell_bytes, BwdPlan *p);
 bool plan_small_forward(const Geom &g, SmallPlan *p);
 bool plan_small_backward(const Geom &g, SmallPlan *p);
 void plan_ordered(const Geom &g, OrdPlan *p);
+// es: storage element bytes; acc_bytes: accumulator cell bytes
+bool plan_rc(const Geom &g, int es, int acc_bytes, const void *x, RcPlan *p);
 void plan_ex(const Geom &g, ExPlan *p);
 int64_t max_taps(const Axis &a);         // most taps of one window on the axis
 

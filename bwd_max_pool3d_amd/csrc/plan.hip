@@ -353,6 +353,63 @@ bool plan_backward(const Geom &g, bool ordered, int cell_bytes, BwdPlan *p)
     return true;
 }
 
+bool plan_rc(const Geom &g, int es, int ab, const void *x, RcPlan *p)
+{
+    const Axis &A = g.ax[0], &B = g.ax[1], &Cw = g.ax[2];
+    if (!g.contiguous() || A.X > 4096) return false;
+    const int64_t HW = (int64_t)B.X * Cw.X;
+    // the column stages: 16-byte column groups, keys of 24 bits, windows at
+    // most 8 wide along D
+    if ((HW * es) % 16 || (uintptr_t)x % 16 || HW >= ((int64_t)1 << 24)) return false;
+    const int64_t maxkd = A.k ? A.k : axis_widest(A);
+    if (maxkd > 8) return false;
+    const int64_t ohw = (int64_t)B.O * Cw.O;
+    const int64_t tab = ((int64_t)(B.O + Cw.O) * 8 + 15) & ~(int64_t)15;
+    if (tab > 16 * 1024) return false;
+    const int64_t budget = std::min<int64_t>(kAccBudget, (int64_t)lds_limit() - 64 - tab);
+    auto r16 = [](int64_t b) { return (b + 15) & ~(int64_t)15; };
+    // LDS of slabs of td slices: the larger of the D-partials of the output
+    // slices reaching a slab (value + d offset) and the slab's accumulator
+    // (+ alignment shift); 0 when some slab's windows exceed one round
+    int64_t cdmax = 0;
+    auto region = [&](int32_t td) -> int64_t {
+        cdmax = 0;
+        for (int32_t d0 = 0; d0 < A.X; d0 += td) {
+            const int32_t d1 = std::min(d0 + td, A.X);
+            const int64_t cd = (int64_t)A.last_starting(d1 - 1) + 1 - A.first_reaching(d0);
+            cdmax = std::max(cdmax, cd);
+        }
+        if (cdmax * ohw > (int64_t)kRcSlots * kBlock) return 0;
+        return std::max(r16(cdmax * HW * ab) + cdmax * HW, r16(((int64_t)td * HW + 8) * ab));
+    };
+    const int64_t per_plane = cdiv(kWantTiles, std::max<int64_t>(g.planes, 1));
+    int32_t td = (int32_t)std::min<int64_t>(A.X, std::max<int64_t>(1, A.X / per_plane));
+    int64_t rb = 0;
+    for (; td >= 1; --td) {
+        rb = region(td);
+        if (rb > 0 && rb <= budget) break;
+    }
+    if (td < 1) return false;
+    // even slabs: fewer slices per slab never need more LDS
+    td = (int32_t)cdiv(A.X, cdiv(A.X, td));
+    rb = region(td);
+    if (rb <= 0 || rb > budget) return false;
+    const int64_t ntd = cdiv(A.X, td);
+    if (g.planes * ntd >= ((int64_t)1 << 31)) return false;
+    p->g = g;
+    p->td = td;
+    p->ntd = (int32_t)ntd;
+    p->ntd_div = FastDiv((uint32_t)ntd);
+    p->ntiles = (uint32_t)(g.planes * ntd);
+    p->maxkd = (int32_t)maxkd;
+    p->ow_div = FastDiv((uint32_t)Cw.O);
+    p->oh_div = FastDiv((uint32_t)B.O);
+    p->tab_bytes = (uint32_t)tab;
+    p->lds_bytes = (uint32_t)(tab + rb);
+    p->slots = (int32_t)cdiv(cdmax * ohw, kBlock);
+    return true;
+}
+
 int64_t max_taps(const Axis &a)
 {
     return a.k ? (int64_t)a.k : axis_widest(a);
