@@ -261,7 +261,7 @@ __device__ __forceinline__ int32_t rc_scan(const typename T::raw *xp, const Geom
     return -1;
 }
 
-template <typename T, int MAXKD, int NT, int KS>
+template <typename T, int MAXKD, int NT, int KS, int KHW>
 __global__ void __launch_bounds__(NT)
 bwd_rc_kernel(const typename T::raw *__restrict__ gy, typename T::raw *__restrict__ gx, RcPlan p,
               IdxRecompute<T> fb)
@@ -320,7 +320,11 @@ bwd_rc_kernel(const typename T::raw *__restrict__ gy, typename T::raw *__restric
             const uint32_t odl = p.oh_div.div(q);
             const int32_t oh = (int32_t)(q - odl * (uint32_t)B.O);
             Acc m;
-            const uint32_t bk = col_scan(pv + odl * HW, pd + odl * HW, W, tab[oh], tab[B.O + ow], m);
+            uint32_t bk;
+            if constexpr (KHW > 0)
+                bk = col_scan_k<KHW>(pv + odl * HW, pd + odl * HW, W, tab[oh], tab[B.O + ow], m);
+            else
+                bk = col_scan(pv + odl * HW, pd + odl * HW, W, tab[oh], tab[B.O + ow], m);
             const int32_t bi = (int32_t)(bk & 0xffffffu);
             const Acc best = pv[odl * HW + bi];          // NaN exactly when bk names a NaN
             const Acc want = T::widen(ry[k]);
@@ -467,17 +471,23 @@ hipError_t launch_backward_rc(const void *gy, void *gx, const RcPlan &p, const I
     };
     // window slots per thread: the fewest of 1, 2, 4, 8 that hold the
     // windows reaching a slab
-    if (p.maxkd <= 4) {
-        if (p.slots <= 1) go(bwd_rc_kernel<T, 4, kBlock, 1>);
-        else if (p.slots <= 2) go(bwd_rc_kernel<T, 4, kBlock, 2>);
-        else if (p.slots <= 4) go(bwd_rc_kernel<T, 4, kBlock, 4>);
-        else go(bwd_rc_kernel<T, 4, kBlock, 8>);
-    } else {
-        if (p.slots <= 1) go(bwd_rc_kernel<T, 8, kBlock, 1>);
-        else if (p.slots <= 2) go(bwd_rc_kernel<T, 8, kBlock, 2>);
-        else if (p.slots <= 4) go(bwd_rc_kernel<T, 8, kBlock, 4>);
-        else go(bwd_rc_kernel<T, 8, kBlock, 8>);
-    }
+    auto slots = [&](auto k1, auto k2, auto k4, auto k8) {
+        if (p.slots <= 1) go(k1);
+        else if (p.slots <= 2) go(k2);
+        else if (p.slots <= 4) go(k4);
+        else go(k8);
+    };
+    // windows of at most 3 taps per axis: exact 3-slice loads and a
+    // 3 x 3 scan with every load issued at once; else loops
+    if (p.small3)
+        slots(bwd_rc_kernel<T, 3, kBlock, 1, 3>, bwd_rc_kernel<T, 3, kBlock, 2, 3>,
+              bwd_rc_kernel<T, 3, kBlock, 4, 3>, bwd_rc_kernel<T, 3, kBlock, 8, 3>);
+    else if (p.maxkd <= 4)
+        slots(bwd_rc_kernel<T, 4, kBlock, 1, 0>, bwd_rc_kernel<T, 4, kBlock, 2, 0>,
+              bwd_rc_kernel<T, 4, kBlock, 4, 0>, bwd_rc_kernel<T, 4, kBlock, 8, 0>);
+    else
+        slots(bwd_rc_kernel<T, 8, kBlock, 1, 0>, bwd_rc_kernel<T, 8, kBlock, 2, 0>,
+              bwd_rc_kernel<T, 8, kBlock, 4, 0>, bwd_rc_kernel<T, 8, kBlock, 8, 0>);
     return hipGetLastError();
 }
 

@@ -139,4 +139,38 @@ __device__ __forceinline__ uint32_t col_scan(const Acc *sv, const uint8_t *sd, i
     return nk != 0xffffffffu ? nk : bk;
 }
 
+// Stage HW for windows of at most K rows and K columns, every load issued
+// at once: row and column numbers are clamped to the window's span, and a
+// clamped tap repeats an element of the window with its own key, which
+// changes neither the maximum nor the smallest key.
+template <int K, typename Acc>
+__device__ __forceinline__ uint32_t col_scan_k(const Acc *sv, const uint8_t *sd, int32_t W, int2 wh,
+                                               int2 ww, Acc &m)
+{
+    int32_t at[K * K];
+    Acc v[K * K];
+    uint8_t dd[K * K];
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+        for (int c = 0; c < K; ++c)
+            at[j * K + c] = min(wh.x + j, wh.y - 1) * W + min(ww.x + c, ww.y - 1);
+#pragma unroll
+    for (int q = 0; q < K * K; ++q) {
+        v[q] = sv[at[q]];
+        dd[q] = sd[at[q]];
+    }
+    m = v[0];
+    uint32_t bk = 0xffffffffu, nk = 0xffffffffu;
+#pragma unroll
+    for (int q = 0; q < K * K; ++q) {
+        const uint32_t k = ((uint32_t)dd[q] << 24) | (uint32_t)at[q];
+        const bool gt = v[q] > m;
+        bk = gt ? k : (v[q] == m ? min(bk, k) : bk);
+        m = gt ? v[q] : m;
+        nk = v[q] != v[q] ? min(nk, k) : nk;
+    }
+    return nk != 0xffffffffu ? nk : bk;
+}
+
 }  // namespace mp3d

@@ -92,6 +92,7 @@ struct RcPlan {
     uint32_t tab_bytes;        // LDS: window table, 16-byte aligned
     uint32_t lds_bytes;        // table + the larger of D-partials and accumulator
     int32_t slots;             // windows per thread: most windows reaching a slab / threads
+    int32_t small3;            // every window has at most 3 taps per axis
 };
 
 // General forward (forward_ex.hip): one thread per output, any geometry.

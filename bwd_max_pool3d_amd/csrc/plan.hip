@@ -407,6 +407,7 @@ bool plan_rc(const Geom &g, int es, int ab, const void *x, RcPlan *p)
     p->tab_bytes = (uint32_t)tab;
     p->lds_bytes = (uint32_t)(tab + rb);
     p->slots = (int32_t)cdiv(cdmax * ohw, kBlock);
+    p->small3 = maxkd <= 3 && max_taps(B) <= 3 && max_taps(Cw) <= 3;
     return true;
 }
 

@@ -173,3 +173,29 @@ def check_backward(orc, gy: torch.Tensor, idx: torch.Tensor, in_shape, gx_gpu,
         assert len(contribs) <= 8, "%s: cell %d has %d contributions" % (what, cell, len(contribs))
         assert int(gb[cell]) in _fold_orders(contribs, code), \
             "%s: cell %d is no serial order of its contributions" % (what, cell)
+
+
+def sample_planes(P: int, n: int = 10, seed: int = 0):
+    """Planes 0 and P - 1 and n seeded picks, sorted."""
+    rng = np.random.default_rng(seed)
+    picks = {0, P - 1} | set(int(v) for v in rng.integers(0, P, size=n))
+    return sorted(picks)
+
+
+def full_backward_property(gy, idx, gx, in_shape):
+    """On every gx element: within the float32-summation bound (plus half a
+    unit in the last place of the storage type) of the exact sum."""
+    N, C, D, H, W = in_shape
+    P, n = N * C, D * H * W
+    ii = idx.view(P, -1).long()
+    g64 = gy.view(P, -1).double()
+    ref = torch.zeros(P, n, dtype=torch.float64, device="cuda").scatter_add_(1, ii, g64)
+    ab = torch.zeros(P, n, dtype=torch.float64, device="cuda").scatter_add_(1, ii, g64.abs())
+    cnt = torch.zeros(P, n, dtype=torch.float64, device="cuda").scatter_add_(
+        1, ii, torch.ones_like(g64))
+    half_ulp = {torch.float32: 0.0, torch.float16: 2.0**-11, torch.bfloat16: 2.0**-8}[gy.dtype]
+    tiny = {torch.float32: 0.0, torch.float16: 2.0**-25, torch.bfloat16: 2.0**-134}[gy.dtype]
+    bound = (cnt - 1).clamp(min=0) * 2.0**-24 * ab * 1.0001 + half_ulp * ref.abs() * 1.0001 + tiny
+    err = (gx.view(P, -1).double() - ref).abs()
+    assert bool((err <= bound).all()), "max excess %g" % float((err - bound).max())
+    assert bool((gx.view(P, -1)[cnt == 0] == 0).all())

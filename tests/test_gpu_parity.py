@@ -293,12 +293,6 @@ def test_errors_leave_outputs_untouched():
 # the named workloads at full size
 # ---------------------------------------------------------------------------
 
-def _sample_planes(P: int, n: int = 10, seed: int = 0):
-    rng = np.random.default_rng(seed)
-    picks = {0, P - 1} | set(int(v) for v in rng.integers(0, P, size=n))
-    return sorted(picks)
-
-
 def _windows(orc, X, O, k, s):
     lo = [orc.window(X, O, k, s, o)[0] for o in range(O)]
     hi = [orc.window(X, O, k, s, o)[1] for o in range(O)]
@@ -325,25 +319,6 @@ def _full_properties(orc, wl, x, y, idx):
         assert bool(((c >= lo.view(shape)) & (c < hi.view(shape))).all())
 
 
-def _full_backward_property(gy, idx, gx, in_shape):
-    """On every gx element: within the float32-summation bound (plus half a
-    unit in the last place of the storage type) of the exact sum."""
-    N, C, D, H, W = in_shape
-    P, n = N * C, D * H * W
-    ii = idx.view(P, -1).long()
-    g64 = gy.view(P, -1).double()
-    ref = torch.zeros(P, n, dtype=torch.float64, device="cuda").scatter_add_(1, ii, g64)
-    ab = torch.zeros(P, n, dtype=torch.float64, device="cuda").scatter_add_(1, ii, g64.abs())
-    cnt = torch.zeros(P, n, dtype=torch.float64, device="cuda").scatter_add_(
-        1, ii, torch.ones_like(g64))
-    half_ulp = {torch.float32: 0.0, torch.float16: 2.0**-11, torch.bfloat16: 2.0**-8}[gy.dtype]
-    tiny = {torch.float32: 0.0, torch.float16: 2.0**-25, torch.bfloat16: 2.0**-134}[gy.dtype]
-    bound = (cnt - 1).clamp(min=0) * 2.0**-24 * ab * 1.0001 + half_ulp * ref.abs() * 1.0001 + tiny
-    err = (gx.view(P, -1).double() - ref).abs()
-    assert bool((err <= bound).all()), "max excess %g" % float((err - bound).max())
-    assert bool((gx.view(P, -1)[cnt == 0] == 0).all())
-
-
 @pytest.mark.parametrize("wl", workloads.WORKLOADS, ids=lambda w: w.name)
 def test_workload_full_size(orc, wl):
     N, C, D, H, W = wl.shape
@@ -355,7 +330,7 @@ def test_workload_full_size(orc, wl):
     y, idx = _gpu.gpu_forward(xd, out, k, s)
     torch.cuda.synchronize()
     small = P * D * H * W <= 1 << 20
-    planes = range(P) if small else _sample_planes(P)
+    planes = range(P) if small else _gpu.sample_planes(P)
     for p in planes:
         n_, c_ = divmod(p, C)
         xp = x[n_:n_ + 1, c_:c_ + 1].contiguous()
@@ -392,7 +367,7 @@ def test_workload_full_size(orc, wl):
         _gpu.check_backward(orc, gy[sl].contiguous(), idx[sl].cpu().contiguous(),
                             (1, 1, D, H, W), gx[sl], exact=exact,
                             what="%s plane %d" % (wl.name, p))
-    _full_backward_property(gyd, idx, gx, wl.shape)
+    _gpu.full_backward_property(gyd, idx, gx, wl.shape)
     # ordered backward: bit-exact on the sampled planes, and the same bits twice
     gx2 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=2)
     gx3 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=2, poison=False)
@@ -424,7 +399,7 @@ def test_float64_full_size(orc, wl):
     gx1 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s)
     gx2 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=2)
     torch.cuda.synchronize()
-    for p in _sample_planes(P):
+    for p in _gpu.sample_planes(P):
         n_, c_ = divmod(p, C)
         sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
         yo, io = _gpu.oracle_forward(orc, x[sl].contiguous(), out, k, s)

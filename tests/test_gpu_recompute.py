@@ -103,11 +103,14 @@ def test_recompute_y_not_from_forward(orc):
 
 
 @pytest.mark.parametrize("wl", [w for w in workloads.WORKLOADS if w.backward], ids=lambda w: w.name)
-def test_recompute_full_size(wl):
+def test_recompute_full_size(orc, wl):
     """At full size the ordered index-free backward equals the ordered
     backward from the forward's idx bit for bit (both are the ascending
-    fold of the same contributions); the idx path is checked against the
-    oracle in test_gpu_parity."""
+    fold of the same contributions; the idx path is checked against the
+    oracle in test_gpu_parity).  The index-free backward in any order (the
+    fused column-stage kernel where it applies) is checked against the
+    oracle, fed the forward's idx, on sampled planes, and within the
+    binary32-summation bound on every element."""
     xd = wl.make_x().cuda()
     if wl.adaptive:
         y, idx = mp.amp3d_forward(xd, wl.out)
@@ -120,3 +123,16 @@ def test_recompute_full_size(wl):
     got = mp.mp3d_backward_recompute(xd, y, gy, overlap=2, **geo)
     iv = torch.int32 if got.element_size() == 4 else torch.int16
     assert torch.equal(got.view(iv), ref.view(iv)), wl.name
+    del ref, got
+    gx = mp.mp3d_backward_recompute(xd, y, gy, **geo)
+    torch.cuda.synchronize()
+    N, C, D, H, W = wl.shape
+    P = N * C
+    planes = range(P) if P * D * H * W <= 1 << 20 else _gpu.sample_planes(P)
+    gyc = gy.cpu()
+    for p in planes:
+        n_, c_ = divmod(p, C)
+        sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
+        _gpu.check_backward(orc, gyc[sl].contiguous(), idx[sl].cpu().contiguous(), (1, 1, D, H, W),
+                            gx[sl], exact=False, what="%s index-free plane %d" % (wl.name, p))
+    _gpu.full_backward_property(gy, idx, gx, wl.shape)
