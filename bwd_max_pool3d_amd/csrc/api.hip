@@ -285,8 +285,9 @@ int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPat
         if (!ordered && plan_rc(g, (int)sizeof(typename T::raw), (int)sizeof(typename T::acc),
                                 src.x, &rp)) {
             if (log_enabled())
-                fprintf(stderr, "[mp3d] backward index-free column dtype=%d slab=%d tiles=%u lds=%u\n",
-                        T::code, rp.td, rp.ntiles, rp.lds_bytes);
+                fprintf(stderr, "[mp3d] backward index-free column dtype=%d slab=%d tiles=%u lds=%u "
+                        "slots=%d maxkd=%d small3=%d\n",
+                        T::code, rp.td, rp.ntiles, rp.lds_bytes, rp.slots, rp.maxkd, rp.small3);
             return hip_status(launch_backward_rc<T>(gy, gx, rp, src, s), "backward index-free launch");
         }
     }

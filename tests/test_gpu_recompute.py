@@ -31,6 +31,15 @@ CASES = [
     ((1, 1, 10, 11, 12), None, (3, 2, 3), (1, 2, 3), (1, 1, 0), (2, 3, 1), False),
     ((1, 1, 2, 3, 4), None, (2, 2, 2), (1, 1, 1), (1, 1, 1), (3, 2, 2), False),
     ((1, 1, 3, 200, 300), None, (3, 3, 3), (1, 2, 2), (1, 1, 1), (1, 1, 1), False),
+    # the fused index-free kernel: 2, 4 and 8 windows per thread with the
+    # looped scan (windows of 4 taps along h, w), 4 and 8 with the 3 x 3
+    # scan, and windows up to 8 slices deep
+    ((1, 2, 8, 48, 48), (5, 14, 14), None, None, None, None, False),
+    ((1, 2, 8, 64, 64), (5, 20, 20), None, None, None, None, False),
+    ((1, 2, 8, 64, 64), (5, 23, 23), None, None, None, None, False),
+    ((1, 2, 8, 40, 40), (5, 20, 20), None, None, None, None, False),
+    ((1, 2, 8, 40, 48), (5, 28, 24), None, None, None, None, False),
+    ((1, 2, 20, 12, 16), (3, 5, 5), None, None, None, None, False),
 ]
 
 
