@@ -288,7 +288,8 @@ int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPat
                 fprintf(stderr, "[mp3d] backward index-free column dtype=%d slab=%d tiles=%u lds=%u "
                         "slots=%d maxkd=%d small3=%d\n",
                         T::code, rp.td, rp.ntiles, rp.lds_bytes, rp.slots, rp.maxkd, rp.small3);
-            return hip_status(launch_backward_rc<T>(gy, gx, rp, src, s), "backward index-free launch");
+            return hip_status(launch_backward_rc<T>(src.x, src.y, gy, gx, rp, s),
+                              "backward index-free launch");
         }
     }
     BwdPlan p;

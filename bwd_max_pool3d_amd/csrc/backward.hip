@@ -234,9 +234,9 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
 // window reaching the slab its first maximum (the first NaN when it holds
 // one); where that element equals y[o], every tap equal to y[o] is a
 // maximum, so the first of them is that element.  Elsewhere -- y not the
-// window's maximum -- the window is scanned in memory (fb).  The LDS that
-// held the D-partials then becomes the slab's accumulator, as in the slab
-// kernel.
+// window's maximum -- the window is scanned in memory (rc_scan).  The LDS
+// that held the D-partials then becomes the slab's accumulator, as in the
+// slab kernel.
 //
 // The fallback scan is a plain loop over the window's in-range taps (one
 // load at a time): it runs only where y is not the window's maximum, and
@@ -263,8 +263,8 @@ __device__ __forceinline__ int32_t rc_scan(const typename T::raw *xp, const Geom
 
 template <typename T, int MAXKD, int NT, int KS, int KHW>
 __global__ void __launch_bounds__(NT)
-bwd_rc_kernel(const typename T::raw *__restrict__ gy, typename T::raw *__restrict__ gx, RcPlan p,
-              IdxRecompute<T> fb)
+bwd_rc_kernel(const typename T::raw *__restrict__ x, const typename T::raw *__restrict__ y,
+              const typename T::raw *__restrict__ gy, typename T::raw *__restrict__ gx, RcPlan p)
 {
     using R = typename T::raw;
     using Acc = typename T::acc;
@@ -287,7 +287,7 @@ bwd_rc_kernel(const typename T::raw *__restrict__ gy, typename T::raw *__restric
     const int32_t cd = max(A.last_starting(d1 - 1) + 1 - od0, 0);
     const int32_t nwin = cd * OHW;                       // <= KS * NT (the plan)
     const int64_t obase = (int64_t)plane * p.g.out_plane + (int64_t)od0 * OHW;
-    const R *xp = fb.x + (int64_t)plane * p.g.in_plane;
+    const R *xp = x + (int64_t)plane * p.g.in_plane;
 
     // y and gy of the windows, in flight during stage D
     R ry[KS], rg[KS];
@@ -297,7 +297,7 @@ bwd_rc_kernel(const typename T::raw *__restrict__ gy, typename T::raw *__restric
         ry[k] = R{};
         rg[k] = R{};
         if (e < nwin) {
-            ry[k] = fb.y[obase + e];
+            ry[k] = y[obase + e];
             rg[k] = gy[obase + e];
         }
     }
@@ -306,7 +306,7 @@ bwd_rc_kernel(const typename T::raw *__restrict__ gy, typename T::raw *__restric
                          : make_int2(Cw.start(j - B.O), Cw.end(j - B.O));
     Acc *pv = reinterpret_cast<Acc *>(region);
     uint8_t *pd = region + (((int64_t)cd * HW * (int64_t)sizeof(Acc) + 15) & ~(int64_t)15);
-    col_stage_d<T, MAXKD, NT>(xp, A, HW, od0, cd, pv, pd);
+    if (cd > 0) col_stage_d<T, MAXKD, NT>(xp, A, HW, od0, cd, pv, pd);   // uniform
     __syncthreads();
 
     int32_t ri[KS];
@@ -459,15 +459,15 @@ hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const 
 }
 
 template <typename T>
-hipError_t launch_backward_rc(const void *gy, void *gx, const RcPlan &p, const IdxRecompute<T> &fb,
-                              hipStream_t s)
+hipError_t launch_backward_rc(const void *x, const void *y, const void *gy, void *gx,
+                              const RcPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
     uint32_t grid = p.ntiles;
     if (grid >= 64) grid = (grid + 7u) & ~7u;            // blocks map per XCD; the surplus exits
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), p.lds_bytes, s, (const R *)gy, (R *)gx,
-                           p, fb);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), p.lds_bytes, s, (const R *)x,
+                           (const R *)y, (const R *)gy, (R *)gx, p);
     };
     // window slots per thread: the fewest of 1, 2, 4, 8 that hold the
     // windows reaching a slab
@@ -516,10 +516,10 @@ template hipError_t launch_backward_tile<BF16, IdxRecompute<BF16>>(const void *,
 template hipError_t launch_backward_tile<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F64, IdxRecompute<F64>>(const void *, const IdxRecompute<F64> &, void *, const BwdPlan &, hipStream_t);
-template hipError_t launch_backward_rc<F32>(const void *, void *, const RcPlan &, const IdxRecompute<F32> &, hipStream_t);
-template hipError_t launch_backward_rc<F16>(const void *, void *, const RcPlan &, const IdxRecompute<F16> &, hipStream_t);
-template hipError_t launch_backward_rc<BF16>(const void *, void *, const RcPlan &, const IdxRecompute<BF16> &, hipStream_t);
-template hipError_t launch_backward_rc<F64>(const void *, void *, const RcPlan &, const IdxRecompute<F64> &, hipStream_t);
+template hipError_t launch_backward_rc<F32>(const void *, const void *, const void *, void *, const RcPlan &, hipStream_t);
+template hipError_t launch_backward_rc<F16>(const void *, const void *, const void *, void *, const RcPlan &, hipStream_t);
+template hipError_t launch_backward_rc<BF16>(const void *, const void *, const void *, void *, const RcPlan &, hipStream_t);
+template hipError_t launch_backward_rc<F64>(const void *, const void *, const void *, void *, const RcPlan &, hipStream_t);
 template hipError_t launch_backward_gather<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);
 template hipError_t launch_backward_gather<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const GatherPlan &, hipStream_t);
 template hipError_t launch_backward_gather<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const GatherPlan &, hipStream_t);

@@ -117,10 +117,4 @@ struct IdxRecompute {
     }
 };
 
-// The index-free backward by column stages (backward.hip); fb scans a
-// window in memory where the recomputed maximum differs from y.
-template <typename T>
-hipError_t launch_backward_rc(const void *gy, void *gx, const RcPlan &p, const IdxRecompute<T> &fb,
-                              hipStream_t s);
-
 }  // namespace mp3d

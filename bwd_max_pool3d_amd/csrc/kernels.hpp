@@ -209,6 +209,9 @@ hipError_t launch_forward_small(const void *x, void *y, IT *idx, const SmallPlan
 template <typename T, typename Src>
 hipError_t launch_backward_small(const void *gy, const Src &src, void *gx, const SmallPlan &p,
                                  hipStream_t s);
+template <typename T>
+hipError_t launch_backward_rc(const void *x, const void *y, const void *gy, void *gx,
+                              const RcPlan &p, hipStream_t s);
 template <typename T, typename Src>
 hipError_t launch_backward_gather(const void *gy, const Src &src, void *gx, const GatherPlan &p,
                                   hipStream_t s);

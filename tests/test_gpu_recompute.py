@@ -40,6 +40,10 @@ CASES = [
     ((1, 2, 8, 40, 40), (5, 20, 20), None, None, None, None, False),
     ((1, 2, 8, 40, 48), (5, 28, 24), None, None, None, None, False),
     ((1, 2, 20, 12, 16), (3, 5, 5), None, None, None, None, False),
+    # slabs that no window reaches: the slices after the last window, and
+    # gaps between windows (stride above the kernel)
+    ((1, 2, 8, 8, 16), None, (3, 3, 3), (2, 2, 2), (0, 0, 0), (1, 1, 1), False),
+    ((1, 2, 10, 8, 8), None, (1, 1, 1), (5, 5, 5), (0, 0, 0), (1, 1, 1), False),
 ]
 
 
