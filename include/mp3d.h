@@ -38,7 +38,10 @@
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Calls enqueue their kernels and return without synchronising;
- * device faults surface at the caller's next synchronisation.
+ * device faults surface at the caller's next synchronisation.  A call only
+ * launches kernels on `stream` (no allocation, memset or synchronisation),
+ * so calls can be recorded under stream capture into a HIP graph and
+ * replayed.
  *
  * Errors: every call returns MP3D_OK (0) or an error code.  All argument
  * checks run before the first launch, so a call that fails leaves every
