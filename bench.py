@@ -291,7 +291,7 @@ def cpu_baseline(target_s: float, threads: int = 1):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-oracle sample size in seconds (0 skips the leg)")
@@ -419,9 +419,11 @@ def main():
         avg = sum(op.ms) / len(op.ms)
         srt = sorted(op.ms)
         med = srt[len(srt) // 2]
+        p90 = srt[min(len(srt) - 1, (9 * len(srt)) // 10)]
         t = med if median else avg
         return {"op": op.name, "ms": round(t, 5), "ms_mean": round(avg, 5),
-                "ms_min": round(srt[0], 5), "ms_median": round(med, 5), "bytes": op.nbytes,
+                "ms_min": round(srt[0], 5), "ms_median": round(med, 5),
+                "ms_p90": round(p90, 5), "bytes": op.nbytes,
                 "GB_s": round(op.nbytes / (t * 1e-3) / 1e9, 1),
                 "elems_per_s": round(op.elems / (t * 1e-3), 1),
                 "frac_of_peak": round(op.nbytes / (t * 1e-3) / 1e9 / PEAK_GBS, 4)}
