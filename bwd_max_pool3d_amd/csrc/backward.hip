@@ -22,6 +22,7 @@
 // sum is rounded once to the storage type.
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "colstage.hpp"
 #include "dtype.hpp"
@@ -304,9 +305,18 @@ bwd_rc_kernel(const typename T::raw *__restrict__ x, const typename T::raw *__re
     for (int32_t j = tid; j < B.O + Cw.O; j += NT)
         tab[j] = j < B.O ? make_int2(B.start(j), B.end(j))
                          : make_int2(Cw.start(j - B.O), Cw.end(j - B.O));
-    Acc *pv = reinterpret_cast<Acc *>(region);
-    uint8_t *pd = region + (((int64_t)cd * HW * (int64_t)sizeof(Acc) + 15) & ~(int64_t)15);
-    if (cd > 0) col_stage_d<T, MAXKD, NT>(xp, A, HW, od0, cd, pv, pd);   // uniform
+    // the partials: packed words for 16-bit storage types, else split
+    // arrays of values and d offsets
+    constexpr bool PK = sizeof(R) == 2;
+    using Part = std::conditional_t<PK, PartPacked<T>, PartSplit<T>>;
+    Part part;
+    if constexpr (PK) {
+        part = Part{reinterpret_cast<uint32_t *>(region)};
+    } else {
+        part = Part{reinterpret_cast<Acc *>(region),
+                    region + (((int64_t)cd * HW * (int64_t)sizeof(Acc) + 15) & ~(int64_t)15)};
+    }
+    if (cd > 0) col_stage_d<T, MAXKD, NT>(xp, A, HW, od0, cd, part);   // uniform
     __syncthreads();
 
     int32_t ri[KS];
@@ -321,12 +331,13 @@ bwd_rc_kernel(const typename T::raw *__restrict__ x, const typename T::raw *__re
             const int32_t oh = (int32_t)(q - odl * (uint32_t)B.O);
             Acc m;
             uint32_t bk;
+            const Part sp = part.at((int32_t)odl * HW);
             if constexpr (KHW > 0)
-                bk = col_scan_k<KHW>(pv + odl * HW, pd + odl * HW, W, tab[oh], tab[B.O + ow], m);
+                bk = col_scan_k<KHW>(sp, W, tab[oh], tab[B.O + ow], m);
             else
-                bk = col_scan(pv + odl * HW, pd + odl * HW, W, tab[oh], tab[B.O + ow], m);
+                bk = col_scan(sp, W, tab[oh], tab[B.O + ow], m);
             const int32_t bi = (int32_t)(bk & 0xffffffu);
-            const Acc best = pv[odl * HW + bi];          // NaN exactly when bk names a NaN
+            const Acc best = sp.value(bi);               // NaN exactly when bk names a NaN
             const Acc want = T::widen(ry[k]);
             const bool same = want != want ? best != best : best == want;
             ri[k] = same ? (A.start(od0 + (int32_t)odl) + (int32_t)(bk >> 24)) * HW + bi
@@ -469,25 +480,29 @@ hipError_t launch_backward_rc(const void *x, const void *y, const void *gy, void
         hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), p.lds_bytes, s, (const R *)x,
                            (const R *)y, (const R *)gy, (R *)gx, p);
     };
-    // window slots per thread: the fewest of 1, 2, 4, 8 that hold the
+    // window slots per thread: the fewest of 1, 2, 4, 8, 16 that hold the
     // windows reaching a slab
-    auto slots = [&](auto k1, auto k2, auto k4, auto k8) {
+    auto slots = [&](auto k1, auto k2, auto k4, auto k8, auto k16) {
         if (p.slots <= 1) go(k1);
         else if (p.slots <= 2) go(k2);
         else if (p.slots <= 4) go(k4);
-        else go(k8);
+        else if (p.slots <= 8) go(k8);
+        else go(k16);
     };
     // windows of at most 3 taps per axis: exact 3-slice loads and a
     // 3 x 3 scan with every load issued at once; else loops
     if (p.small3)
         slots(bwd_rc_kernel<T, 3, kBlock, 1, 3>, bwd_rc_kernel<T, 3, kBlock, 2, 3>,
-              bwd_rc_kernel<T, 3, kBlock, 4, 3>, bwd_rc_kernel<T, 3, kBlock, 8, 3>);
+              bwd_rc_kernel<T, 3, kBlock, 4, 3>, bwd_rc_kernel<T, 3, kBlock, 8, 3>,
+              bwd_rc_kernel<T, 3, kBlock, 16, 3>);
     else if (p.maxkd <= 4)
         slots(bwd_rc_kernel<T, 4, kBlock, 1, 0>, bwd_rc_kernel<T, 4, kBlock, 2, 0>,
-              bwd_rc_kernel<T, 4, kBlock, 4, 0>, bwd_rc_kernel<T, 4, kBlock, 8, 0>);
+              bwd_rc_kernel<T, 4, kBlock, 4, 0>, bwd_rc_kernel<T, 4, kBlock, 8, 0>,
+              bwd_rc_kernel<T, 4, kBlock, 16, 0>);
     else
         slots(bwd_rc_kernel<T, 8, kBlock, 1, 0>, bwd_rc_kernel<T, 8, kBlock, 2, 0>,
-              bwd_rc_kernel<T, 8, kBlock, 4, 0>, bwd_rc_kernel<T, 8, kBlock, 8, 0>);
+              bwd_rc_kernel<T, 8, kBlock, 4, 0>, bwd_rc_kernel<T, 8, kBlock, 8, 0>,
+              bwd_rc_kernel<T, 8, kBlock, 16, 0>);
     return hipGetLastError();
 }
 

@@ -41,10 +41,44 @@ __device__ __forceinline__ void col_load(ColWin<MAXKD> &w, const R *__restrict__
         w.q[j] = *reinterpret_cast<const u32x4 *>(col + (int64_t)min(j, n - 1) * hw);
 }
 
-// Element-wise first maximum over the window's slots: writes the values and
-// the winning slot (the d offset in the window) to LDS.
-template <typename T, int MAXKD>
-__device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, typename T::acc *pv, uint8_t *pd)
+// Where stage D writes a slice's D-partials and stage HW reads them.
+// PartSplit: the values (binary32, or binary64 for float64) and their 8-bit
+// d offsets in two arrays.
+template <typename T>
+struct PartSplit {
+    using Acc = typename T::acc;
+    Acc *pv;
+    uint8_t *pd;
+    __device__ __forceinline__ void put(int32_t i, Acc v, int32_t jd) const {
+        pv[i] = v;
+        pd[i] = (uint8_t)jd;
+    }
+    __device__ __forceinline__ Acc value(int32_t i) const { return pv[i]; }
+    __device__ __forceinline__ uint32_t dof(int32_t i) const { return pd[i]; }
+    __device__ __forceinline__ PartSplit at(int32_t off) const { return {pv + off, pd + off}; }
+};
+
+// PartPacked (16-bit storage types): one 32-bit word per partial, the value
+// narrowed back to its storage bits in the low half (exact for every
+// number; a NaN stays a NaN) and the d offset in the high half.
+template <typename T>
+struct PartPacked {
+    using Acc = typename T::acc;
+    uint32_t *pk;
+    __device__ __forceinline__ void put(int32_t i, Acc v, int32_t jd) const {
+        pk[i] = (uint32_t)T::narrow(v) | ((uint32_t)jd << 16);
+    }
+    __device__ __forceinline__ Acc value(int32_t i) const {
+        return T::widen((typename T::raw)(pk[i] & 0xffffu));
+    }
+    __device__ __forceinline__ uint32_t dof(int32_t i) const { return pk[i] >> 16; }
+    __device__ __forceinline__ PartPacked at(int32_t off) const { return {pk + off}; }
+};
+
+// Element-wise first maximum over the window's slots: stores the values and
+// the winning slot (the d offset in the window) through the partial store.
+template <typename T, int MAXKD, typename P>
+__device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, const P &part)
 {
     using A = typename T::acc;
     constexpr int VE = 16 / (int)sizeof(typename T::raw);
@@ -76,19 +110,17 @@ __device__ __forceinline__ void col_reduce(const ColWin<MAXKD> &w, typename T::a
                 val = hit ? v[j][i] : val;
             }
         }
-        pv[i] = val;
-        pd[i] = (uint8_t)jd;
+        part.put(i, val, jd);
     }
 }
 
 // Stage D for output slices [od0, od0 + cd) of one plane (xp): the
-// D-partials of slice odl go to pv / pd + odl * HW.  The loads of two
+// D-partials of slice odl go to part.at(odl * HW).  The loads of two
 // windows are in flight while the previous one is reduced; a slice shared
 // by two windows is read twice, the second time from L2.
-template <typename T, int MAXKD, int NT>
+template <typename T, int MAXKD, int NT, typename P>
 __device__ __forceinline__ void col_stage_d(const typename T::raw *__restrict__ xp, const Axis &A,
-                                            int32_t HW, int32_t od0, int32_t cd,
-                                            typename T::acc *pv, uint8_t *pd)
+                                            int32_t HW, int32_t od0, int32_t cd, const P &part)
 {
     using R = typename T::raw;
     constexpr int VE = 16 / (int)sizeof(R);
@@ -103,33 +135,31 @@ __device__ __forceinline__ void col_stage_d(const typename T::raw *__restrict__ 
                 ds = A.start(od0 + odl + 1);
                 col_load<R, MAXKD>(wb, col + (int64_t)ds * HW, HW, A.end(od0 + odl + 1) - ds);
             }
-            col_reduce<T, MAXKD>(wa, pv + odl * HW + gi * VE, pd + odl * HW + gi * VE);
+            col_reduce<T, MAXKD>(wa, part.at(odl * HW + gi * VE));
             if (odl + 2 < cd) {
                 ds = A.start(od0 + odl + 2);
                 col_load<R, MAXKD>(wa, col + (int64_t)ds * HW, HW, A.end(od0 + odl + 2) - ds);
             }
             if (odl + 1 < cd)
-                col_reduce<T, MAXKD>(wb, pv + (odl + 1) * HW + gi * VE, pd + (odl + 1) * HW + gi * VE);
+                col_reduce<T, MAXKD>(wb, part.at((odl + 1) * HW + gi * VE));
         }
     }
 }
 
 // Stage HW for one window: rows [wh.x, wh.y), columns [ww.x, ww.y) of one
-// slice's D-partials (sv values, sd d offsets).  Returns the key of the
-// first maximum (the first NaN when there is one) and sets m to the
-// maximum.
-template <typename Acc>
-__device__ __forceinline__ uint32_t col_scan(const Acc *sv, const uint8_t *sd, int32_t W, int2 wh,
-                                             int2 ww, Acc &m)
+// slice's D-partials.  Returns the key of the first maximum (the first NaN
+// when there is one) and sets m to the maximum.
+template <typename P, typename Acc>
+__device__ __forceinline__ uint32_t col_scan(const P &sp, int32_t W, int2 wh, int2 ww, Acc &m)
 {
-    m = sv[wh.x * W + ww.x];
+    m = sp.value(wh.x * W + ww.x);
     uint32_t bk = 0xffffffffu, nk = 0xffffffffu;
     for (int32_t h = wh.x; h < wh.y; ++h) {
 #pragma unroll 4
         for (int32_t w = ww.x; w < ww.y; ++w) {
             const int32_t i = h * W + w;
-            const Acc v = sv[i];
-            const uint32_t k = ((uint32_t)sd[i] << 24) | (uint32_t)i;
+            const Acc v = sp.value(i);
+            const uint32_t k = (sp.dof(i) << 24) | (uint32_t)i;
             const bool gt = v > m;
             bk = gt ? k : (v == m ? min(bk, k) : bk);
             m = gt ? v : m;
@@ -143,13 +173,12 @@ __device__ __forceinline__ uint32_t col_scan(const Acc *sv, const uint8_t *sd, i
 // at once: row and column numbers are clamped to the window's span, and a
 // clamped tap repeats an element of the window with its own key, which
 // changes neither the maximum nor the smallest key.
-template <int K, typename Acc>
-__device__ __forceinline__ uint32_t col_scan_k(const Acc *sv, const uint8_t *sd, int32_t W, int2 wh,
-                                               int2 ww, Acc &m)
+template <int K, typename P, typename Acc>
+__device__ __forceinline__ uint32_t col_scan_k(const P &sp, int32_t W, int2 wh, int2 ww, Acc &m)
 {
     int32_t at[K * K];
     Acc v[K * K];
-    uint8_t dd[K * K];
+    uint32_t dd[K * K];
 #pragma unroll
     for (int j = 0; j < K; ++j)
 #pragma unroll
@@ -157,14 +186,14 @@ __device__ __forceinline__ uint32_t col_scan_k(const Acc *sv, const uint8_t *sd,
             at[j * K + c] = min(wh.x + j, wh.y - 1) * W + min(ww.x + c, ww.y - 1);
 #pragma unroll
     for (int q = 0; q < K * K; ++q) {
-        v[q] = sv[at[q]];
-        dd[q] = sd[at[q]];
+        v[q] = sp.value(at[q]);
+        dd[q] = sp.dof(at[q]);
     }
     m = v[0];
     uint32_t bk = 0xffffffffu, nk = 0xffffffffu;
 #pragma unroll
     for (int q = 0; q < K * K; ++q) {
-        const uint32_t k = ((uint32_t)dd[q] << 24) | (uint32_t)at[q];
+        const uint32_t k = (dd[q] << 24) | (uint32_t)at[q];
         const bool gt = v[q] > m;
         bk = gt ? k : (v[q] == m ? min(bk, k) : bk);
         m = gt ? v[q] : m;

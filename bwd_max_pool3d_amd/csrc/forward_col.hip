@@ -47,7 +47,7 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         tab[j] = j < B.O ? make_int2(B.start(j), B.end(j))
                          : make_int2(Cw.start(j - B.O), Cw.end(j - B.O));
 
-    col_stage_d<T, MAXKD, NT>(xp, A, HW, od0, cd, pv, pd);
+    col_stage_d<T, MAXKD, NT>(xp, A, HW, od0, cd, PartSplit<T>{pv, pd});
     __syncthreads();
 
     // stage HW
@@ -61,7 +61,8 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         const int32_t oh = (int32_t)(q - odl * (uint32_t)B.O);
         const Acc *sv = pv + odl * HW;
         Acc m;
-        const uint32_t bk = col_scan(sv, pd + odl * HW, W, tab[oh], tab[B.O + ow], m);
+        const uint32_t bk = col_scan(PartSplit<T>{pv + odl * HW, pd + odl * HW}, W, tab[oh],
+                                     tab[B.O + ow], m);
         const int32_t bi = (int32_t)(bk & 0xffffffu);
         const int32_t pos = (A.start(od0 + (int32_t)odl) + (int32_t)(bk >> 24)) * HW + bi;
         const Acc best = sv[bi];          // the element itself: keeps the sign of a zero

@@ -81,7 +81,7 @@ constexpr int kMaxPhase = 64;              // ordered slab: at most this many ph
 // first maximum of every window reaching the slab with the column forward's
 // two stages, takes it as the argmax where it equals y[o] (else scans the
 // window in memory), then reuses the same LDS as the slab's accumulator.
-constexpr int kRcSlots = 8;                // at most this many windows per thread (one round)
+constexpr int kRcSlots = 16;               // at most this many windows per thread (one round)
 struct RcPlan {
     Geom g;
     int32_t td, ntd;           // slices per slab, slabs per plane

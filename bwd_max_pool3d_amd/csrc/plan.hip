@@ -380,7 +380,9 @@ bool plan_rc(const Geom &g, int es, int ab, const void *x, RcPlan *p)
             cdmax = std::max(cdmax, cd);
         }
         if (cdmax * ohw > (int64_t)kRcSlots * kBlock) return 0;
-        return std::max(r16(cdmax * HW * ab) + cdmax * HW, r16(((int64_t)td * HW + 8) * ab));
+        // partials: one packed word for 16-bit storage, else value + d byte
+        const int64_t part = es == 2 ? r16(cdmax * HW * 4) : r16(cdmax * HW * ab) + cdmax * HW;
+        return std::max(part, r16(((int64_t)td * HW + 8) * ab));
     };
     const int64_t per_plane = cdiv(kWantTiles, std::max<int64_t>(g.planes, 1));
     int32_t td = (int32_t)std::min<int64_t>(A.X, std::max<int64_t>(1, A.X / per_plane));
