@@ -184,6 +184,10 @@ def build_ops(torch, mp, workloads, variants=True):
             gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, out=gx))
         exf_ops.append(Op(wl, "fwd_f64", f, nin * 8 + nout * 12, nin, "forward, float64"))
         exb_ops.append(Op(wl, "bwd_f64", b, nout * 12 + nin * 8, nin, "backward, float64"))
+        bo = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
+            gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, overlap=2, out=gx))
+        exb_ops.append(Op(wl, "bwd_f64_ordered", bo, nout * 12 + nin * 8, nin,
+                          "ordered backward, float64"))
     # the variants run in the step's order: forwards, then backwards
     return fwd_ops + bwd_ops, (vo_ops + exf_ops + ord_ops + exb_ops) if variants else []
 
@@ -461,7 +465,8 @@ def main():
         "index_free_backward": [op_row(op, True) for op in vo_ops if op.kind == "bwd_recompute"],
         "int64_index_forward": [op_row(op, True) for op in vo_ops if op.kind == "fwd_i64"],
         "padded": [op_row(op, True) for op in vo_ops if op.kind in ("fwd_pad", "bwd_pad")],
-        "float64": [op_row(op, True) for op in vo_ops if op.kind in ("fwd_f64", "bwd_f64")],
+        "float64": [op_row(op, True) for op in vo_ops
+                    if op.kind in ("fwd_f64", "bwd_f64", "bwd_f64_ordered")],
     }
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)

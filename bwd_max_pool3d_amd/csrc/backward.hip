@@ -448,16 +448,13 @@ hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const 
     int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)1 << 24);
     if (p.slab) {
         // one workgroup per slab; a multiple of 8 lets blocks map per XCD
-        // (the surplus blocks exit at once).  The ordered slab is binary32
-        // only (the plan gives binary64 cells no phases).
+        // (the surplus blocks exit at once)
         if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
-        if constexpr (sizeof(typename T::acc) == 4) {
-            if (p.nphase) {
-                hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kOrdThreads, true, kOrdRound>),
-                                   dim3((uint32_t)grid), dim3(kOrdThreads), p.lds_bytes, s,
-                                   (const R *)gy, src, (R *)gx, p);
-                return hipGetLastError();
-            }
+        if (p.nphase) {
+            hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kOrdThreads, true, kOrdRound>),
+                               dim3((uint32_t)grid), dim3(kOrdThreads), p.lds_bytes, s,
+                               (const R *)gy, src, (R *)gx, p);
+            return hipGetLastError();
         }
         hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kSlabBlock, false, Src::kSlots>),
                            dim3((uint32_t)grid), dim3(kSlabBlock), p.lds_bytes, s,

@@ -176,8 +176,7 @@ bool plan_fixed(const Geom &g, int elem_bytes, const void *x, const void *y,
 
 bool plan_forward(const Geom &g, int elem_bytes, FwdPlan *p);
 bool plan_col(const Geom &g, int elem_bytes, const void *x, ColPlan *p);
-// cell_bytes: the accumulator cell, 4 (binary32) or 8 (binary64: no
-// ordered slab).
+// cell_bytes: the accumulator cell, 4 (binary32) or 8 (binary64).
 // plan_backward with ordered = false always succeeds; with ordered = true
 // it fails when the ordered slab cannot hold the geometry (slices larger
 // than the accumulator, a slab reached by more windows than one round

@@ -291,8 +291,6 @@ bool plan_backward(const Geom &g, bool ordered, int cell_bytes, BwdPlan *p)
     const int64_t budget = std::min<int64_t>(ordered ? kOrdBudget : kAccBudget,
                                              (int64_t)lds_limit() - 64);
     const int64_t cb = cell_bytes;
-    // binary64 cells: no ordered slab (its phases add binary32 cells)
-    if (cb != 4 && ordered) return false;
     const int64_t slice = (int64_t)H * W * cb;
     p->g = g;
     if (slice <= budget) {
