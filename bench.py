@@ -24,7 +24,8 @@ the roofline of the dominant op (those events cost a few microseconds per
 op, so that pass is not the metric).  The values-only forward of each
 workload (no index written), the forward with int64 indices, the fixed
 workloads with padding k//2 (forward and backward), the ordered backward
-(overlap=2), the index-free backward (argmax recomputed from x and y) and
+(overlap=2), the index-free backward (argmax recomputed from x and y; one
+pass, and two through a workspace) and
 float64 forward and backward of the two large overlapping workloads are
 timed the same way, apart from the step, each launch after an untimed read
 of a 512 MiB buffer that leaves the caches clean, and reported on their own
@@ -126,6 +127,13 @@ def build_ops(torch, mp, workloads, variants=True):
                 x, y, gy, out=gx, **geo))
             ord_ops.append(Op(wl, "bwd_recompute", rc, nin * es + 2 * nout * es + nin * es, nin,
                               "index-free backward (argmax recomputed from x and y)"))
+            ws = torch.empty(mp.recompute_workspace_size(x.dtype, N, C, o3), dtype=torch.uint8,
+                             device="cuda")
+            rw = (lambda x=x, y=y, gy=gy, gx=gx, geo=geo, ws=ws: mp.mp3d_backward_recompute(
+                x, y, gy, out=gx, workspace=ws, **geo))
+            ord_ops.append(Op(wl, "bwd_recompute_ws", rw, nin * es + 2 * nout * es + nin * es,
+                              nin, "index-free backward through a workspace (the forward into "
+                              "it, its argmax checked against y)"))
         if not variants:
             continue
         # int64 indices (torch's index type): general forward kernel
@@ -462,7 +470,8 @@ def main():
         "per_op": per_op,
         "values_only_forward": [op_row(op, True) for op in vo_ops if op.kind == "fwd_values"],
         "ordered_backward": [op_row(op, True) for op in vo_ops if op.kind == "bwd_ordered"],
-        "index_free_backward": [op_row(op, True) for op in vo_ops if op.kind == "bwd_recompute"],
+        "index_free_backward": [op_row(op, True) for op in vo_ops
+                                if op.kind in ("bwd_recompute", "bwd_recompute_ws")],
         "int64_index_forward": [op_row(op, True) for op in vo_ops if op.kind == "fwd_i64"],
         "padded": [op_row(op, True) for op in vo_ops if op.kind in ("fwd_pad", "bwd_pad")],
         "float64": [op_row(op, True) for op in vo_ops

@@ -33,7 +33,7 @@ from ._lib import Mp3dError  # noqa: F401
 
 __all__ = ["mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
            "mp3d_forward_ex", "mp3d_backward_ex", "mp3d_out_size_ex",
-           "mp3d_backward_recompute", "Mp3dError"]
+           "mp3d_backward_recompute", "recompute_workspace_size", "Mp3dError"]
 
 _IDX = {torch.int32: _lib.MP3D_IDX_I32, torch.int64: _lib.MP3D_IDX_I64}
 
@@ -249,14 +249,27 @@ def mp3d_backward_ex(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel, stri
     return out
 
 
+def recompute_workspace_size(dtype: torch.dtype, N: int, C: int, out_size) -> int:
+    """Bytes of workspace the two-pass index-free backward needs."""
+    nbytes = ctypes.c_size_t()
+    _lib.check(_lib.load().mp3d_recompute_workspace_size(_DTYPE[dtype], N, C,
+                                                         *_triple(out_size),
+                                                         ctypes.byref(nbytes)))
+    return nbytes.value
+
+
 def mp3d_backward_recompute(x: torch.Tensor, y: torch.Tensor, gy: torch.Tensor, kernel=None,
                             stride=None, padding=0, dilation=1, overlap: int = -1,
-                            out: torch.Tensor | None = None):
+                            out: torch.Tensor | None = None, workspace=None):
     """Index-free backward: gx of x's shape, with each window's argmax
     recomputed from the forward's input ``x`` and output ``y`` (the first
     element of the window equal to y, the first NaN when y is NaN).
     ``kernel`` None means adaptive windows (y's extents); ``overlap`` as for
-    mp3d_backward (2: ordered)."""
+    mp3d_backward (2: ordered).  ``workspace``: None for the one-pass
+    kernels; a contiguous uint8 device tensor of at least
+    recompute_workspace_size(...) bytes, or True to allocate one, for the
+    two-pass form (the forward into the workspace, its argmax checked
+    against y)."""
     lib = _lib.load()
     for t, n in ((x, "x"), (y, "y"), (gy, "gy")):
         _check_tensor(t, n)
@@ -279,8 +292,22 @@ def mp3d_backward_recompute(x: torch.Tensor, y: torch.Tensor, gy: torch.Tensor, 
         if out.shape != x.shape or out.dtype != x.dtype:
             raise ValueError("out must match x")
     od, oh, ow = gy.shape[2:]
-    _lib.check(lib.mp3d_backward_recompute(x.data_ptr(), y.data_ptr(), gy.data_ptr(),
-                                           out.data_ptr(), _code(gy), N, C, D, H, W, od, oh, ow,
-                                           _arr3(k), _arr3(s), _arr3(pd), _arr3(dl),
-                                           int(overlap), _stream(gy)))
+    if workspace is None or workspace is False:
+        _lib.check(lib.mp3d_backward_recompute(x.data_ptr(), y.data_ptr(), gy.data_ptr(),
+                                               out.data_ptr(), _code(gy), N, C, D, H, W, od, oh,
+                                               ow, _arr3(k), _arr3(s), _arr3(pd), _arr3(dl),
+                                               int(overlap), _stream(gy)))
+        return out
+    if workspace is True:
+        workspace = torch.empty(recompute_workspace_size(x.dtype, N, C, (od, oh, ow)),
+                                dtype=torch.uint8, device=x.device)
+    if (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8
+            or not workspace.is_cuda or not workspace.is_contiguous()
+            or workspace.device != x.device):
+        raise ValueError("workspace must be a contiguous uint8 tensor on x's device")
+    _lib.check(lib.mp3d_backward_recompute_ws(x.data_ptr(), y.data_ptr(), gy.data_ptr(),
+                                              out.data_ptr(), _code(gy), N, C, D, H, W, od, oh,
+                                              ow, _arr3(k), _arr3(s), _arr3(pd), _arr3(dl),
+                                              int(overlap), workspace.data_ptr(),
+                                              workspace.numel(), _stream(gy)))
     return out

@@ -43,6 +43,14 @@ bool small_enabled()
     return !(v && strcmp(v, "0") == 0);
 }
 
+// MP3D_TWO_PASS=1: the index-free backward takes the two-pass form whenever
+// a workspace is given (tests use it to reach that form on any shape).
+bool two_pass_forced()
+{
+    const char *v = getenv("MP3D_TWO_PASS");
+    return v && strcmp(v, "1") == 0;
+}
+
 bool log_enabled()
 {
     static int on = -1;
@@ -255,10 +263,12 @@ enum class BwdPath { gather, accumulate, ordered };
 
 template <typename S> struct is_array_src : std::false_type {};
 template <typename IT> struct is_array_src<IdxArray<IT>> : std::true_type {};
+template <typename S> struct is_recompute_src : std::false_type {};
+template <typename T> struct is_recompute_src<IdxRecompute<T>> : std::true_type {};
 
 // The gather and small-tensor kernels visit every window of each input
-// element, so they take only index arrays; a recomputed argmax (a window
-// scan per call) goes to the slab / box kernels, which ask once per window.
+// element, so they take only index arrays; a recomputed or checked argmax
+// goes to the slab / box kernels, which ask once per window.
 template <typename T, typename Src>
 int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPath path,
                  hipStream_t s)
@@ -279,7 +289,7 @@ int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPat
         }
     }
     const bool ordered = path == BwdPath::ordered;
-    if constexpr (!is_array_src<Src>::value) {
+    if constexpr (is_recompute_src<Src>::value) {
         // index-free, any order: the column stages recompute the argmax
         RcPlan rp;
         if (!ordered && plan_rc(g, (int)sizeof(typename T::raw), (int)sizeof(typename T::acc),
@@ -294,10 +304,14 @@ int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPat
     }
     BwdPlan p;
     if (plan_backward(g, ordered, (int)sizeof(typename T::acc), &p)) {
+
         if (log_enabled())
             fprintf(stderr, "[mp3d] backward %s%s dtype=%d box=(%d,%d,%d) tiles=%lld lds=%u phases=%d\n",
                     ordered ? "ordered slab" : "accumulate",
-                    is_array_src<Src>::value ? "" : " (argmax recomputed)", T::code, p.td, p.th,
+                    is_array_src<Src>::value ? "" : is_recompute_src<Src>::value
+                                                        ? " (argmax recomputed)"
+                                                        : " (argmax checked)",
+                    T::code, p.td, p.th,
                     p.tw, (long long)p.ntiles, p.lds_bytes, p.nphase);
         return hip_status(launch_backward_tile<T, Src>(gy, src, gx, p, s), "backward tile launch");
     }
@@ -323,6 +337,33 @@ IdxRecompute<T> recompute_src(const void *x, const void *y, const Geom &g)
     r.ow_div = FastDiv((uint32_t)g.ax[2].O);
     r.oh_div = FastDiv((uint32_t)g.ax[1].O);
     return r;
+}
+
+template <typename T>
+IdxChecked<T> checked_src(const void *x, const void *y, const void *yf, const int32_t *idxf,
+                          const Geom &g)
+{
+    IdxChecked<T> r;
+    r.idxf = idxf;
+    r.yf = (const typename T::raw *)yf;
+    r.x = (const typename T::raw *)x;
+    r.y = (const typename T::raw *)y;
+    r.g = g;
+    r.ow_div = FastDiv((uint32_t)g.ax[2].O);
+    r.oh_div = FastDiv((uint32_t)g.ax[1].O);
+    return r;
+}
+
+// Workspace of the two-pass index-free backward: the forward's maximum
+// (storage type) then its int32 argmax, each part starting on 256 bytes.
+struct WsLayout {
+    size_t y_bytes, bytes;
+};
+
+WsLayout ws_layout(int64_t outputs, int es)
+{
+    const size_t yb = ((size_t)outputs * (size_t)es + 255) & ~(size_t)255;
+    return {yb, yb + (size_t)outputs * 4};
 }
 
 // Windows tile an axis -- each position in exactly one window, the one
@@ -363,8 +404,12 @@ int set_axes_ex(Geom *g, int64_t D, int64_t H, int64_t W, int32_t od, int32_t oh
 
 // Shared by the backward entry points.  idx_type < 0: no index array, the
 // argmax is recomputed from x and y (x, y then required).
+// A workspace (ws, with idx_type < 0) takes the two-pass index-free
+// backward: the forward into the workspace, then the argmax checked
+// against y.
 int backward(const void *gy, const void *idx, int idx_type, const void *x, const void *y,
-             void *gx, int dtype, Geom &g, int64_t N, int64_t C, int overlap, hipStream_t s)
+             void *gx, int dtype, Geom &g, int64_t N, int64_t C, int overlap, hipStream_t s,
+             void *ws = nullptr, size_t ws_bytes = 0)
 {
     int rc;
     if (overlap < -1 || overlap > 2)
@@ -384,6 +429,31 @@ int backward(const void *gy, const void *idx, int idx_type, const void *x, const
         // with windows that tile, every input has at most one contribution:
         // the accumulate path gives the gather's (and the ordered) result
         const BwdPath rp = path == BwdPath::ordered ? BwdPath::ordered : BwdPath::accumulate;
+        const int es = dtype == MP3D_F64 ? 8 : dtype == MP3D_F32 ? 4 : 2;
+        const WsLayout L = ws_layout(g.planes * (int64_t)g.out_plane, es);
+        if (ws && ws_bytes < L.bytes)
+            return fail(MP3D_EINVAL, "workspace of %zu bytes; this call needs %zu", ws_bytes,
+                        L.bytes);
+        // the two-pass form, except for small tensors (one launch instead
+        // of two) and where the fused one-pass kernel takes slabs of 4
+        // slices or more (there it measured as fast or faster: each window
+        // is recomputed by few slabs)
+        RcPlan rcp;
+        const bool small = g.planes * (int64_t)g.in_plane < ((int64_t)1 << 22);
+        const bool fused_wide = rp != BwdPath::ordered &&
+                                plan_rc(g, es, es == 8 ? 8 : 4, x, &rcp) && rcp.td >= 4;
+        if (ws && (two_pass_forced() || (!small && !fused_wide))) {
+            if (log_enabled()) fprintf(stderr, "[mp3d] index-free backward: two passes\n");
+            void *yf = ws;
+            int32_t *idxf = (int32_t *)((char *)ws + L.y_bytes);
+            if ((rc = forward(x, yf, idxf, MP3D_IDX_I32, dtype, g, s))) return rc;
+            switch (dtype) {
+            case MP3D_F32: return run_backward<F32>(gy, checked_src<F32>(x, y, yf, idxf, g), gx, g, rp, s);
+            case MP3D_F16: return run_backward<F16>(gy, checked_src<F16>(x, y, yf, idxf, g), gx, g, rp, s);
+            case MP3D_F64: return run_backward<F64>(gy, checked_src<F64>(x, y, yf, idxf, g), gx, g, rp, s);
+            default: return run_backward<BF16>(gy, checked_src<BF16>(x, y, yf, idxf, g), gx, g, rp, s);
+            }
+        }
         switch (dtype) {
         case MP3D_F32: return run_backward<F32>(gy, recompute_src<F32>(x, y, g), gx, g, rp, s);
         case MP3D_F16: return run_backward<F16>(gy, recompute_src<F16>(x, y, g), gx, g, rp, s);
@@ -567,6 +637,37 @@ int mp3d_backward_recompute(const void *x, const void *y, const void *gy, void *
     Geom g;
     if ((rc = set_axes_ex(&g, D, H, W, od, oh, ow, kernel, stride, pad, dilation))) return rc;
     return backward(gy, nullptr, -1, x, y, gx, dtype, g, N, C, overlap, (hipStream_t)stream);
+}
+
+int mp3d_recompute_workspace_size(int dtype, int64_t N, int64_t C, int32_t od, int32_t oh,
+                                  int32_t ow, size_t *bytes)
+{
+    if (!bytes) return fail(MP3D_EINVAL, "bytes is NULL");
+    if (dtype < MP3D_F32 || dtype > MP3D_F64)
+        return fail(MP3D_EDTYPE, "dtype %d is not one of MP3D_F32/F16/BF16/F64", dtype);
+    if (N < 0 || C < 0 || od <= 0 || oh <= 0 || ow <= 0)
+        return fail(MP3D_EINVAL, "N, C must be >= 0 and the output extents >= 1");
+    const int64_t per = (int64_t)od * oh * ow;
+    if (per > kInt32Max || (N && C && (N > INT64_MAX / C || N * C > (INT64_MAX / 16) / per)))
+        return fail(MP3D_EOVERFLOW, "output size out of range");
+    const int es = dtype == MP3D_F64 ? 8 : dtype == MP3D_F32 ? 4 : 2;
+    *bytes = ws_layout(N * C * per, es).bytes;
+    return MP3D_OK;
+}
+
+int mp3d_backward_recompute_ws(const void *x, const void *y, const void *gy, void *gx, int dtype,
+                               int64_t N, int64_t C, int64_t D, int64_t H, int64_t W, int32_t od,
+                               int32_t oh, int32_t ow, const int32_t *kernel,
+                               const int32_t *stride, const int32_t *pad,
+                               const int32_t *dilation, int overlap, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    int rc = check_common(dtype, N, C, D, H, W);
+    if (rc) return rc;
+    Geom g;
+    if ((rc = set_axes_ex(&g, D, H, W, od, oh, ow, kernel, stride, pad, dilation))) return rc;
+    return backward(gy, nullptr, -1, x, y, gx, dtype, g, N, C, overlap, (hipStream_t)stream,
+                    workspace, workspace_bytes);
 }
 
 

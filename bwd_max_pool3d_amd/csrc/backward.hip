@@ -162,21 +162,62 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
 
     int32_t ri[kRound];
     R rg[kRound];
+    // the first round's windows: their loads are in flight during the zero
+    // fill.  A two-phase source's loads are resolved only after it
+    // (settle): a branch between the loads of two windows would make each
+    // wait for the one before.
+    typename pending_of<Src>::type q[kRound];
     auto fetch = [&](int32_t round) {
 #pragma unroll
         for (int k = 0; k < kRound; ++k) {
             const int32_t e = (round * kRound + k) * NT + tid;
-            ri[k] = -1;
-            if (e < nw) {
-                ri[k] = src(wbase + e);
-                rg[k] = gy[wbase + e];
+            if constexpr (two_phase_src<Src>::value) {
+                if (e < nw) {
+                    q[k] = src.load(wbase + e);
+                    rg[k] = gy[wbase + e];
+                }
+            } else {
+                ri[k] = -1;
+                if (e < nw) {
+                    ri[k] = src(wbase + e);
+                    rg[k] = gy[wbase + e];
+                }
             }
         }
     };
-    fetch(0);                                   // in flight during the zero fill
+    auto settle = [&](int32_t round) {
+        if constexpr (two_phase_src<Src>::value) {
+#pragma unroll
+            for (int k = 0; k < kRound; ++k) Src::pin(q[k]);
+            uint32_t miss = 0;
+#pragma unroll
+            for (int k = 0; k < kRound; ++k) {
+                const int32_t e = (round * kRound + k) * NT + tid;
+                ri[k] = -1;
+                if (e < nw) {
+                    ri[k] = q[k].idx;
+                    if (!Src::settled(q[k])) miss |= 1u << k;
+                }
+            }
+            if (miss) {
+#pragma unroll
+                for (int k = 0; k < kRound; ++k)
+                    if (miss >> k & 1u) ri[k] = src.rescan(wbase + (round * kRound + k) * NT + tid);
+            }
+        }
+    };
+    fetch(0);
     for (int32_t e = tid; e < (n + shift + AE - 1) / AE; e += NT)
         reinterpret_cast<u32x4 *>(acc)[e] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
+    settle(0);
+    if constexpr (ORD && !two_phase_src<Src>::value) {
+        // keeps the class computation below the barrier: hoisted above it,
+        // it makes the wave wait for its loads before the barrier instead of
+        // behind it
+#pragma unroll
+        for (int k = 0; k < kRound; ++k) asm volatile("" : "+v"(ri[k]));
+    }
     if constexpr (ORD) {
         const Axis B = p.g.ax[1], Cw = p.g.ax[2];
         const uint32_t W = (uint32_t)Cw.X, OW = (uint32_t)Cw.O;
@@ -222,7 +263,21 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
                 if (ri[k] >= 0 && l < (uint32_t)n) lds_add(&a[l], T::widen(rg[k]));
             }
             if ((round + 1) * kRound * NT >= nw) break;
-            fetch(round + 1);
+            if constexpr (two_phase_src<Src>::value) {
+                // later rounds (slabs reached by more windows than one
+                // round holds) ask each window in one call
+#pragma unroll
+                for (int k = 0; k < kRound; ++k) {
+                    const int32_t e = ((round + 1) * kRound + k) * NT + tid;
+                    ri[k] = -1;
+                    if (e < nw) {
+                        ri[k] = src(wbase + e);
+                        rg[k] = gy[wbase + e];
+                    }
+                }
+            } else {
+                fetch(round + 1);
+            }
         }
         __syncthreads();
     }
@@ -235,33 +290,13 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
 // window reaching the slab its first maximum (the first NaN when it holds
 // one); where that element equals y[o], every tap equal to y[o] is a
 // maximum, so the first of them is that element.  Elsewhere -- y not the
-// window's maximum -- the window is scanned in memory (rc_scan).  The LDS
+// window's maximum -- the window is scanned in memory.  The LDS
 // that held the D-partials then becomes the slab's accumulator, as in the
 // slab kernel.
 //
-// The fallback scan is a plain loop over the window's in-range taps (one
-// load at a time): it runs only where y is not the window's maximum, and
-// adds few registers to those of the common path.
-template <typename T>
-__device__ __forceinline__ int32_t rc_scan(const typename T::raw *xp, const Geom &g,
-                                                     int32_t od, int32_t oh, int32_t ow,
-                                                     typename T::acc want)
-{
-    const Taps td = window_taps(g.ax[0], od), th = window_taps(g.ax[1], oh);
-    const Taps tw = window_taps(g.ax[2], ow);
-    const int32_t H = g.ax[1].X, W = g.ax[2].X;
-    const bool nan = want != want;
-    for (int32_t a = td.j0; a <= td.j1; ++a)
-        for (int32_t b = th.j0; b <= th.j1; ++b) {
-            const int32_t row = ((td.b + a * td.t) * H + th.b + b * th.t) * W + tw.b;
-            for (int32_t c = tw.j0; c <= tw.j1; ++c) {
-                const typename T::acc v = T::widen(xp[row + c * tw.t]);
-                if (nan ? v != v : v == want) return row + c * tw.t;
-            }
-        }
-    return -1;
-}
-
+// The fallback scan (scan_first_equal, a plain loop) runs only where y is
+// not the window's maximum, and adds few registers to those of the common
+// path.
 template <typename T, int MAXKD, int NT, int KS, int KHW>
 __global__ void __launch_bounds__(NT)
 bwd_rc_kernel(const typename T::raw *__restrict__ x, const typename T::raw *__restrict__ y,
@@ -341,7 +376,7 @@ bwd_rc_kernel(const typename T::raw *__restrict__ x, const typename T::raw *__re
             const Acc want = T::widen(ry[k]);
             const bool same = want != want ? best != best : best == want;
             ri[k] = same ? (A.start(od0 + (int32_t)odl) + (int32_t)(bk >> 24)) * HW + bi
-                         : rc_scan<T>(xp, p.g, od0 + (int32_t)odl, oh, ow, want);
+                         : scan_first_equal<T>(xp, p.g, od0 + (int32_t)odl, oh, ow, want);
         }
     }
     __syncthreads();                                     // the D-partials are consumed
@@ -519,15 +554,19 @@ hipError_t launch_backward_gather(const void *gy, const Src &src, void *gx, cons
 template hipError_t launch_backward_tile<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F32, IdxRecompute<F32>>(const void *, const IdxRecompute<F32> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F32, IdxChecked<F32>>(const void *, const IdxChecked<F32> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F16, IdxRecompute<F16>>(const void *, const IdxRecompute<F16> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F16, IdxChecked<F16>>(const void *, const IdxChecked<F16> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<BF16, IdxRecompute<BF16>>(const void *, const IdxRecompute<BF16> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<BF16, IdxChecked<BF16>>(const void *, const IdxChecked<BF16> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_tile<F64, IdxRecompute<F64>>(const void *, const IdxRecompute<F64> &, void *, const BwdPlan &, hipStream_t);
+template hipError_t launch_backward_tile<F64, IdxChecked<F64>>(const void *, const IdxChecked<F64> &, void *, const BwdPlan &, hipStream_t);
 template hipError_t launch_backward_rc<F32>(const void *, const void *, const void *, void *, const RcPlan &, hipStream_t);
 template hipError_t launch_backward_rc<F16>(const void *, const void *, const void *, void *, const RcPlan &, hipStream_t);
 template hipError_t launch_backward_rc<BF16>(const void *, const void *, const void *, void *, const RcPlan &, hipStream_t);

@@ -5,10 +5,12 @@
 // recomputed from the forward's input and output, which lets a caller run
 // the values-only forward and keep no index at all (the teenygrad kernel ABI
 // passes no index buffer, "Struct Maxpool3dForward", Kernel trait; its
-// backward receives the forward's inputs and output, RuntimeOp).
+// backward receives the forward's inputs and output, RuntimeOp), or is
+// taken from a forward run into a caller's workspace and checked against y.
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "dtype.hpp"
 #include "kernels.hpp"
@@ -115,6 +117,101 @@ struct IdxRecompute {
         }
         return -1;
     }
+};
+
+// The first tap of window (od, oh, ow) of one plane (xp) equal to want, in
+// d, h, w scan order (the first NaN when want is NaN); -1 if none is.  A
+// plain loop over the window's in-range taps, one load at a time: it serves
+// the windows whose y is not their maximum, which are rare, and keeps the
+// callers' common path small.
+template <typename T>
+__device__ __forceinline__ int32_t scan_first_equal(const typename T::raw *xp, const Geom &g,
+                                                    int32_t od, int32_t oh, int32_t ow,
+                                                    typename T::acc want)
+{
+    const Taps td = window_taps(g.ax[0], od), th = window_taps(g.ax[1], oh);
+    const Taps tw = window_taps(g.ax[2], ow);
+    const int32_t H = g.ax[1].X, W = g.ax[2].X;
+    const bool nan = want != want;
+    for (int32_t a = td.j0; a <= td.j1; ++a)
+        for (int32_t b = th.j0; b <= th.j1; ++b) {
+            const int32_t row = ((td.b + a * td.t) * H + th.b + b * th.t) * W + tw.b;
+            for (int32_t c = tw.j0; c <= tw.j1; ++c) {
+                const typename T::acc v = T::widen(xp[row + c * tw.t]);
+                if (nan ? v != v : v == want) return row + c * tw.t;
+            }
+        }
+    return -1;
+}
+
+// Recomputed from x and y by way of the forward's own argmax and maximum
+// (idxf, yf: the forward run on x into a caller's workspace).  Where y[o]
+// equals yf[o] (both NaN, or equal as numbers) every tap equal to y[o] is a
+// maximum of the window, so the first of them is the forward's argmax (the
+// first maximum; the first NaN when the window holds one); elsewhere the
+// window is scanned in x.  The same result as IdxRecompute, for three
+// streamed loads per window in the common case.
+template <typename T>
+struct IdxChecked {
+    static constexpr int kSlots = kBwdRound;   // windows per thread per slab round
+    const int32_t *idxf;
+    const typename T::raw *yf;
+    const typename T::raw *x;
+    const typename T::raw *y;
+    Geom g;
+    FastDiv ow_div, oh_div;    // by OW, then by OH
+
+    // Two phases, so that a caller with several windows in hand issues
+    // every window's loads before the first compare: load (no branch), then
+    // settled (the common case: the forward's argmax stands) or rescan
+    // (the window scanned in x; it loads y[o] again, so that nothing of a
+    // window is held across the scans of the others).
+    // 16-bit storage is held widened to 32 bits as loaded (a whole register)
+    using Word = std::conditional_t<(sizeof(typename T::raw) < 4), uint32_t, typename T::raw>;
+    struct Pending {
+        Word y, yf;
+        int32_t idx;
+    };
+    __device__ __forceinline__ Pending load(int64_t o) const {
+        return {(Word)y[o], (Word)yf[o], idxf[o]};
+    }
+    // Pins a pending window's values at this point of the program: a
+    // caller that passed a barrier since load calls it first, so that the
+    // compares that follow stay below the barrier (hoisted above it, they
+    // make the wave wait for its loads before the barrier instead of
+    // behind it).
+    __device__ __forceinline__ static void pin(Pending &q) {
+        asm volatile("" : "+v"(q.y), "+v"(q.yf), "+v"(q.idx));
+    }
+    __device__ __forceinline__ static bool settled(const Pending &q) {
+        using A = typename T::acc;
+        using R = typename T::raw;
+        const A want = T::widen((R)q.y), got = T::widen((R)q.yf);
+        return want != want ? got != got : got == want;
+    }
+    __device__ __forceinline__ int32_t rescan(int64_t o) const {
+        const typename T::acc want = T::widen(y[o]);
+        const int64_t plane = o / g.out_plane;
+        const uint32_t r0 = (uint32_t)(o - plane * g.out_plane);
+        const uint32_t r = ow_div.div(r0);
+        const uint32_t od = oh_div.div(r);
+        return scan_first_equal<T>(x + plane * (int64_t)g.in_plane, g, (int32_t)od,
+                                   (int32_t)(r - od * (uint32_t)g.ax[1].O),
+                                   (int32_t)(r0 - r * (uint32_t)g.ax[2].O), want);
+    }
+    __device__ __forceinline__ int32_t operator()(int64_t o) const {
+        const Pending q = load(o);
+        return settled(q) ? q.idx : rescan(o);
+    }
+};
+
+// Index sources that split a query into load and resolve, and what a
+// caller holds between the two (unused for the others).
+template <typename S> struct two_phase_src : std::false_type {};
+template <typename T> struct two_phase_src<IdxChecked<T>> : std::true_type {};
+template <typename S, typename = void> struct pending_of { using type = int32_t; };
+template <typename S> struct pending_of<S, std::void_t<typename S::Pending>> {
+    using type = typename S::Pending;
 };
 
 }  // namespace mp3d

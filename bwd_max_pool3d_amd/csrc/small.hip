@@ -210,22 +210,26 @@ hipError_t launch_backward_small(const void *gy, const Src &src, void *gx, const
 template hipError_t launch_backward_ordered<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<F32, IdxRecompute<F32>>(const void *, const IdxRecompute<F32> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F32, IdxChecked<F32>>(const void *, const IdxChecked<F32> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_small<F32, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_small<F32, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<F16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<F16, IdxRecompute<F16>>(const void *, const IdxRecompute<F16> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F16, IdxChecked<F16>>(const void *, const IdxChecked<F16> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_small<F16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_small<F16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<BF16, IdxRecompute<BF16>>(const void *, const IdxRecompute<BF16> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<BF16, IdxChecked<BF16>>(const void *, const IdxChecked<BF16> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_small<BF16, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_small<BF16, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
 
 template hipError_t launch_backward_ordered<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_ordered<F64, IdxRecompute<F64>>(const void *, const IdxRecompute<F64> &, void *, const OrdPlan &, hipStream_t);
+template hipError_t launch_backward_ordered<F64, IdxChecked<F64>>(const void *, const IdxChecked<F64> &, void *, const OrdPlan &, hipStream_t);
 template hipError_t launch_backward_small<F64, IdxArray<int32_t>>(const void *, const IdxArray<int32_t> &, void *, const SmallPlan &, hipStream_t);
 template hipError_t launch_backward_small<F64, IdxArray<int64_t>>(const void *, const IdxArray<int64_t> &, void *, const SmallPlan &, hipStream_t);
 

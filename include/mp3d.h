@@ -183,6 +183,40 @@ int mp3d_backward_recompute(const void *x, const void *y, const void *gy, void *
                             const int32_t *pad, const int32_t *dilation,
                             int overlap, void *stream);
 
+/* Bytes of workspace mp3d_backward_recompute_ws needs for N*C planes of
+ * od*oh*ow outputs of dtype: the forward's maximum in the storage type,
+ * rounded up to 256 bytes, then its int32 argmax.  Into *bytes. */
+int mp3d_recompute_workspace_size(int dtype, int64_t N, int64_t C, int32_t od, int32_t oh,
+                                  int32_t ow, size_t *bytes);
+
+/* The index-free backward of mp3d_backward_recompute (same arguments, same
+ * result bit for bit in the ordered mode and within the same bounds
+ * otherwise) in two passes through a caller's device workspace: the
+ * forward runs on x into the workspace (its maximum yf and argmax), then
+ * the backward takes the argmax of window o from there wherever y[o]
+ * equals yf[o] (both NaN, or equal as numbers: then every tap equal to
+ * y[o] is a maximum of the window and the first of them is the forward's
+ * argmax) and scans window o of x where it does not.  For callers who can
+ * lend transient device memory (a fraction of x: yf and an int32 per
+ * output) but keep no index between forward and backward; faster than
+ * the one-pass form where windows overlap and slabs of gx are thin.
+ * workspace: device memory of workspace_bytes >=
+ * mp3d_recompute_workspace_size(...), overlapping none of x, y, gy, gx;
+ * its contents on entry do not matter and are overwritten; the caller
+ * owns it and may reuse it once the stream has passed this call.
+ * workspace NULL: the one-pass mp3d_backward_recompute.  A smaller
+ * workspace_bytes: MP3D_EINVAL.  The one-pass form still runs, and the
+ * workspace stays untouched, where it measured as fast: tensors under 2^22
+ * elements, and geometries whose one-pass slabs hold 4 or more slices of
+ * gx (environment MP3D_TWO_PASS=1 takes two passes regardless). */
+int mp3d_backward_recompute_ws(const void *x, const void *y, const void *gy, void *gx, int dtype,
+                               int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                               int32_t od, int32_t oh, int32_t ow,
+                               const int32_t *kernel, const int32_t *stride,
+                               const int32_t *pad, const int32_t *dilation,
+                               int overlap, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 /* Output extent into *out.  ceil_mode 0: (X + 2*pad - span)/s + 1, rounded
  * down.  ceil_mode 1: rounded up, less one if that last window would start
  * at or beyond X + pad (so every window starts inside the input or the

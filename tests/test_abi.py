@@ -170,3 +170,43 @@ def test_strerror_covers_every_code():
     texts = {lib.mp3d_strerror(c).decode() for c in range(6)}
     assert len(texts) == 6
     assert lib.mp3d_strerror(99).decode() == "unknown status"
+
+
+def _ws_size(dtype, N, C, out):
+    import ctypes
+    v = ctypes.c_size_t(0)
+    rc = _lib.load().mp3d_recompute_workspace_size(dtype, N, C, *out, ctypes.byref(v))
+    return rc, v.value
+
+
+def test_recompute_workspace_size():
+    """The forward's maximum (storage bytes, rounded up to 256) then one
+    int32 per output; host arithmetic only."""
+    r256 = lambda b: (b + 255) // 256 * 256
+    for dtype, es in ((_lib.MP3D_F32, 4), (_lib.MP3D_F16, 2), (_lib.MP3D_BF16, 2),
+                      (_lib.MP3D_F64, 8)):
+        for N, C, out in ((1, 1, (1, 1, 1)), (2, 3, (5, 7, 7)), (8, 128, (15, 27, 27)),
+                          (0, 4, (2, 2, 2))):
+            n = N * C * out[0] * out[1] * out[2]
+            assert _ws_size(dtype, N, C, out) == (_lib.MP3D_OK, r256(n * es) + 4 * n)
+    assert _ws_size(4, 1, 1, (1, 1, 1))[0] == _lib.MP3D_EDTYPE
+    assert _ws_size(_lib.MP3D_F32, 1, 1, (0, 1, 1))[0] == _lib.MP3D_EINVAL
+    assert _ws_size(_lib.MP3D_F32, -1, 1, (1, 1, 1))[0] == _lib.MP3D_EINVAL
+    assert _ws_size(_lib.MP3D_F32, 1 << 40, 1 << 20, (4, 4, 4))[0] == _lib.MP3D_EOVERFLOW
+
+
+def test_recompute_ws_empty_batch_and_checks():
+    """Argument checks of the workspace form before any launch: an empty
+    batch is a no-op (null pointers allowed), and a bad overlap or dtype is
+    refused."""
+    import ctypes
+    lib = _lib.load()
+    a3 = lambda v: (ctypes.c_int32 * 3)(*v)
+    call = lambda dtype=_lib.MP3D_F32, shape=(0, 2, 6, 6, 6), overlap=-1: \
+        lib.mp3d_backward_recompute_ws(None, None, None, None, dtype, *shape, 3, 3, 3,
+                                       a3((2, 2, 2)), a3((2, 2, 2)), a3((0, 0, 0)),
+                                       a3((1, 1, 1)), overlap, None, 0, None)
+    assert call() == _lib.MP3D_OK
+    assert call(overlap=3) == _lib.MP3D_EINVAL
+    assert call(dtype=7) == _lib.MP3D_EDTYPE
+    assert call(shape=(1, 2, 6, 6, 6)) == _lib.MP3D_EINVAL      # null tensors

@@ -9,7 +9,8 @@ same kernel (2 or 3) and stride 2, with padding and rounding still drawn
 per axis.  On each case: the forward (indices and
 values only) must equal the oracle's y bits and idx; the backward from idx
 (library's pick, accumulate, ordered) and the index-free backward (any
-order, ordered) must meet the bar of the hand-picked cases.  The windows
+order, ordered; one-pass and through a workspace) must meet the bar of
+the hand-picked cases.  The windows
 follow the definitions of "Struct Maxpool3dForward" (teenygrad,
 description) and the PR #308 page (Summary); padding, dilation and ceil
 rounding follow the pooling output-size rule the oracle pins to torch.
@@ -105,14 +106,18 @@ def _backward(gy, idx, c, overlap):
     return gx
 
 
-def _recompute(x, y, gy, c, overlap):
+def _recompute(x, y, gy, c, overlap, ws=None):
     lib = _lib.load()
     gx = torch.empty_like(x)
     k, s, p, d = c["geo"]
-    _lib.check(lib.mp3d_backward_recompute(x.data_ptr(), y.data_ptr(), gy.data_ptr(),
-                                           gx.data_ptr(), _gpu.CODE[gy.dtype], *c["shape"],
-                                           *c["out"], _a3(k), _a3(s), _a3(p), _a3(d), overlap,
-                                           _stream()))
+    geo = (_gpu.CODE[gy.dtype],) + c["shape"] + c["out"] + (_a3(k), _a3(s), _a3(p), _a3(d))
+    if ws is None:
+        _lib.check(lib.mp3d_backward_recompute(x.data_ptr(), y.data_ptr(), gy.data_ptr(),
+                                               gx.data_ptr(), *geo, overlap, _stream()))
+    else:
+        _lib.check(lib.mp3d_backward_recompute_ws(x.data_ptr(), y.data_ptr(), gy.data_ptr(),
+                                                  gx.data_ptr(), *geo, overlap, ws.data_ptr(),
+                                                  ws.numel(), _stream()))
     return gx
 
 
@@ -163,7 +168,12 @@ def test_random_geometry(orc, i, monkeypatch):
                             what="%s backward overlap=%d" % (what, overlap))
     ia = orc.argmax_from_output(_gpu.storage(x), _gpu.storage(y), code, k, s, p, d)
     assert np.array_equal(ia, io), "%s: argmax from (x, y) differs from the forward's" % what
+    ws = torch.empty(mp.recompute_workspace_size(x.dtype, *c["shape"][:2], c["out"]),
+                     dtype=torch.uint8, device=x.device)
+    monkeypatch.setenv("MP3D_TWO_PASS", "1")       # the two-pass form on these small shapes
     for overlap, exact in ((-1, False), (2, True)):
-        gx = _recompute(x, y, gy, c, overlap)
-        _gpu.check_backward(orc, gy.cpu(), idx32, c["shape"], gx, exact=exact,
-                            what="%s index-free overlap=%d" % (what, overlap))
+        for w in (None, ws):
+            gx = _recompute(x, y, gy, c, overlap, w)
+            _gpu.check_backward(orc, gy.cpu(), idx32, c["shape"], gx, exact=exact,
+                                what="%s index-free overlap=%d%s" % (
+                                    what, overlap, " workspace" if w is not None else ""))

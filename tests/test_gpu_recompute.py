@@ -4,6 +4,8 @@ to its backward.  With y from the values-only forward this is the whole
 index-free pipeline; y that disagrees with x drops those windows."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -78,9 +80,22 @@ def _oracle_argmax(orc, x, y, case):
     return orc.argmax_from_output(xs, ys, code, k, s, p, d)
 
 
+@pytest.fixture(params=["one-pass", "two-pass"])
+def ws(request, monkeypatch):
+    """'two-pass': a workspace, and MP3D_TWO_PASS=1 so that the forward into
+    it and the checked argmax run on every shape (the library keeps small
+    tensors on the one-pass form by itself)."""
+    if request.param == "one-pass":
+        return False
+    monkeypatch.setenv("MP3D_TWO_PASS", "1")
+    return True
+
+
 @pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
 @pytest.mark.parametrize("case", CASES, ids=_cid)
-def test_recompute_backward(orc, case, dtype):
+def test_recompute_backward(orc, case, dtype, ws):
+    """Both forms: the one-pass kernels, and the forward into a workspace
+    with its argmax checked against y."""
     shape = case[0]
     code = _gpu.CODE[dtype]
     base = abs(hash(case)) % 10000
@@ -91,14 +106,16 @@ def test_recompute_backward(orc, case, dtype):
         ia = _oracle_argmax(orc, x.cpu(), y.cpu(), case)
         ref_idx = torch.from_numpy(ia.astype(np.int32))
         for overlap, exact in ((-1, False), (2, True)):
-            gx = mp.mp3d_backward_recompute(x, y, gy, overlap=overlap, **_geom(case))
+            gx = mp.mp3d_backward_recompute(x, y, gy, overlap=overlap, workspace=ws,
+                                            **_geom(case))
             _gpu.check_backward(orc, gy.cpu(), ref_idx, shape, gx, exact=exact,
                                 what="%s %s overlap=%d" % (_cid(case), kind, overlap))
 
 
-def test_recompute_y_not_from_forward(orc):
+def test_recompute_y_not_from_forward(orc, ws):
     """Windows whose y matches no element of the window contribute nothing;
-    the others route to the first match."""
+    the others route to the first match (with a workspace: the windows
+    where y is not the forward's maximum take the scan)."""
     case = ((1, 2, 9, 8, 7), None, (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), False)
     x = _pins.from_storage(_pins.draw(case[0], 0, "ties", 77), 0).cuda()
     y = _forward_values(x, case).clone()
@@ -110,7 +127,7 @@ def test_recompute_y_not_from_forward(orc):
     assert (ia < 0).sum() > 0 and (ia >= 0).sum() > 0
     ref_idx = torch.from_numpy(ia.astype(np.int32))
     for overlap, exact in ((-1, False), (1, False), (2, True)):
-        gx = mp.mp3d_backward_recompute(x, y, gy, overlap=overlap, **_geom(case))
+        gx = mp.mp3d_backward_recompute(x, y, gy, overlap=overlap, workspace=ws, **_geom(case))
         _gpu.check_backward(orc, gy.cpu(), ref_idx, case[0], gx, exact=exact,
                             what="perturbed y overlap=%d" % overlap)
 
@@ -136,6 +153,17 @@ def test_recompute_full_size(orc, wl):
     got = mp.mp3d_backward_recompute(xd, y, gy, overlap=2, **geo)
     iv = torch.int32 if got.element_size() == 4 else torch.int16
     assert torch.equal(got.view(iv), ref.view(iv)), wl.name
+    ws = torch.empty(mp.recompute_workspace_size(xd.dtype, *wl.shape[:2], tuple(y.shape[2:])),
+                     dtype=torch.uint8, device=xd.device)
+    got = mp.mp3d_backward_recompute(xd, y, gy, overlap=2, workspace=ws, **geo)
+    assert torch.equal(got.view(iv), ref.view(iv)), wl.name + " workspace"
+    os.environ["MP3D_TWO_PASS"] = "1"      # the two-pass form on every workload
+    try:
+        got = mp.mp3d_backward_recompute(xd, y, gy, overlap=2, workspace=ws, **geo)
+        assert torch.equal(got.view(iv), ref.view(iv)), wl.name + " two-pass"
+        gxw = mp.mp3d_backward_recompute(xd, y, gy, workspace=ws, **geo)
+    finally:
+        del os.environ["MP3D_TWO_PASS"]
     del ref, got
     gx = mp.mp3d_backward_recompute(xd, y, gy, **geo)
     torch.cuda.synchronize()
@@ -146,6 +174,19 @@ def test_recompute_full_size(orc, wl):
     for p in planes:
         n_, c_ = divmod(p, C)
         sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
-        _gpu.check_backward(orc, gyc[sl].contiguous(), idx[sl].cpu().contiguous(), (1, 1, D, H, W),
-                            gx[sl], exact=False, what="%s index-free plane %d" % (wl.name, p))
+        for g, form in ((gx, "one-pass"), (gxw, "two-pass")):
+            _gpu.check_backward(orc, gyc[sl].contiguous(), idx[sl].cpu().contiguous(),
+                                (1, 1, D, H, W), g[sl], exact=False,
+                                what="%s index-free %s plane %d" % (wl.name, form, p))
     _gpu.full_backward_property(gy, idx, gx, wl.shape)
+    _gpu.full_backward_property(gy, idx, gxw, wl.shape)
+
+
+def test_recompute_workspace_too_small():
+    """A workspace smaller than the size query is refused before any launch."""
+    x = torch.zeros((1, 2, 6, 6, 6), dtype=torch.float32, device="cuda")
+    y = mp.amp3d_forward(x, (3, 3, 3), indices=False)
+    need = mp.recompute_workspace_size(torch.float32, 1, 2, (3, 3, 3))
+    ws = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mp.Mp3dError, match="workspace"):
+        mp.mp3d_backward_recompute(x, y, torch.ones_like(y), workspace=ws)
