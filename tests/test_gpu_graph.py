@@ -80,3 +80,64 @@ def test_graph_replay(case, overlap):
                 # any order: the same sums up to the order of the additions
                 assert bool(torch.isfinite(gx.float()).all()), "replay %d input %d: gx" % (rep, i)
                 torch.testing.assert_close(gx.float(), rgx.float(), rtol=1e-2, atol=1e-3)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-%s" % ("x".join(map(str, c[0])),
+                                                                 str(c[1]).split(".")[-1]))
+@pytest.mark.parametrize("form", ["one-pass", "two-pass"])
+def test_graph_replay_index_free(case, form, monkeypatch):
+    """The values-only forward and the index-free backward (one pass, or two
+    through a workspace the caller allocated before capture) under capture:
+    every replay equals the eager calls bit for bit (ordered mode)."""
+    shape, dt, k, s, out = case
+    if form == "two-pass":
+        monkeypatch.setenv("MP3D_TWO_PASS", "1")
+    g = torch.Generator().manual_seed(12)
+    xs = [torch.randn(shape, generator=g).to(dt).cuda() for _ in range(3)]
+    x = xs[0].clone()
+    y = mp.mp3d_forward(x, k, s, indices=False) if k else mp.amp3d_forward(x, out, indices=False)
+    gy = torch.randn(tuple(y.shape), generator=g).to(dt).cuda()
+    gx = torch.empty_like(x)
+    ws = None
+    if form == "two-pass":
+        ws = torch.empty(mp.recompute_workspace_size(dt, *shape[:2], tuple(y.shape[2:])),
+                         dtype=torch.uint8, device="cuda")
+    geo = dict(kernel=k, stride=s) if k else dict(kernel=None)
+
+    def step():
+        if k:
+            mp.mp3d_forward(x, k, s, out=y, indices=False)
+        else:
+            mp.amp3d_forward(x, out, out=y, indices=False)
+        mp.mp3d_backward_recompute(x, y, gy, overlap=2, out=gx, workspace=ws, **geo)
+
+    refs = []
+    for xi in xs:
+        x.copy_(xi)
+        step()
+        torch.cuda.synchronize()
+        refs.append((y.clone(), gx.clone()))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    for rep in range(2):
+        for i, xi in enumerate(xs):
+            x.copy_(xi)
+            y.fill_(0)
+            gx.fill_(float("nan"))
+            if ws is not None:
+                ws.fill_(0xFF)
+            graph.replay()
+            torch.cuda.synchronize()
+            ry, rgx = refs[i]
+            assert torch.equal(_bits(y), _bits(ry)), "replay %d input %d: y" % (rep, i)
+            assert torch.equal(_bits(gx), _bits(rgx)), "replay %d input %d: gx" % (rep, i)
