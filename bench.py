@@ -134,6 +134,15 @@ def build_ops(torch, mp, workloads, variants=True):
             ord_ops.append(Op(wl, "bwd_recompute_ws", rw, nin * es + 2 * nout * es + nin * es,
                               nin, "index-free backward through a workspace (the forward into "
                               "it, its argmax checked against y)"))
+            ro = (lambda x=x, y=y, gy=gy, gx=gx, geo=geo: mp.mp3d_backward_recompute(
+                x, y, gy, out=gx, overlap=2, **geo))
+            ord_ops.append(Op(wl, "bwd_recompute_ordered", ro, nin * es + 2 * nout * es + nin * es,
+                              nin, "ordered index-free backward, one pass"))
+            rwo = (lambda x=x, y=y, gy=gy, gx=gx, geo=geo, ws=ws: mp.mp3d_backward_recompute(
+                x, y, gy, out=gx, overlap=2, workspace=ws, **geo))
+            ord_ops.append(Op(wl, "bwd_recompute_ws_ordered", rwo,
+                              nin * es + 2 * nout * es + nin * es, nin,
+                              "ordered index-free backward through a workspace"))
         if not variants:
             continue
         # int64 indices (torch's index type): general forward kernel
@@ -471,7 +480,7 @@ def main():
         "values_only_forward": [op_row(op, True) for op in vo_ops if op.kind == "fwd_values"],
         "ordered_backward": [op_row(op, True) for op in vo_ops if op.kind == "bwd_ordered"],
         "index_free_backward": [op_row(op, True) for op in vo_ops
-                                if op.kind in ("bwd_recompute", "bwd_recompute_ws")],
+                                if op.kind.startswith("bwd_recompute")],
         "int64_index_forward": [op_row(op, True) for op in vo_ops if op.kind == "fwd_i64"],
         "padded": [op_row(op, True) for op in vo_ops if op.kind in ("fwd_pad", "bwd_pad")],
         "float64": [op_row(op, True) for op in vo_ops
