@@ -434,6 +434,8 @@ int backward(const void *gy, const void *idx, int idx_type, const void *x, const
         if (ws && ws_bytes < L.bytes)
             return fail(MP3D_EINVAL, "workspace of %zu bytes; this call needs %zu", ws_bytes,
                         L.bytes);
+        if (ws && (uintptr_t)ws % 16)
+            return fail(MP3D_EINVAL, "workspace must be 16-byte aligned");
         // the two-pass form, except for small tensors (one launch instead
         // of two) and where the fused one-pass kernel takes slabs of 4
         // slices or more (there it measured as fast or faster: each window

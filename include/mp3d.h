@@ -201,7 +201,8 @@ int mp3d_recompute_workspace_size(int dtype, int64_t N, int64_t C, int32_t od, i
  * output) but keep no index between forward and backward; faster than
  * the one-pass form where windows overlap and slabs of gx are thin.
  * workspace: device memory of workspace_bytes >=
- * mp3d_recompute_workspace_size(...), overlapping none of x, y, gy, gx;
+ * mp3d_recompute_workspace_size(...), 16-byte aligned (else MP3D_EINVAL),
+ * overlapping none of x, y, gy, gx;
  * its contents on entry do not matter and are overwritten; the caller
  * owns it and may reuse it once the stream has passed this call.
  * workspace NULL: the one-pass mp3d_backward_recompute.  A smaller

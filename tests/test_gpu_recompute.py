@@ -183,10 +183,15 @@ def test_recompute_full_size(orc, wl):
 
 
 def test_recompute_workspace_too_small():
-    """A workspace smaller than the size query is refused before any launch."""
+    """A workspace smaller than the size query, or not 16-byte aligned, is
+    refused before any launch."""
     x = torch.zeros((1, 2, 6, 6, 6), dtype=torch.float32, device="cuda")
     y = mp.amp3d_forward(x, (3, 3, 3), indices=False)
     need = mp.recompute_workspace_size(torch.float32, 1, 2, (3, 3, 3))
     ws = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
     with pytest.raises(mp.Mp3dError, match="workspace"):
+        mp.mp3d_backward_recompute(x, y, torch.ones_like(y), workspace=ws)
+    # an unaligned workspace of enough bytes is refused too
+    ws = torch.empty(need + 16, dtype=torch.uint8, device="cuda")[1:]
+    with pytest.raises(mp.Mp3dError, match="aligned"):
         mp.mp3d_backward_recompute(x, y, torch.ones_like(y), workspace=ws)
