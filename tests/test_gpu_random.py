@@ -28,7 +28,7 @@ import _pins
 import bwd_max_pool3d_amd as mp
 from bwd_max_pool3d_amd import _lib
 
-N_CASES = 120
+N_CASES = 240
 DTYPES = [torch.float32, torch.float16, torch.bfloat16, torch.float64]
 KINDS = ["normal", "sparse_nan", "special", "zeros"]
 
