@@ -33,7 +33,8 @@ from ._lib import Mp3dError  # noqa: F401
 
 __all__ = ["mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
            "mp3d_forward_ex", "mp3d_backward_ex", "mp3d_out_size_ex",
-           "mp3d_backward_recompute", "recompute_workspace_size", "Mp3dError"]
+           "mp3d_backward_recompute", "recompute_workspace_size",
+           "mp3d_backward_workspace_bytes", "mp3d_time_next_call", "Mp3dError"]
 
 _IDX = {torch.int32: _lib.MP3D_IDX_I32, torch.int64: _lib.MP3D_IDX_I64}
 
@@ -247,6 +248,26 @@ def mp3d_backward_ex(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel, stri
                                     _IDX[idx.dtype], N, C, D, H, W, od, oh, ow, _arr3(k),
                                     _arr3(s), _arr3(pd), _arr3(dl), int(overlap), _stream(gy)))
     return out
+
+
+def mp3d_backward_workspace_bytes(dtype: torch.dtype, index_dtype, N: int, C: int,
+                                  out_size) -> int:
+    """Workspace bytes of a backward: 0 with an index array (index_dtype
+    torch.int32 or torch.int64), the two-pass size for the index-free
+    backward (index_dtype None)."""
+    it = _lib.MP3D_IDX_NONE if index_dtype is None else _IDX[index_dtype]
+    nbytes = ctypes.c_size_t()
+    _lib.check(_lib.load().mp3d_backward_workspace_bytes(_DTYPE[dtype], it, N, C,
+                                                         *_triple(out_size),
+                                                         ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def mp3d_time_next_call(start_event: int | None, stop_event: int | None) -> None:
+    """Arms kernel-time events (raw hipEvent_t handles) for the next call on
+    this thread: the start of its first kernel and the end of its last.
+    None, None disarms."""
+    _lib.check(_lib.load().mp3d_time_next_call(start_event, stop_event))
 
 
 def recompute_workspace_size(dtype: torch.dtype, N: int, C: int, out_size) -> int:

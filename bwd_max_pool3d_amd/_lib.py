@@ -11,14 +11,16 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libmp3d.so")
 
-MP3D_OK, MP3D_EINVAL, MP3D_EDTYPE, MP3D_ENOTDIV, MP3D_EOVERFLOW, MP3D_EHIP = range(6)
+(MP3D_OK, MP3D_EINVAL, MP3D_EDTYPE, MP3D_ENOTDIV, MP3D_EOVERFLOW, MP3D_EHIP,
+ MP3D_EWORKSPACE) = range(7)
 MP3D_F32, MP3D_F16, MP3D_BF16, MP3D_F64 = 0, 1, 2, 3
 
-MP3D_IDX_I32, MP3D_IDX_I64 = 0, 1
+MP3D_IDX_NONE, MP3D_IDX_I32, MP3D_IDX_I64 = -1, 0, 1
 
 EXPORTS = ("mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
            "mp3d_out_size_ex", "mp3d_forward_ex", "mp3d_backward_ex", "mp3d_backward_recompute",
-           "mp3d_recompute_workspace_size", "mp3d_backward_recompute_ws", "mp3d_strerror",
+           "mp3d_recompute_workspace_size", "mp3d_backward_recompute_ws",
+           "mp3d_backward_workspace_bytes", "mp3d_time_next_call", "mp3d_strerror",
            "mp3d_last_error")
 
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -66,6 +68,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mp3d_backward_recompute_ws.argtypes = ([_vp, _vp, _vp, _vp, ctypes.c_int] + [_i64] * 5
                                                + [_i32] * 3 + [_a3] * 4
                                                + [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
+    lib.mp3d_backward_workspace_bytes.argtypes = ([ctypes.c_int] * 2 + [_i64] * 2 + [_i32] * 3
+                                                  + [ctypes.POINTER(ctypes.c_size_t)])
+    lib.mp3d_time_next_call.argtypes = [_vp, _vp]
     lib.mp3d_strerror.argtypes = [ctypes.c_int]
     lib.mp3d_strerror.restype = ctypes.c_char_p
     lib.mp3d_last_error.argtypes = []
@@ -73,7 +78,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     for name in ("mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
                  "mp3d_out_size_ex", "mp3d_forward_ex", "mp3d_backward_ex",
                  "mp3d_backward_recompute", "mp3d_recompute_workspace_size",
-                 "mp3d_backward_recompute_ws"):
+                 "mp3d_backward_recompute_ws", "mp3d_backward_workspace_bytes",
+                 "mp3d_time_next_call"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -25,6 +25,15 @@ namespace {
 
 thread_local char g_msg[256] = "";
 
+// mp3d_time_next_call: events armed for the next call on this thread
+thread_local LaunchTiming g_timing = {nullptr, nullptr};
+
+// Disarms the kernel-time events when a C-ABI call returns, whether or not
+// it launched anything.
+struct TimingScope {
+    ~TimingScope() { g_timing = {nullptr, nullptr}; }
+};
+
 int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char *fmt, ...)
 {
@@ -179,15 +188,19 @@ int run_forward(const void *x, void *y, IT *idx, const Geom &g, hipStream_t s)
                     T::code, g.ax[0].k, g.ax[0].s, fp.nthreads, fp.vec_store);
         return hip_status(launch_forward_fixed<T, IT>(x, y, idx, fp, s), "forward fixed launch");
     }
+    // tiny tensors: one thread per output, every load at once, no barrier
+    // (latency, not bandwidth, is their cost)
+    SmallPlan sp;
+    const bool tiny = g.planes * (int64_t)g.in_plane <= kTinyInputs;
+    const bool small = small_enabled() && plan_small_forward(g, &sp);
     ColPlan cp;
-    if (plan_col(g, (int)sizeof(typename T::raw), x, &cp)) {
+    if (!(tiny && small) && plan_col(g, (int)sizeof(typename T::raw), x, &cp)) {
         if (log_enabled())
             fprintf(stderr, "[mp3d] forward column dtype=%d tod=%d tiles=%u maxkd=%d lds=%u\n",
                     T::code, cp.tod, cp.ntiles, cp.maxkd, cp.lds_bytes);
         return hip_status(launch_forward_col<T, IT>(x, y, idx, cp, s), "forward column launch");
     }
-    SmallPlan sp;
-    if (small_enabled() && plan_small_forward(g, &sp)) {
+    if (small) {
         if (log_enabled()) fprintf(stderr, "[mp3d] forward small dtype=%d outputs=%u\n", T::code, sp.total);
         return hip_status(launch_forward_small<T, IT>(x, y, idx, sp, s), "forward small launch");
     }
@@ -275,7 +288,8 @@ int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPat
 {
     if constexpr (is_array_src<Src>::value) {
         if (path == BwdPath::gather) {
-            GatherPlan p{g, g.ax[0].X / g.ax[0].O, g.ax[1].X / g.ax[1].O, g.ax[2].X / g.ax[2].O};
+            GatherPlan p;
+            plan_gather(g, &p);
             if (log_enabled()) fprintf(stderr, "[mp3d] backward gather dtype=%d\n", T::code);
             return hip_status(launch_backward_gather<T, Src>(gy, src, gx, p, s),
                               "backward gather launch");
@@ -289,6 +303,22 @@ int run_backward(const void *gy, const Src &src, void *gx, const Geom &g, BwdPat
         }
     }
     const bool ordered = path == BwdPath::ordered;
+    if constexpr (is_array_src<Src>::value) {
+        // The owner-gather slab gives the ascending-order fold, with no
+        // atomics and no phases: the ordered path takes it wherever it
+        // applies.  (As the accumulate path it measured slower than the
+        // compare-and-swap slab on both large overlapping workloads: 104
+        // against 94 us and 100 against 63 us.)
+        OwnerPlan op;
+        if (ordered && plan_owner(g, (int)sizeof(typename T::raw), &op)) {
+            if (log_enabled())
+                fprintf(stderr, "[mp3d] backward owner-gather dtype=%d slab=%d tiles=%lld "
+                        "threads=%d lds=%u\n", T::code, op.td, (long long)op.ntiles,
+                        op.threads, op.lds_bytes);
+            return hip_status(launch_backward_owner<T, Src>(gy, src, gx, op, s),
+                              "backward owner-gather launch");
+        }
+    }
     if constexpr (is_recompute_src<Src>::value) {
         // index-free, any order: the column stages recompute the argmax
         RcPlan rp;
@@ -432,10 +462,10 @@ int backward(const void *gy, const void *idx, int idx_type, const void *x, const
         const int es = dtype == MP3D_F64 ? 8 : dtype == MP3D_F32 ? 4 : 2;
         const WsLayout L = ws_layout(g.planes * (int64_t)g.out_plane, es);
         if (ws && ws_bytes < L.bytes)
-            return fail(MP3D_EINVAL, "workspace of %zu bytes; this call needs %zu", ws_bytes,
+            return fail(MP3D_EWORKSPACE, "workspace of %zu bytes; this call needs %zu", ws_bytes,
                         L.bytes);
         if (ws && (uintptr_t)ws % 16)
-            return fail(MP3D_EINVAL, "workspace must be 16-byte aligned");
+            return fail(MP3D_EWORKSPACE, "workspace must be 16-byte aligned");
         // the two-pass form, except for small tensors (one launch instead
         // of two) and where the fused one-pass kernel takes slabs of 4
         // slices or more (there it measured as fast or faster: each window
@@ -482,6 +512,8 @@ int backward(const void *gy, const void *idx, int idx_type, const void *x, const
 }
 
 }  // namespace
+
+LaunchTiming &launch_timing() { return g_timing; }
 
 int device_cus()
 {
@@ -548,6 +580,7 @@ int mp3d_forward(const void *x, void *y, int32_t *idx, int dtype, int64_t N, int
                  int64_t D, int64_t H, int64_t W, int32_t kd, int32_t kh, int32_t kw,
                  int32_t sd, int32_t sh, int32_t sw, void *stream)
 {
+    TimingScope timing_scope;
     int rc = check_common(dtype, N, C, D, H, W);
     if (rc) return rc;
     Geom g;
@@ -562,6 +595,7 @@ int amp3d_forward(const void *x, void *y, int32_t *idx, int dtype, int64_t N, in
                   int64_t D, int64_t H, int64_t W, int32_t od, int32_t oh, int32_t ow,
                   void *stream)
 {
+    TimingScope timing_scope;
     int rc = check_common(dtype, N, C, D, H, W);
     if (rc) return rc;
     Geom g;
@@ -577,6 +611,7 @@ int mp3d_forward_ex(const void *x, void *y, void *idx, int dtype, int idx_type, 
                     int32_t ow, const int32_t *kernel, const int32_t *stride, const int32_t *pad,
                     const int32_t *dilation, void *stream)
 {
+    TimingScope timing_scope;
     int rc = check_common(dtype, N, C, D, H, W);
     if (rc) return rc;
     if (idx_type != MP3D_IDX_I32 && idx_type != MP3D_IDX_I64)
@@ -592,6 +627,7 @@ int mp3d_backward(const void *gy, const int32_t *idx, void *gx, int dtype, int64
                   int32_t ow, int32_t kd, int32_t kh, int32_t kw, int32_t sd, int32_t sh,
                   int32_t sw, int overlap, void *stream)
 {
+    TimingScope timing_scope;
     int rc = check_common(dtype, N, C, D, H, W);
     if (rc) return rc;
     const int64_t X[3] = {D, H, W};
@@ -618,6 +654,7 @@ int mp3d_backward_ex(const void *gy, const void *idx, void *gx, int dtype, int i
                      int32_t oh, int32_t ow, const int32_t *kernel, const int32_t *stride,
                      const int32_t *pad, const int32_t *dilation, int overlap, void *stream)
 {
+    TimingScope timing_scope;
     int rc = check_common(dtype, N, C, D, H, W);
     if (rc) return rc;
     if (idx_type != MP3D_IDX_I32 && idx_type != MP3D_IDX_I64)
@@ -634,6 +671,7 @@ int mp3d_backward_recompute(const void *x, const void *y, const void *gy, void *
                             const int32_t *pad, const int32_t *dilation, int overlap,
                             void *stream)
 {
+    TimingScope timing_scope;
     int rc = check_common(dtype, N, C, D, H, W);
     if (rc) return rc;
     Geom g;
@@ -664,6 +702,7 @@ int mp3d_backward_recompute_ws(const void *x, const void *y, const void *gy, voi
                                const int32_t *dilation, int overlap, void *workspace,
                                size_t workspace_bytes, void *stream)
 {
+    TimingScope timing_scope;
     int rc = check_common(dtype, N, C, D, H, W);
     if (rc) return rc;
     Geom g;
@@ -672,6 +711,29 @@ int mp3d_backward_recompute_ws(const void *x, const void *y, const void *gy, voi
                     workspace, workspace_bytes);
 }
 
+
+int mp3d_time_next_call(void *start_event, void *stop_event)
+{
+    if (!stop_event && start_event) return fail(MP3D_EINVAL, "start event without a stop event");
+    g_timing = {(hipEvent_t)start_event, (hipEvent_t)stop_event};
+    return MP3D_OK;
+}
+
+int mp3d_backward_workspace_bytes(int dtype, int idx_type, int64_t N, int64_t C, int32_t od,
+                                  int32_t oh, int32_t ow, size_t *bytes)
+{
+    if (!bytes) return fail(MP3D_EINVAL, "bytes is NULL");
+    if (idx_type != MP3D_IDX_I32 && idx_type != MP3D_IDX_I64 && idx_type != MP3D_IDX_NONE)
+        return fail(MP3D_EDTYPE, "idx_type %d is not MP3D_IDX_I32, MP3D_IDX_I64 or MP3D_IDX_NONE",
+                    idx_type);
+    if (idx_type == MP3D_IDX_NONE) return mp3d_recompute_workspace_size(dtype, N, C, od, oh, ow, bytes);
+    if (dtype < MP3D_F32 || dtype > MP3D_F64)
+        return fail(MP3D_EDTYPE, "dtype %d is not one of MP3D_F32/F16/BF16/F64", dtype);
+    if (N < 0 || C < 0 || od <= 0 || oh <= 0 || ow <= 0)
+        return fail(MP3D_EINVAL, "N, C must be >= 0 and the output extents >= 1");
+    *bytes = 0;                      // every index-array path keeps its accumulator in LDS
+    return MP3D_OK;
+}
 
 const char *mp3d_strerror(int code)
 {
@@ -682,6 +744,7 @@ const char *mp3d_strerror(int code)
     case MP3D_ENOTDIV: return "windows do not tile every axis";
     case MP3D_EOVERFLOW: return "size exceeds the index range";
     case MP3D_EHIP: return "HIP runtime error";
+    case MP3D_EWORKSPACE: return "workspace too small or misaligned";
     default: return "unknown status";
     }
 }

@@ -128,7 +128,7 @@ __device__ __forceinline__ void store_span(typename T::raw *dst, const typename 
 template <typename T, typename Src, int NT, bool ORD, int kRound>
 __global__ void __launch_bounds__(NT)
 bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
-                typename T::raw *__restrict__ gx, BwdPlan p)
+                typename T::raw *__restrict__ gx, BwdPlan p, int64_t tile0)
 {
     using R = typename T::raw;
     using Acc = typename T::acc;
@@ -141,7 +141,7 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
     const int32_t OHW = p.g.ax[1].O * p.g.ax[2].O;
     const int32_t tid = threadIdx.x;
 
-    const uint32_t t = xcd_local_block(blockIdx.x, gridDim.x);
+    const int64_t t = tile0 + xcd_local_block(blockIdx.x, gridDim.x);
     if (t >= p.ntiles) return;                   // whole workgroup: no barrier skipped
     int64_t plane;
     int32_t td, th, tw;
@@ -300,7 +300,8 @@ bwd_slab_kernel(const typename T::raw *__restrict__ gy, const Src src,
 template <typename T, int MAXKD, int NT, int KS, int KHW>
 __global__ void __launch_bounds__(NT)
 bwd_rc_kernel(const typename T::raw *__restrict__ x, const typename T::raw *__restrict__ y,
-              const typename T::raw *__restrict__ gy, typename T::raw *__restrict__ gx, RcPlan p)
+              const typename T::raw *__restrict__ gy, typename T::raw *__restrict__ gx, RcPlan p,
+              uint32_t tile0)
 {
     using R = typename T::raw;
     using Acc = typename T::acc;
@@ -313,7 +314,7 @@ bwd_rc_kernel(const typename T::raw *__restrict__ x, const typename T::raw *__re
     int2 *tab = reinterpret_cast<int2 *>(smem);          // window spans: oh, then ow
     unsigned char *region = smem + p.tab_bytes;          // D-partials, then the accumulator
 
-    const uint32_t t = xcd_local_block(blockIdx.x, gridDim.x);
+    const uint32_t t = tile0 + xcd_local_block(blockIdx.x, gridDim.x);
     if (t >= p.ntiles) return;                           // whole workgroup: no barrier skipped
     const uint32_t plane = p.ntd_div.div(t);
     const int32_t sd = (int32_t)(t - plane * (uint32_t)p.ntd);
@@ -451,25 +452,134 @@ bwd_box_kernel(const typename T::raw *__restrict__ gy, const Src src,
     }
 }
 
-template <typename T, typename Src>
+// Windows tile every axis (q = X / O per axis): input (d, h, w) lies in the
+// one window (d / qd, h / qh, w / qw), and window o covers the qd x qh x qw
+// box at (od*qd, oh*qh, ow*qw).  A thread takes kGatherV consecutive windows
+// of one output row: it loads their idx and gy (16-byte and 8-byte vectors
+// where aligned), then writes each of the qd*qh input rows under them -- the
+// qw*kGatherV elements of a row are contiguous, gy where idx names the
+// element and +0 elsewhere -- with 16-byte streaming stores where the row
+// segment is aligned, else element stores.
+constexpr int kGatherV = 4;
+
+// QW: qw as a compile-time constant (1 or 2), 0 for any qw.
+template <typename T, typename Src, int QW>
 __global__ void __launch_bounds__(kBlock)
 bwd_gather_kernel(const typename T::raw *__restrict__ gy, const Src src,
                   typename T::raw *__restrict__ gx, GatherPlan p)
 {
+    using R = typename T::raw;
+    using Acc = typename T::acc;
+    constexpr int V = kGatherV;
     const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X;
-    const int32_t OH = p.g.ax[1].O, OW = p.g.ax[2].O;
-    const int64_t total = p.g.planes * (int64_t)p.g.in_plane;
-    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * kBlock) {
-        const int64_t plane = e / p.g.in_plane;
-        const int32_t i = (int32_t)(e - plane * p.g.in_plane);
-        const int32_t w = i % W, r = i / W, h = r % H, d = r / H;
-        const int64_t o = plane * (int64_t)p.g.out_plane +
-                          ((d / p.qd) * OH + h / p.qh) * OW + w / p.qw;
-        using Acc = typename T::acc;
-        typename T::raw out = T::narrow(Acc(0));
-        if (src(o) == i) out = T::narrow(Acc(0) + T::widen(gy[o]));
-        gx[e] = out;
+    const int32_t OD = p.g.ax[0].O, OH = p.g.ax[1].O, OW = p.g.ax[2].O;
+    const int32_t G = (OW + V - 1) / V;                 // window groups per output row
+    const int64_t total = p.g.planes * (int64_t)OD * OH * G;
+    for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * kBlock) {
+        int64_t row;                                   // output row: plane * OD * OH + od * OH + oh
+        int32_t grp;
+        if (p.fast) {
+            const uint32_t q = p.grp_div.div((uint32_t)t);
+            row = q;
+            grp = (int32_t)((uint32_t)t - q * (uint32_t)G);
+        } else {
+            row = t / G;
+            grp = (int32_t)(t - row * G);
+        }
+        int64_t plane;
+        int32_t od, oh;
+        if (p.fast) {
+            const uint32_t q = p.oh_div.div((uint32_t)row);
+            oh = (int32_t)((uint32_t)row - q * (uint32_t)OH);
+            const uint32_t q2 = p.od_div.div(q);
+            od = (int32_t)(q - q2 * (uint32_t)OD);
+            plane = q2;
+        } else {
+            const int64_t q = row / OH;
+            oh = (int32_t)(row - q * OH);
+            plane = q / OD;
+            od = (int32_t)(q - plane * OD);
+        }
+        const int32_t ow0 = grp * V, nwin = min(V, OW - ow0);
+        const int64_t o0 = plane * (int64_t)p.g.out_plane + ((int64_t)od * OH + oh) * OW + ow0;
+        int32_t ix[V];
+        Acc gv[V];
+        if (nwin == V && p.vec_in && (o0 & (V - 1)) == 0) {
+            src.load4(o0, ix);
+            if constexpr (sizeof(R) == 2) {
+                const u32x2 g2 = *reinterpret_cast<const u32x2 *>(gy + o0);
+                const uint32_t gw[2] = {g2.x, g2.y};
+#pragma unroll
+                for (int k = 0; k < V; ++k) gv[k] = T::widen((R)(gw[k / 2] >> (16 * (k % 2))));
+            } else {
+#pragma unroll
+                for (int k = 0; k < V; ++k) gv[k] = T::widen(gy[o0 + k]);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                ix[k] = -1;
+                gv[k] = Acc(0);
+                if (k < nwin) {
+                    ix[k] = src(o0 + k);
+                    gv[k] = T::widen(gy[o0 + k]);
+                }
+            }
+        }
+        // 0 + gy: a -0 gradient gives +0, as the accumulate path does
+        R val[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) val[k] = T::narrow(Acc(0) + gv[k]);
+        const R zero = T::narrow(Acc(0));
+        const int32_t qw = QW ? QW : p.qw;
+        const int32_t w0 = ow0 * qw, nel = nwin * qw;   // the row segment under the windows
+        R *gp = gx + plane * (int64_t)p.g.in_plane;
+        for (int32_t dd = 0; dd < p.qd; ++dd) {
+            for (int32_t hh = 0; hh < p.qh; ++hh) {
+                const int32_t pos0 = ((od * p.qd + dd) * H + oh * p.qh + hh) * W + w0;
+                R *seg = gp + pos0;
+                if constexpr (QW > 0 && (QW * V * sizeof(R)) % 16 == 0) {
+                    if (nwin == V && ((uintptr_t)seg & 15) == 0) {
+                        // QW * V elements, whole 16-byte vectors; element q
+                        // lies in window q / QW
+                        constexpr int NE = QW * V, VE = 16 / (int)sizeof(R);
+                        R e[NE];
+#pragma unroll
+                        for (int q = 0; q < NE; ++q) e[q] = ix[q / QW] == pos0 + q ? val[q / QW] : zero;
+#pragma unroll
+                        for (int c = 0; c < NE; c += VE) {
+                            uint32_t w4[4];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                if constexpr (sizeof(R) == 2)
+                                    w4[j] = (uint32_t)e[c + 2 * j] | ((uint32_t)e[c + 2 * j + 1] << 16);
+                                else if constexpr (sizeof(R) == 4)
+                                    w4[j] = __builtin_bit_cast(uint32_t, e[c + j]);
+                                else
+                                    w4[j] = (uint32_t)(__builtin_bit_cast(uint64_t, e[c + j / 2]) >> (32 * (j % 2)));
+                            }
+                            st_stream(reinterpret_cast<u32x4 *>(seg + c), u32x4{w4[0], w4[1], w4[2], w4[3]});
+                        }
+                        continue;
+                    }
+                }
+                // element stores: any qw, any alignment, a short last group
+                for (int32_t k = 0; k < nwin; ++k) {
+                    int32_t ik = ix[0];
+                    R vk = val[0];
+#pragma unroll
+                    for (int kk = 1; kk < V; ++kk) {
+                        ik = kk == k ? ix[kk] : ik;
+                        vk = kk == k ? val[kk] : vk;
+                    }
+                    for (int32_t ww = 0; ww < qw; ++ww) {
+                        const int32_t q = k * qw + ww;
+                        seg[q] = ik == pos0 + q ? vk : zero;
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -480,25 +590,30 @@ hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const 
                                 hipStream_t s)
 {
     using R = typename T::raw;
-    int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)1 << 24);
-    if (p.slab) {
-        // one workgroup per slab; a multiple of 8 lets blocks map per XCD
-        // (the surplus blocks exit at once)
-        if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
-        if (p.nphase) {
-            hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kOrdThreads, true, kOrdRound>),
-                               dim3((uint32_t)grid), dim3(kOrdThreads), p.lds_bytes, s,
-                               (const R *)gy, src, (R *)gx, p);
-            return hipGetLastError();
-        }
-        hipLaunchKernelGGL((bwd_slab_kernel<T, Src, kSlabBlock, false, Src::kSlots>),
-                           dim3((uint32_t)grid), dim3(kSlabBlock), p.lds_bytes, s,
-                           (const R *)gy, src, (R *)gx, p);
+    if (!p.slab) {
+        // boxes are strided over the workgroups
+        const int64_t grid = std::min<int64_t>(p.ntiles, kMaxTileGrid);
+        launch_kernel((bwd_box_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
+                      (const R *)gy, src, (R *)gx, p);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((bwd_box_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s,
-                       (const R *)gy, src, (R *)gx, p);
-    return hipGetLastError();
+    // one workgroup per slab, in launches of at most kMaxTileGrid workgroups
+    // (so workgroups x threads stay within one dispatch); a multiple of 8
+    // lets blocks map per XCD (the surplus blocks exit at once)
+    for (int64_t t0 = 0; t0 < p.ntiles; t0 += kMaxTileGrid) {
+        const uint32_t grid = tile_grid(p.ntiles, t0);
+        if (p.nphase)
+            launch_kernel((bwd_slab_kernel<T, Src, kOrdThreads, true, kOrdRound>),
+                          dim3((uint32_t)grid), dim3(kOrdThreads), p.lds_bytes, s, (const R *)gy,
+                          src, (R *)gx, p, t0);
+        else
+            launch_kernel((bwd_slab_kernel<T, Src, kSlabBlock, false, Src::kSlots>),
+                          dim3((uint32_t)grid), dim3(kSlabBlock), p.lds_bytes, s, (const R *)gy,
+                          src, (R *)gx, p, t0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <typename T>
@@ -506,11 +621,14 @@ hipError_t launch_backward_rc(const void *x, const void *y, const void *gy, void
                               const RcPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
-    uint32_t grid = p.ntiles;
-    if (grid >= 64) grid = (grid + 7u) & ~7u;            // blocks map per XCD; the surplus exits
+    // one workgroup per slab, in launches of at most kMaxTileGrid workgroups;
+    // a multiple of 8 lets blocks map per XCD (the surplus exits)
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), p.lds_bytes, s, (const R *)x,
-                           (const R *)y, (const R *)gy, (R *)gx, p);
+        for (int64_t t0 = 0; t0 < (int64_t)p.ntiles; t0 += kMaxTileGrid) {
+            const uint32_t grid = tile_grid(p.ntiles, t0);
+            launch_kernel(kern, dim3((uint32_t)grid), dim3(kBlock), p.lds_bytes, s, (const R *)x,
+                          (const R *)y, (const R *)gy, (R *)gx, p, (uint32_t)t0);
+        }
     };
     // window slots per thread: the fewest of 1, 2, 4, 8, 16 that hold the
     // windows reaching a slab
@@ -543,11 +661,17 @@ hipError_t launch_backward_gather(const void *gy, const Src &src, void *gx, cons
                                   hipStream_t s)
 {
     using R = typename T::raw;
-    const int64_t total = p.g.planes * (int64_t)p.g.in_plane;
-    int64_t grid = (total + kBlock - 1) / kBlock;
-    if (grid > (1 << 20)) grid = 1 << 20;
-    hipLaunchKernelGGL((bwd_gather_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
-                       (const R *)gy, src, (R *)gx, p);
+    GatherPlan q = p;
+    q.vec_in = src.aligned4() && (sizeof(R) != 2 || (uintptr_t)gy % 8 == 0);
+    if (q.qw == 1)
+        launch_kernel((bwd_gather_kernel<T, Src, 1>), dim3(q.grid), dim3(kBlock), 0, s,
+                      (const R *)gy, src, (R *)gx, q);
+    else if (q.qw == 2)
+        launch_kernel((bwd_gather_kernel<T, Src, 2>), dim3(q.grid), dim3(kBlock), 0, s,
+                      (const R *)gy, src, (R *)gx, q);
+    else
+        launch_kernel((bwd_gather_kernel<T, Src, 0>), dim3(q.grid), dim3(kBlock), 0, s,
+                      (const R *)gy, src, (R *)gx, q);
     return hipGetLastError();
 }
 

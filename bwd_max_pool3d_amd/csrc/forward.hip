@@ -311,7 +311,7 @@ hipError_t launch_forward_tile(const void *x, void *y, IT *idx, const FwdPlan &p
         per_cu = 1;
     int64_t grid = std::min<int64_t>(p.ntiles, (int64_t)per_cu * device_cus());
     if (grid >= 64) grid &= ~(int64_t)7;    // a multiple of 8 lets blocks map per XCD
-    hipLaunchKernelGGL((fwd_tile_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock),
+    launch_kernel((fwd_tile_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock),
                        p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
@@ -323,7 +323,7 @@ hipError_t launch_forward_direct(const void *x, void *y, IT *idx, const Geom &g,
     const int64_t total = g.planes * (int64_t)g.out_plane;
     int64_t grid = (total + kBlock - 1) / kBlock;
     if (grid > (1 << 20)) grid = 1 << 20;
-    hipLaunchKernelGGL((fwd_direct_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
+    launch_kernel((fwd_direct_kernel<T, IT>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
                        (const R *)x, (R *)y, idx, g);
     return hipGetLastError();
 }

@@ -11,6 +11,8 @@
 // D-reduce in registers from coalesced 16-byte column loads, then one scan
 // per window over the D-partials in LDS.  NT threads: 256, or 512 when the
 // tile's D-partials need much LDS and few workgroups fit on a CU.
+#include <algorithm>
+
 #include "colstage.hpp"
 #include "dtype.hpp"
 #include "kernels.hpp"
@@ -22,7 +24,7 @@ namespace {
 template <typename T, typename IT, int MAXKD, int NT>
 __global__ void __launch_bounds__(NT)
 fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict__ y,
-               IT *__restrict__ idx, ColPlan p)
+               IT *__restrict__ idx, ColPlan p, uint32_t tile0)
 {
     using R = typename T::raw;
     using Acc = typename T::acc;
@@ -36,7 +38,8 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
     Acc *pv = reinterpret_cast<Acc *>(smem + p.tab_bytes);
     uint8_t *pd = reinterpret_cast<uint8_t *>(smem + p.tab_bytes + p.pv_bytes);
 
-    const uint32_t t = xcd_local_block(blockIdx.x, gridDim.x);
+    const uint32_t t = tile0 + xcd_local_block(blockIdx.x, gridDim.x);
+    if (t >= p.ntiles) return;                 // whole workgroup: no barrier skipped
     const uint32_t plane = p.ntd_div.div(t);
     const int32_t td = (int32_t)(t - plane * (uint32_t)p.ntd);
     const int32_t od0 = td * p.tod, od1 = min(od0 + p.tod, A.O);
@@ -80,14 +83,21 @@ template <typename T, typename IT, int MAXKD>
 hipError_t launch_col(const void *x, void *y, IT *idx, const ColPlan &p, hipStream_t s)
 {
     using R = typename T::raw;
-    int64_t grid = p.ntiles;
-    if (p.lds_bytes > kColBigLds)
-        hipLaunchKernelGGL((fwd_col_kernel<T, IT, MAXKD, kColBigThreads>), dim3((uint32_t)grid),
-                           dim3(kColBigThreads), p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
-    else
-        hipLaunchKernelGGL((fwd_col_kernel<T, IT, MAXKD, kBlock>), dim3((uint32_t)grid),
-                           dim3(kBlock), p.lds_bytes, s, (const R *)x, (R *)y, idx, p);
-    return hipGetLastError();
+    // one workgroup per tile, in launches of at most kMaxTileGrid workgroups;
+    // a multiple of 8 lets blocks map per XCD (the surplus exits)
+    for (int64_t t0 = 0; t0 < (int64_t)p.ntiles; t0 += kMaxTileGrid) {
+        const uint32_t grid = tile_grid(p.ntiles, t0);
+        if (p.lds_bytes > kColBigLds)
+            launch_kernel((fwd_col_kernel<T, IT, MAXKD, kColBigThreads>), dim3((uint32_t)grid),
+                          dim3(kColBigThreads), p.lds_bytes, s, (const R *)x, (R *)y, idx, p,
+                          (uint32_t)t0);
+        else
+            launch_kernel((fwd_col_kernel<T, IT, MAXKD, kBlock>), dim3((uint32_t)grid),
+                          dim3(kBlock), p.lds_bytes, s, (const R *)x, (R *)y, idx, p, (uint32_t)t0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace

@@ -132,10 +132,10 @@ hipError_t launch_forward_ex(const void *x, void *y, IT *idx, const ExPlan &p, h
     using R = typename T::raw;
     const int64_t grid = std::min<int64_t>((p.total + kBlock - 1) / kBlock, (int64_t)1 << 20);
     if (p.km == 3)
-        hipLaunchKernelGGL((fwd_ex_kernel<T, IT, 3>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
+        launch_kernel((fwd_ex_kernel<T, IT, 3>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
                            (const R *)x, (R *)y, idx, p);
     else
-        hipLaunchKernelGGL((fwd_ex_kernel<T, IT, 0>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
+        launch_kernel((fwd_ex_kernel<T, IT, 0>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
                            (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }

@@ -452,29 +452,12 @@ hipError_t launch_fixed(const void *x, void *y, IT *idx, const FixedPlan &p, hip
         grid = (uint32_t)((p.nthreads + kBlock - 1) / kBlock);
     }
     grid = (grid + 7u) & ~7u;
-    hipLaunchKernelGGL((fwd_fixed_kernel<T, IT, KD, KH, KW, SD, SH, SW, FixedPlan::V, PAD, PW>), dim3(grid),
+    launch_kernel((fwd_fixed_kernel<T, IT, KD, KH, KW, SD, SH, SW, FixedPlan::V, PAD, PW>), dim3(grid),
                        dim3(kBlock), 0, s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
 
 }  // namespace
-
-// The window shapes with a compiled kernel: 2x2x2 / stride 2 and
-// 3x3x3 / stride 2, the two fixed-window workloads' shapes, with no padding
-// or one position of padding per side (dilation 1).  Along w a tap past the
-// end needs the padding column of that axis (the plan then checks that the
-// row's last group lies wholly past the end); along d and h the row clamp
-// covers both ends.
-bool fixed_shape_supported(const Geom &g)
-{
-    const Axis &a = g.ax[0], &b = g.ax[1], &c = g.ax[2];
-    if (!a.k || a.k != b.k || a.k != c.k || a.s != b.s || a.s != c.s) return false;
-    if (!((a.k == 2 && a.s == 2) || (a.k == 3 && a.s == 2))) return false;
-    for (int i = 0; i < 3; ++i)
-        if (g.ax[i].dil != 1 || g.ax[i].pad > 1) return false;
-    if (g.plain()) return true;
-    return c.pad == 1 || (int64_t)(c.O - 1) * c.s - c.pad + c.k <= c.X;
-}
 
 template <typename T, typename IT, int K>
 hipError_t launch_fixed_k(const void *x, void *y, IT *idx, const FixedPlan &p, hipStream_t s)

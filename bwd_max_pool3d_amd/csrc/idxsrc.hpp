@@ -23,6 +23,21 @@ struct IdxArray {
     static constexpr int kSlots = kBwdRound; // windows per thread per slab round
     const IT *p;
     __device__ __forceinline__ int32_t operator()(int64_t o) const { return ld_idx(p, o); }
+    // four consecutive indices from o (a multiple of 4), as vector loads
+    // (the array must start on 16 bytes: aligned4)
+    __device__ __forceinline__ void load4(int64_t o, int32_t (&ix)[4]) const {
+        if constexpr (sizeof(IT) == 4) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(p + o);
+            ix[0] = v.x; ix[1] = v.y; ix[2] = v.z; ix[3] = v.w;
+        } else {
+            const i64x2 a = *reinterpret_cast<const i64x2 *>(p + o);
+            const i64x2 b = *reinterpret_cast<const i64x2 *>(p + o + 2);
+            const int64_t v[4] = {a.x, a.y, b.x, b.y};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ix[k] = v[k] == (int64_t)(int32_t)v[k] ? (int32_t)v[k] : -1;
+        }
+    }
+    __host__ bool aligned4() const { return (uintptr_t)p % 16 == 0; }
 };
 
 // Recomputed from x and y: the first tap of window o, in d, h, w scan

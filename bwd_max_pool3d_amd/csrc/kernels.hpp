@@ -2,6 +2,7 @@
 // (api.hip) and the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -12,6 +13,21 @@ namespace mp3d {
 
 constexpr int kBlock = 256;            // threads per workgroup (4 waves)
 constexpr int kSlabThreads = 512;      // threads per backward slab workgroup
+// Workgroups per launch of the one-tile-per-workgroup kernels (more tiles
+// take more launches): with at most 512 threads each, 2^20 keeps a launch
+// within 2^32 work-items.
+constexpr int64_t kMaxTileGrid = (int64_t)1 << 20;
+
+// Workgroups of the launch that starts at tile t0 of a one-tile-per-
+// workgroup kernel over ntiles tiles (launches start at t0 = 0,
+// kMaxTileGrid, 2 kMaxTileGrid, ...); rounded up to a multiple of 8, which
+// lets blocks map per XCD (the surplus workgroups exit at once).
+inline uint32_t tile_grid(int64_t ntiles, int64_t t0)
+{
+    int64_t grid = ntiles - t0 < kMaxTileGrid ? ntiles - t0 : kMaxTileGrid;
+    if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
+    return (uint32_t)grid;
+}
 
 // Index elements come as int32 (the library's own) or int64 (torch's).  An
 // int64 value outside the int32 range reads as -1, which the backward
@@ -95,6 +111,26 @@ struct RcPlan {
     int32_t small3;            // every window has at most 3 taps per axis
 };
 
+// Owner-gather backward (backward_owner.hip): each workgroup owns a slab
+// [d0, d0 + td) of whole slices of one plane's gx, staged in LDS in the
+// storage type, with the (idx, gy) of the windows reaching the slab; the
+// first window (in output order) whose argmax is an element sums every
+// window's gy there, in ascending output order, and writes it.
+constexpr int kOwnerSlots = 8;             // windows per thread per fetch round (512 threads)
+struct OwnerPlan {
+    Geom g;
+    int32_t td, ntd;           // slices per slab, slabs per plane
+    FastDiv ntd_div;           // slab number -> plane (when fast)
+    int32_t fast;              // slab numbers fit 31 bits
+    int64_t ntiles;            // planes * ntd
+    int32_t threads;           // 256 or 512
+    uint32_t st_bytes;         // LDS: staged slab, 16-byte aligned
+    uint32_t ti_bytes;         // LDS: window idx table, 16-byte aligned
+    uint32_t lds_bytes;        // + window gy table
+    FastDiv hw_div, w_div;     // by H*W, by W (plane positions)
+    int32_t depth2;            // every position in at most two windows per axis
+};
+
 // General forward (forward_ex.hip): one thread per output, any geometry.
 struct ExPlan {
     Geom g;
@@ -118,6 +154,7 @@ struct OrdPlan {
 constexpr int kSmallK = 3;                 // forward: widest window per axis
 constexpr int64_t kSmallFwd = 1 << 18;     // forward: at most this many outputs
 constexpr int64_t kSmallBwd = 1 << 20;     // backward: at most this many input elements
+constexpr int64_t kTinyInputs = 1 << 16;   // forward: the small kernel first up to this many inputs
 struct SmallPlan {
     Geom g;
     uint32_t total;            // threads
@@ -129,6 +166,11 @@ struct SmallPlan {
 struct GatherPlan {
     Geom g;
     int32_t qd, qh, qw;
+    int32_t fast;              // thread count < 2^31: the FastDivs below apply
+    FastDiv grp_div;           // by the window groups per output row
+    FastDiv oh_div, od_div;    // by OH, by OD
+    int32_t vec_in;            // idx (and gy) may be read as vectors of 4 windows
+    uint32_t grid;             // workgroups (threads are strided over them)
 };
 
 // Forward with compile-time window shape: one thread per V consecutive
@@ -161,10 +203,33 @@ struct ColPlan {
 // Workgroups are dealt to the 8 XCDs round-robin by workgroup id; renumber
 // them so that each XCD walks one contiguous run of the work (and shares
 // its L2 across neighbouring tiles).
-__device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks)
+__host__ __device__ __forceinline__ uint32_t xcd_local_block(uint32_t b, uint32_t nblocks)
 {
     if (nblocks % 8u) return b;
     return (b % 8u) * (nblocks / 8u) + b / 8u;
+}
+
+// Kernel-time events armed for the next C-ABI call on this thread (see
+// mp3d_time_next_call): the call's first kernel records `start` at its
+// start, each kernel records `stop` at its end (the last one's stands).
+struct LaunchTiming {
+    hipEvent_t start, stop;
+};
+LaunchTiming &launch_timing();
+
+// Every kernel of the library is launched through here.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds,
+                          hipStream_t s, Args... args)
+{
+    LaunchTiming &t = launch_timing();
+    if (t.stop) {
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, s, t.start, t.stop, 0u,
+                              static_cast<KArgs>(args)...);
+        t.start = nullptr;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<KArgs>(args)...);
+    }
 }
 
 size_t lds_limit();
@@ -185,9 +250,14 @@ bool plan_backward(const Geom &g, bool ordered, int cell_bytes, BwdPlan *p);
 bool plan_small_forward(const Geom &g, SmallPlan *p);
 bool plan_small_backward(const Geom &g, SmallPlan *p);
 void plan_ordered(const Geom &g, OrdPlan *p);
+// windows that tile every axis (q = X / O per axis)
+void plan_gather(const Geom &g, GatherPlan *p);
 // es: storage element bytes; acc_bytes: accumulator cell bytes
 bool plan_rc(const Geom &g, int es, int acc_bytes, const void *x, RcPlan *p);
 void plan_ex(const Geom &g, ExPlan *p);
+// es: storage element bytes.  Fails when a slab's staging and window table
+// do not fit LDS or a position lies in too many windows.
+bool plan_owner(const Geom &g, int es, OwnerPlan *p);
 int64_t max_taps(const Axis &a);         // most taps of one window on the axis
 
 template <typename T, typename IT>
@@ -205,6 +275,9 @@ hipError_t launch_backward_tile(const void *gy, const Src &src, void *gx, const 
                                 hipStream_t s);
 template <typename T, typename IT>
 hipError_t launch_forward_small(const void *x, void *y, IT *idx, const SmallPlan &p, hipStream_t s);
+template <typename T, typename Src>
+hipError_t launch_backward_owner(const void *gy, const Src &src, void *gx, const OwnerPlan &p,
+                                 hipStream_t s);
 template <typename T, typename Src>
 hipError_t launch_backward_small(const void *gy, const Src &src, void *gx, const SmallPlan &p,
                                  hipStream_t s);

@@ -8,6 +8,8 @@
 //
 // Backward: a tile is a box of one plane's gx held as binary32 in LDS,
 // again whole slices where possible.
+#include <stdlib.h>
+
 #include <algorithm>
 
 #include "kernels.hpp"
@@ -20,6 +22,9 @@ constexpr int64_t kLdsCap = 64 * 1024;     // forward LDS per workgroup, all use
 constexpr int64_t kAccBudget = 40 * 1024;   // backward accumulator per workgroup
 constexpr int64_t kOrdBudget = 40 * 1024;   // the same, ordered slabs
 constexpr int64_t kWantTiles = 1024;        // >= 4 workgroups per CU
+constexpr int64_t kOwnerBudget = 80 * 1024; // owner gather: LDS per workgroup (2 per CU)
+constexpr int64_t kOwnerMaxCand = 64;       // owner gather: windows containing one position
+constexpr int64_t kMaxGrid = (int64_t)1 << 20;       // grid-stride kernels: workgroups per launch
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -115,6 +120,23 @@ bool plan_forward(const Geom &g, int es, FwdPlan *p)
     p->part_bytes = (uint32_t)part;
     p->lds_bytes = (uint32_t)lds;
     return true;
+}
+
+// The window shapes with a compiled kernel: 2x2x2 / stride 2 and
+// 3x3x3 / stride 2, the two fixed-window workloads' shapes, with no padding
+// or one position of padding per side (dilation 1).  Along w a tap past the
+// end needs the padding column of that axis (the plan then checks that the
+// row's last group lies wholly past the end); along d and h the row clamp
+// covers both ends.
+bool fixed_shape_supported(const Geom &g)
+{
+    const Axis &a = g.ax[0], &b = g.ax[1], &c = g.ax[2];
+    if (!a.k || a.k != b.k || a.k != c.k || a.s != b.s || a.s != c.s) return false;
+    if (!((a.k == 2 && a.s == 2) || (a.k == 3 && a.s == 2))) return false;
+    for (int i = 0; i < 3; ++i)
+        if (g.ax[i].dil != 1 || g.ax[i].pad > 1) return false;
+    if (g.plain()) return true;
+    return c.pad == 1 || (int64_t)(c.O - 1) * c.s - c.pad + c.k <= c.X;
 }
 
 bool plan_fixed(const Geom &g, int es, const void *x, const void *y, const void *idx,
@@ -351,6 +373,67 @@ bool plan_backward(const Geom &g, bool ordered, int cell_bytes, BwdPlan *p)
     return true;
 }
 
+// Owner-gather backward: slabs of whole slices.  LDS per slab: the staged
+// slab (storage type, plus the alignment shift) and the idx and gy tables
+// of the windows reaching it.  The largest slab within the budget that
+// still gives enough slabs to fill the chip; MP3D_OWNER_SLICES and
+// MP3D_OWNER_THREADS override the slab depth and the workgroup size
+// (tuning sweeps).
+bool plan_owner(const Geom &g, int es, OwnerPlan *p)
+{
+    const Axis &A = g.ax[0], &B = g.ax[1], &Cw = g.ax[2];
+    if (A.X > (1 << 20)) return false;                 // bounds the slab scans below
+    const int32_t md = axis_depth(A), mh = axis_depth(B), mw = axis_depth(Cw);
+    // positions in many windows make each owner's enumeration long
+    if (!md || !mh || !mw || (int64_t)md * mh * mw > kOwnerMaxCand) return false;
+    const int64_t HW = (int64_t)B.X * Cw.X, ohw = (int64_t)B.O * Cw.O;
+    const int64_t ve = 16 / es;
+    const int64_t budget = std::min<int64_t>(kOwnerBudget, (int64_t)lds_limit() - 64);
+    auto r16 = [](int64_t b) { return (b + 15) & ~(int64_t)15; };
+    auto lds = [&](int32_t td, int64_t *st, int64_t *ti) -> int64_t {
+        const int64_t maxw = slab_reach(A, td) * ohw;
+        *st = r16((td * HW + ve) * es);
+        *ti = r16(maxw * 4);
+        return *st + *ti + r16(maxw * es);
+    };
+    int64_t st = 0, ti = 0;
+    const char *ev = getenv("MP3D_OWNER_SLICES");
+    int32_t td = 0;
+    if (ev && atoi(ev) > 0) {
+        td = std::min<int32_t>(atoi(ev), A.X);
+        if (lds(td, &st, &ti) > (int64_t)lds_limit() - 64) return false;
+    } else {
+        const int64_t per_plane = cdiv(kWantTiles, std::max<int64_t>(g.planes, 1));
+        const int32_t cap = (int32_t)std::max<int64_t>(1, A.X / per_plane);
+        for (int32_t t = std::min<int32_t>(A.X, cap); t >= 1; --t)
+            if (lds(t, &st, &ti) <= budget) { td = t; break; }
+        if (td < 1) return false;
+        td = (int32_t)cdiv(A.X, cdiv(A.X, td));        // even slabs need no more LDS
+    }
+    const int64_t total = lds(td, &st, &ti);
+    const int64_t ntd = cdiv(A.X, td);
+    p->g = g;
+    p->td = td;
+    p->ntd = (int32_t)ntd;
+    p->ntd_div = FastDiv((uint32_t)ntd);
+    p->ntiles = g.planes * ntd;
+    p->fast = p->ntiles < ((int64_t)1 << 31);
+    // 512 threads where a slab has many windows to resolve, else 256
+    // (measured: 3645 windows per slab of the 3x3x3/2 f16 workload, 245 of
+    // the adaptive f32 one)
+    const char *et = getenv("MP3D_OWNER_THREADS");
+    const int64_t maxw = slab_reach(A, td) * ohw;
+    p->threads = (et && atoi(et) == 256) ? 256 : (et && atoi(et) == 512) ? 512
+                 : maxw >= 2048 ? 512 : 256;
+    p->st_bytes = (uint32_t)st;
+    p->ti_bytes = (uint32_t)ti;
+    p->lds_bytes = (uint32_t)total;
+    p->hw_div = FastDiv((uint32_t)HW);
+    p->w_div = FastDiv((uint32_t)Cw.X);
+    p->depth2 = md <= 2 && mh <= 2 && mw <= 2;
+    return true;
+}
+
 bool plan_rc(const Geom &g, int es, int ab, const void *x, RcPlan *p)
 {
     const Axis &A = g.ax[0], &B = g.ax[1], &Cw = g.ax[2];
@@ -427,6 +510,25 @@ void plan_ex(const Geom &g, ExPlan *p)
     p->plane_div = FastDiv((uint32_t)g.out_plane);
     p->ow_div = FastDiv((uint32_t)g.ax[2].O);
     p->oh_div = FastDiv((uint32_t)g.ax[1].O);
+}
+
+void plan_gather(const Geom &g, GatherPlan *p)
+{
+    constexpr int V = 4;                       // windows per thread (kGatherV)
+    p->g = g;
+    p->qd = g.ax[0].X / g.ax[0].O;
+    p->qh = g.ax[1].X / g.ax[1].O;
+    p->qw = g.ax[2].X / g.ax[2].O;
+    const int64_t G = cdiv(g.ax[2].O, V);
+    const int64_t threads = g.planes * g.ax[0].O * g.ax[1].O * G;
+    p->fast = threads < ((int64_t)1 << 31);
+    p->grp_div = FastDiv((uint32_t)G);
+    p->oh_div = FastDiv((uint32_t)g.ax[1].O);
+    p->od_div = FastDiv((uint32_t)g.ax[0].O);
+    p->vec_in = 0;                             // set by the launcher (pointer alignment)
+    int64_t grid = std::min<int64_t>(cdiv(threads, kBlock), kMaxGrid);
+    if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
+    p->grid = (uint32_t)std::max<int64_t>(grid, 1);
 }
 
 void plan_ordered(const Geom &g, OrdPlan *p)

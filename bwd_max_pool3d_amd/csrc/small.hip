@@ -180,7 +180,7 @@ hipError_t launch_backward_ordered(const void *gy, const Src &src, void *gx, con
 {
     using R = typename T::raw;
     const int64_t grid = std::min<int64_t>((p.total + kBlock - 1) / kBlock, (int64_t)1 << 20);
-    hipLaunchKernelGGL((bwd_ordered_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
+    launch_kernel((bwd_ordered_kernel<T, Src>), dim3((uint32_t)grid), dim3(kBlock), 0, s,
                        (const R *)gy, src, (R *)gx, p);
     return hipGetLastError();
 }
@@ -190,7 +190,7 @@ hipError_t launch_forward_small(const void *x, void *y, IT *idx, const SmallPlan
                                 hipStream_t s)
 {
     using R = typename T::raw;
-    hipLaunchKernelGGL((fwd_small_kernel<T, IT>), dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
+    launch_kernel((fwd_small_kernel<T, IT>), dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
                        s, (const R *)x, (R *)y, idx, p);
     return hipGetLastError();
 }
@@ -200,7 +200,7 @@ hipError_t launch_backward_small(const void *gy, const Src &src, void *gx, const
                                  hipStream_t s)
 {
     using R = typename T::raw;
-    hipLaunchKernelGGL((bwd_small_kernel<T, Src>), dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
+    launch_kernel((bwd_small_kernel<T, Src>), dim3((p.total + kBlock - 1) / kBlock), dim3(kBlock), 0,
                        s, (const R *)gy, src, (R *)gx, p);
     return hipGetLastError();
 }

@@ -103,3 +103,12 @@ WORKLOADS = (
 )
 
 BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+# The input shapes and dtypes of the latency table on the PR #308 page
+# ("[KernelGen][MThreads] Add adaptive_max_pool3d_backward Moore Threads
+# specialized operator", Performance).  The page prints no output_size;
+# callers pair each shape with output sizes of their own.
+PR308_SHAPES = tuple((dt, shape) for dt in ("float16", "float32", "bfloat16")
+                     for shape in ((1, 1, 4, 4, 4), (2, 3, 8, 8, 8), (1, 1, 16, 16, 16),
+                                   (2, 8, 4, 4, 4)))

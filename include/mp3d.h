@@ -69,7 +69,9 @@ enum mp3d_status {
                            tile every axis (see mp3d_backward) */
     MP3D_EOVERFLOW = 4, /* D*H*W > INT32_MAX (int32 idx impossible) or an
                            element count beyond 2^62 */
-    MP3D_EHIP = 5       /* a HIP launch failed; the message names it */
+    MP3D_EHIP = 5,      /* a HIP launch failed; the message names it */
+    MP3D_EWORKSPACE = 6 /* a workspace smaller than its size query, or not
+                           16-byte aligned */
 };
 
 /* Storage types.  float16 and bfloat16 values are compared and gradients
@@ -78,8 +80,9 @@ enum mp3d_status {
  * dtype of its own, served by the general kernels). */
 enum mp3d_dtype { MP3D_F32 = 0, MP3D_F16 = 1, MP3D_BF16 = 2, MP3D_F64 = 3 };
 
-/* Index element type of the _ex entry points (the others use int32). */
-enum mp3d_index { MP3D_IDX_I32 = 0, MP3D_IDX_I64 = 1 };
+/* Index element type of the _ex entry points (the others use int32).
+ * MP3D_IDX_NONE names the index-free backward in the workspace query. */
+enum mp3d_index { MP3D_IDX_NONE = -1, MP3D_IDX_I32 = 0, MP3D_IDX_I64 = 1 };
 
 /* Forward with fixed windows (teenygrad "Struct Maxpool3dForward",
  * description): kernel (kd, kh, kw), stride (sd, sh, sw), no padding.
@@ -254,6 +257,30 @@ int mp3d_backward_ex(const void *gy, const void *idx, void *gx, int dtype, int i
                      const int32_t *kernel, const int32_t *stride,
                      const int32_t *pad, const int32_t *dilation,
                      int overlap, void *stream);
+
+/* Workspace bytes a backward needs for N*C planes of od*oh*ow outputs of
+ * dtype, into *bytes: 0 for every backward that reads an index array
+ * (idx_type MP3D_IDX_I32 or MP3D_IDX_I64: their accumulators, tables and
+ * staged slabs live in LDS, so mp3d_backward and mp3d_backward_ex take no
+ * workspace), and for the index-free backward (MP3D_IDX_NONE) the size of
+ * mp3d_recompute_workspace_size, the workspace its two-pass form takes.
+ * MP3D_EDTYPE for another dtype or idx_type, MP3D_EINVAL for negative N or
+ * C, an output extent < 1 or a NULL bytes.  Host arithmetic only. */
+int mp3d_backward_workspace_bytes(int dtype, int idx_type, int64_t N, int64_t C, int32_t od,
+                                  int32_t oh, int32_t ow, size_t *bytes);
+
+/* Kernel timing of the next call (a measurement aid, for benchmarks).  The
+ * next call on the calling thread that launches kernels records
+ * start_event when its first kernel starts and stop_event when its last
+ * kernel ends (hipExtLaunchKernel's kernel-time events), so that
+ * hipEventElapsedTime(start_event, stop_event) gives that call's kernel
+ * time without the overhead of separate event records around it.  The
+ * events are the caller's (hipEvent_t from hipEventCreate, passed as
+ * void*).  Only the next call is timed: every launching call disarms the
+ * events when it returns, whether or not it launched anything (a call that
+ * launches nothing records neither event).  stop_event NULL disarms;
+ * start_event without stop_event is MP3D_EINVAL. */
+int mp3d_time_next_call(void *start_event, void *stop_event);
 
 /* Text for a status code (static storage). */
 const char *mp3d_strerror(int code);

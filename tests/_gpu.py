@@ -20,6 +20,8 @@ NaN outputs match NaN outputs; their payload bits are not compared.
 from __future__ import annotations
 
 import itertools
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -126,11 +128,16 @@ def check_backward(orc, gy: torch.Tensor, idx: torch.Tensor, in_shape, gx_gpu,
                    exact: bool, what=""):
     """Compare gx from the device with the oracle on the same gy and idx."""
     code = CODE[gy.dtype]
-    gys = storage(gy)
-    ids = idx.cpu().numpy()
-    r = orc.backward(gys, ids, code, tuple(in_shape))
+    check_backward_arrays(orc, storage(gy), idx.cpu().numpy(), storage(gx_gpu), code,
+                          tuple(in_shape), exact, what)
+
+
+def check_backward_arrays(orc, gys: np.ndarray, ids: np.ndarray, got: np.ndarray, code: int,
+                          in_shape, exact: bool, what=""):
+    """check_backward on host arrays: gy and gx in storage form, idx int32."""
+    r = orc.backward(np.ascontiguousarray(gys), np.ascontiguousarray(ids), code, tuple(in_shape))
     want = r["gx"].reshape(-1)
-    got = storage(gx_gpu).reshape(-1)
+    got = got.reshape(-1)
     ubits = {0: np.uint32, 3: np.uint64}.get(code, np.uint16)
     wb, gb = want.view(ubits), got.view(ubits)
     nan_w, nan_g = _nan_mask(want, code), _nan_mask(got, code)
@@ -173,6 +180,73 @@ def check_backward(orc, gy: torch.Tensor, idx: torch.Tensor, in_shape, gx_gpu,
         assert len(contribs) <= 8, "%s: cell %d has %d contributions" % (what, cell, len(contribs))
         assert int(gb[cell]) in _fold_orders(contribs, code), \
             "%s: cell %d is no serial order of its contributions" % (what, cell)
+
+
+# ---------------------------------------------------------------------------
+# every plane of a full-size tensor against the oracle, plane ranges in
+# parallel host threads (each oracle call releases the interpreter lock)
+# ---------------------------------------------------------------------------
+
+def _threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _ranges(P: int, parts: int):
+    cuts = np.linspace(0, P, max(1, min(parts, P)) + 1).astype(int)
+    return [(int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+
+
+def _each_range(P: int, fn, parts: int | None = None):
+    parts = parts or 4 * _threads()
+    with ThreadPoolExecutor(_threads()) as pool:
+        list(pool.map(lambda r: fn(*r), _ranges(P, parts)))
+
+
+def check_forward_all(orc, x: torch.Tensor, y, idx, out=None, k=None, s=None, what=""):
+    """Every plane's y bits and idx against the oracle (x on the host; y and
+    idx on the device)."""
+    N, C, D, H, W = x.shape
+    P = N * C
+    code = CODE[x.dtype]
+    o3 = out_shape(orc, x.shape, out, k, s)
+    kk = tuple(k) if k is not None else (0, 0, 0)
+    ss = tuple(s) if s is not None else (0, 0, 0)
+    xs = storage(x).reshape(P, 1, D, H, W)
+    yg = storage(y).reshape(P, -1)
+    ig = idx.cpu().numpy().reshape(P, -1)
+    ubits = {0: np.uint32, 3: np.uint64}.get(code, np.uint16)
+
+    def run(a, b):
+        yo, io = orc.forward(xs[a:b], code, o3, kk, ss)
+        io = io.reshape(b - a, -1)
+        bad = np.nonzero((io != ig[a:b]).ravel())[0]
+        assert bad.size == 0, "%s: %d idx mismatches in planes %d..%d, first at plane %d" % (
+            what, bad.size, a, b, a + bad[0] // io.shape[1])
+        assert np.array_equal(yo.reshape(b - a, -1).view(ubits), yg[a:b].view(ubits)), \
+            "%s: y bits differ in planes %d..%d" % (what, a, b)
+    _each_range(P, run)
+
+
+def check_backward_all(orc, gy: torch.Tensor, idx, in_shape, gx, exact: bool, what=""):
+    """check_backward on every plane (gy on the host or the device; idx and
+    gx on either)."""
+    N, C, D, H, W = in_shape
+    P = N * C
+    code = CODE[gy.dtype]
+    OD, OH, OW = gy.shape[2:]
+    gys = storage(gy).reshape(P, 1, OD, OH, OW)
+    ids = (idx.cpu() if isinstance(idx, torch.Tensor) else torch.as_tensor(idx)).numpy()
+    ids = ids.reshape(P, 1, OD, OH, OW)
+    gxs = storage(gx).reshape(P, -1)
+
+    def run(a, b):
+        check_backward_arrays(orc, gys[a:b], ids[a:b], gxs[a:b], code, (b - a, 1, D, H, W),
+                              exact, "%s planes %d..%d" % (what, a, b))
+    _each_range(P, run)
 
 
 def sample_planes(P: int, n: int = 10, seed: int = 0):

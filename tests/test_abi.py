@@ -167,8 +167,8 @@ def test_empty_batch_is_a_no_op():
 
 def test_strerror_covers_every_code():
     lib = _lib.load()
-    texts = {lib.mp3d_strerror(c).decode() for c in range(6)}
-    assert len(texts) == 6
+    texts = {lib.mp3d_strerror(c).decode() for c in range(7)}
+    assert len(texts) == 7
     assert lib.mp3d_strerror(99).decode() == "unknown status"
 
 
@@ -210,3 +210,36 @@ def test_recompute_ws_empty_batch_and_checks():
     assert call(overlap=3) == _lib.MP3D_EINVAL
     assert call(dtype=7) == _lib.MP3D_EDTYPE
     assert call(shape=(1, 2, 6, 6, 6)) == _lib.MP3D_EINVAL      # null tensors
+
+
+def _bwd_ws(dtype, idx_type, N, C, out):
+    v = ctypes.c_size_t(12345)
+    rc = _lib.load().mp3d_backward_workspace_bytes(dtype, idx_type, N, C, *out, ctypes.byref(v))
+    return rc, v.value
+
+
+def test_backward_workspace_bytes():
+    """The backward's workspace query: none for the index-array paths, the
+    two-pass size for the index-free one; host arithmetic only."""
+    for dtype in (_lib.MP3D_F32, _lib.MP3D_F16, _lib.MP3D_BF16, _lib.MP3D_F64):
+        for N, C, out in ((1, 1, (1, 1, 1)), (8, 128, (15, 27, 27)), (0, 3, (2, 2, 2))):
+            for it in (_lib.MP3D_IDX_I32, _lib.MP3D_IDX_I64):
+                assert _bwd_ws(dtype, it, N, C, out) == (_lib.MP3D_OK, 0)
+            assert _bwd_ws(dtype, _lib.MP3D_IDX_NONE, N, C, out) == _ws_size(dtype, N, C, out)
+    assert _bwd_ws(_lib.MP3D_F32, 2, 1, 1, (1, 1, 1))[0] == _lib.MP3D_EDTYPE
+    assert _bwd_ws(9, _lib.MP3D_IDX_I32, 1, 1, (1, 1, 1))[0] == _lib.MP3D_EDTYPE
+    assert _bwd_ws(_lib.MP3D_F32, _lib.MP3D_IDX_I32, 1, 1, (0, 1, 1))[0] == _lib.MP3D_EINVAL
+    assert _bwd_ws(_lib.MP3D_F32, _lib.MP3D_IDX_I32, -1, 1, (1, 1, 1))[0] == _lib.MP3D_EINVAL
+    assert _lib.load().mp3d_backward_workspace_bytes(0, 0, 1, 1, 1, 1, 1, None) == _lib.MP3D_EINVAL
+
+
+def test_time_next_call_arming():
+    """The timing hook only stores the caller's events for the next call:
+    disarming, and a start event without a stop event, need no GPU."""
+    lib = _lib.load()
+    assert lib.mp3d_time_next_call(None, None) == _lib.MP3D_OK
+    assert lib.mp3d_time_next_call(FAKE, None) == _lib.MP3D_EINVAL
+    # a failing call disarms the events it was given (nothing is launched)
+    assert lib.mp3d_time_next_call(FAKE, FAKE) == _lib.MP3D_OK
+    assert fwd(dtype=9) == _lib.MP3D_EDTYPE
+    assert lib.mp3d_time_next_call(None, None) == _lib.MP3D_OK

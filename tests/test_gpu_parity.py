@@ -321,22 +321,19 @@ def _full_properties(orc, wl, x, y, idx):
 
 @pytest.mark.parametrize("wl", workloads.WORKLOADS, ids=lambda w: w.name)
 def test_workload_full_size(orc, wl):
+    """Each named workload at full size, every plane against the oracle
+    (host threads over plane ranges): forward y bits and idx, the
+    accumulate backward to its bar, the ordered backward bit for bit (and
+    the same bits on a second run); plus the exact properties on every
+    element."""
     N, C, D, H, W = wl.shape
-    P = N * C
     x = wl.make_x()
     xd = x.cuda()
     out = wl.out
     k, s = wl.kernel, wl.stride
     y, idx = _gpu.gpu_forward(xd, out, k, s)
     torch.cuda.synchronize()
-    small = P * D * H * W <= 1 << 20
-    planes = range(P) if small else _gpu.sample_planes(P)
-    for p in planes:
-        n_, c_ = divmod(p, C)
-        xp = x[n_:n_ + 1, c_:c_ + 1].contiguous()
-        yo, io = _gpu.oracle_forward(orc, xp, out, k, s)
-        _gpu.assert_forward_match(y[n_:n_ + 1, c_:c_ + 1], idx[n_:n_ + 1, c_:c_ + 1], yo, io,
-                                  "%s plane %d" % (wl.name, p))
+    _gpu.check_forward_all(orc, x, y, idx, out, k, s, wl.name)
     _full_properties(orc, wl, xd, y, idx)
     # int64 indices: the same positions and the same y
     if k is None:
@@ -352,44 +349,41 @@ def test_workload_full_size(orc, wl):
     assert torch.equal(yv.view(torch.int16 if yv.element_size() == 2 else torch.int32),
                        y.view(torch.int16 if y.element_size() == 2 else torch.int32)), \
         "%s values-only y differs" % wl.name
-    del yv
-    if not wl.backward:
-        return
+    del yv, xd
     gy = wl.make_gy(tuple(y.shape))
     gyd = gy.cuda()
+    if not wl.backward:
+        # the windows tile every axis: the gather backward, bit for bit
+        gx = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=0)
+        torch.cuda.synchronize()
+        _gpu.check_backward_all(orc, gy, idx, wl.shape, gx, exact=True,
+                                what="%s gather" % wl.name)
+        return
     gx = _gpu.gpu_backward(gyd, idx, wl.shape, k, s)
     torch.cuda.synchronize()
     exact = all(X % O == 0 for X, O in zip(wl.shape[2:], y.shape[2:])) and (
         k is None or all(ka == sa for ka, sa in zip(k, s)))
-    for p in planes:
-        n_, c_ = divmod(p, C)
-        sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
-        _gpu.check_backward(orc, gy[sl].contiguous(), idx[sl].cpu().contiguous(),
-                            (1, 1, D, H, W), gx[sl], exact=exact,
-                            what="%s plane %d" % (wl.name, p))
+    _gpu.check_backward_all(orc, gy, idx, wl.shape, gx, exact=exact, what=wl.name)
     _gpu.full_backward_property(gyd, idx, gx, wl.shape)
-    # ordered backward: bit-exact on the sampled planes, and the same bits twice
+    del gx
+    # ordered backward: bit-exact on every plane, and the same bits twice
     gx2 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=2)
     gx3 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=2, poison=False)
     torch.cuda.synchronize()
     iv = torch.int32 if gx2.element_size() == 4 else torch.int16
     assert torch.equal(gx2.view(iv), gx3.view(iv)), "%s: ordered backward not reproducible" % wl.name
-    for p in planes:
-        n_, c_ = divmod(p, C)
-        sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
-        _gpu.check_backward(orc, gy[sl].contiguous(), idx[sl].cpu().contiguous(),
-                            (1, 1, D, H, W), gx2[sl], exact=True,
-                            what="%s ordered plane %d" % (wl.name, p))
+    del gx3
+    _gpu.check_backward_all(orc, gy, idx, wl.shape, gx2, exact=True,
+                            what="%s ordered" % wl.name)
 
 
 @pytest.mark.parametrize("wl", [w for w in workloads.WORKLOADS if w.backward and w.shape[0] > 4],
                          ids=lambda w: w.name)
 def test_float64_full_size(orc, wl):
     """The two large overlapping workloads with x and gy widened exactly to
-    float64: forward and the ordered backward bit-exact with the oracle on
-    sampled planes, the accumulate backward within the binary64 bound."""
-    N, C, D, H, W = wl.shape
-    P = N * C
+    float64, every plane against the oracle: forward and the ordered
+    backward bit-exact, the accumulate backward within the binary64
+    bound."""
     x = wl.make_x().to(torch.float64)
     xd = x.cuda()
     out, k, s = wl.out, wl.kernel, wl.stride
@@ -399,15 +393,53 @@ def test_float64_full_size(orc, wl):
     gx1 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s)
     gx2 = _gpu.gpu_backward(gyd, idx, wl.shape, k, s, overlap=2)
     torch.cuda.synchronize()
-    for p in _gpu.sample_planes(P):
+    del xd
+    _gpu.check_forward_all(orc, x, y, idx, out, k, s, "%s f64" % wl.name)
+    _gpu.check_backward_all(orc, gy, idx, wl.shape, gx1, exact=False, what="%s f64" % wl.name)
+    _gpu.check_backward_all(orc, gy, idx, wl.shape, gx2, exact=True,
+                            what="%s f64 ordered" % wl.name)
+
+
+class _Geo:
+    """A workload-like description of a geometry for _full_properties."""
+
+    def __init__(self, shape, out=None, kernel=None, stride=None):
+        self.shape, self.out, self.kernel, self.stride = shape, out, kernel, stride
+
+
+def test_planes_beyond_one_launch(orc):
+    """2^24 + 2^12 planes of float32 (3, 2, 2) pooled adaptively to (2, 1, 1)
+    (the two windows along d share slice 1): the column forward, the slab
+    backward and the ordered backward take one workgroup per plane, so each
+    needs 17 launches of at most 2^20 workgroups.  Planes on both sides of
+    every launch boundary, and the last ones, against the oracle; the exact
+    properties on every element."""
+    N, C, D, H, W = 4097, 4096, 3, 2, 2
+    out = (2, 1, 1)
+    P = N * C
+    g = torch.Generator(device="cuda").manual_seed(31)
+    xd = torch.rand((N, C, D, H, W), generator=g, device="cuda") * 2 - 1
+    y, idx = _gpu.gpu_forward(xd, out)
+    gyd = torch.randn((N, C) + out, generator=g, device="cuda")
+    gx = _gpu.gpu_backward(gyd, idx, (N, C, D, H, W))
+    gx2 = _gpu.gpu_backward(gyd, idx, (N, C, D, H, W), overlap=2)
+    torch.cuda.synchronize()
+    planes = sorted({0, 1, P - 2, P - 1} | {b + d for b in range(1 << 20, P, 1 << 20)
+                                           for d in (-1, 0, 1)})
+    for p in planes:
         n_, c_ = divmod(p, C)
         sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
-        yo, io = _gpu.oracle_forward(orc, x[sl].contiguous(), out, k, s)
-        _gpu.assert_forward_match(y[sl], idx[sl], yo, io, "%s f64 plane %d" % (wl.name, p))
-        for gx, exact in ((gx1, False), (gx2, True)):
-            _gpu.check_backward(orc, gy[sl].contiguous(), idx[sl].cpu().contiguous(),
-                                (1, 1, D, H, W), gx[sl], exact=exact,
-                                what="%s f64 plane %d" % (wl.name, p))
+        xp = xd[sl].cpu().contiguous()
+        yo, io = _gpu.oracle_forward(orc, xp, out)
+        _gpu.assert_forward_match(y[sl], idx[sl], yo, io, "plane %d" % p)
+        gyp = gyd[sl].cpu().contiguous()
+        _gpu.check_backward(orc, gyp, idx[sl].cpu().contiguous(), (1, 1, D, H, W), gx[sl],
+                            exact=False, what="plane %d" % p)
+        _gpu.check_backward(orc, gyp, idx[sl].cpu().contiguous(), (1, 1, D, H, W), gx2[sl],
+                            exact=True, what="ordered plane %d" % p)
+    _full_properties(orc, _Geo((N, C, D, H, W), out=out), xd, y, idx)
+    _gpu.full_backward_property(gyd, idx, gx, (N, C, D, H, W))
+    _gpu.full_backward_property(gyd, idx, gx2, (N, C, D, H, W))
 
 
 def test_maximum_sizes(orc):

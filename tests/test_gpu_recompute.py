@@ -139,7 +139,7 @@ def test_recompute_full_size(orc, wl):
     fold of the same contributions; the idx path is checked against the
     oracle in test_gpu_parity).  The index-free backward in any order (the
     fused column-stage kernel where it applies) is checked against the
-    oracle, fed the forward's idx, on sampled planes, and within the
+    oracle, fed the forward's idx, on every plane, and within the
     binary32-summation bound on every element."""
     xd = wl.make_x().cuda()
     if wl.adaptive:
@@ -167,17 +167,10 @@ def test_recompute_full_size(orc, wl):
     del ref, got
     gx = mp.mp3d_backward_recompute(xd, y, gy, **geo)
     torch.cuda.synchronize()
-    N, C, D, H, W = wl.shape
-    P = N * C
-    planes = range(P) if P * D * H * W <= 1 << 20 else _gpu.sample_planes(P)
     gyc = gy.cpu()
-    for p in planes:
-        n_, c_ = divmod(p, C)
-        sl = (slice(n_, n_ + 1), slice(c_, c_ + 1))
-        for g, form in ((gx, "one-pass"), (gxw, "two-pass")):
-            _gpu.check_backward(orc, gyc[sl].contiguous(), idx[sl].cpu().contiguous(),
-                                (1, 1, D, H, W), g[sl], exact=False,
-                                what="%s index-free %s plane %d" % (wl.name, form, p))
+    for g, form in ((gx, "one-pass"), (gxw, "two-pass")):
+        _gpu.check_backward_all(orc, gyc, idx, wl.shape, g, exact=False,
+                                what="%s index-free %s" % (wl.name, form))
     _gpu.full_backward_property(gy, idx, gx, wl.shape)
     _gpu.full_backward_property(gy, idx, gxw, wl.shape)
 
