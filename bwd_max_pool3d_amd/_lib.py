@@ -20,8 +20,8 @@ MP3D_IDX_NONE, MP3D_IDX_I32, MP3D_IDX_I64 = -1, 0, 1
 EXPORTS = ("mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
            "mp3d_out_size_ex", "mp3d_forward_ex", "mp3d_backward_ex", "mp3d_backward_recompute",
            "mp3d_recompute_workspace_size", "mp3d_backward_recompute_ws",
-           "mp3d_backward_workspace_bytes", "mp3d_time_next_call", "mp3d_strerror",
-           "mp3d_last_error")
+           "mp3d_backward_workspace_bytes", "mp3d_time_next_call",
+           "mp3d_backward_recompute_static", "mp3d_strerror", "mp3d_last_error")
 
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 _lib = None
@@ -71,6 +71,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mp3d_backward_workspace_bytes.argtypes = ([ctypes.c_int] * 2 + [_i64] * 2 + [_i32] * 3
                                                   + [ctypes.POINTER(ctypes.c_size_t)])
     lib.mp3d_time_next_call.argtypes = [_vp, _vp]
+    lib.mp3d_backward_recompute_static.argtypes = ([_vp, _vp, _vp, _vp, ctypes.c_int]
+                                                   + [_i64] * 5 + [_i32] * 3 + [_a3] * 4
+                                                   + [ctypes.c_int, _vp])
     lib.mp3d_strerror.argtypes = [ctypes.c_int]
     lib.mp3d_strerror.restype = ctypes.c_char_p
     lib.mp3d_last_error.argtypes = []
@@ -79,7 +82,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                  "mp3d_out_size_ex", "mp3d_forward_ex", "mp3d_backward_ex",
                  "mp3d_backward_recompute", "mp3d_recompute_workspace_size",
                  "mp3d_backward_recompute_ws", "mp3d_backward_workspace_bytes",
-                 "mp3d_time_next_call"):
+                 "mp3d_time_next_call", "mp3d_backward_recompute_static"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

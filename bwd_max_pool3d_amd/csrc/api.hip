@@ -511,6 +511,43 @@ int backward(const void *gy, const void *idx, int idx_type, const void *x, const
     }
 }
 
+// Scratch of mp3d_backward_recompute_static: the two-pass index-free
+// backward's workspace in device memory of the library's own, for callers
+// that cannot allocate.  Each device holds its own copy until the process
+// ends.  In host code the array's name is only a stand-in: its device
+// address, per device, comes from hipGetSymbolAddress (scratch_address).
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The current device's address of `scratch`, looked up once per device
+// with that device current; nullptr (and the message set) on failure.
+void *scratch_address()
+{
+    static std::mutex mu;
+    static void *cache[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        hip_status(e, "hipGetDevice");
+        return nullptr;
+    }
+    if (dev < 0 || dev >= 64) {
+        fail(MP3D_EHIP, "device %d beyond the 64 the scratch table holds", dev);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cache[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            return nullptr;
+        }
+        cache[dev] = ptr;
+    }
+    return cache[dev];
+}
+
 }  // namespace
 
 LaunchTiming &launch_timing() { return g_timing; }
@@ -711,6 +748,30 @@ int mp3d_backward_recompute_ws(const void *x, const void *y, const void *gy, voi
                     workspace, workspace_bytes);
 }
 
+
+int mp3d_backward_recompute_static(const void *x, const void *y, const void *gy, void *gx,
+                                   int dtype, int64_t N, int64_t C, int64_t D, int64_t H,
+                                   int64_t W, int32_t od, int32_t oh, int32_t ow,
+                                   const int32_t *kernel, const int32_t *stride,
+                                   const int32_t *pad, const int32_t *dilation, int overlap,
+                                   void *stream)
+{
+    TimingScope timing_scope;
+    int rc = check_common(dtype, N, C, D, H, W);
+    if (rc) return rc;
+    Geom g;
+    if ((rc = set_axes_ex(&g, D, H, W, od, oh, ow, kernel, stride, pad, dilation))) return rc;
+    size_t need = 0;
+    if ((rc = mp3d_recompute_workspace_size(dtype, N, C, od, oh, ow, &need))) return rc;
+    if (need > kScratchBytes)
+        return fail(MP3D_EWORKSPACE, "this call needs %zu bytes of workspace; the library's "
+                    "static scratch holds %zu (use mp3d_backward_recompute_ws)", need,
+                    kScratchBytes);
+    void *ws = nullptr;
+    if (N * C > 0 && !(ws = scratch_address())) return MP3D_EHIP;
+    return backward(gy, nullptr, -1, x, y, gx, dtype, g, N, C, overlap, (hipStream_t)stream,
+                    ws, kScratchBytes);
+}
 
 int mp3d_time_next_call(void *start_event, void *stop_event)
 {

@@ -221,6 +221,26 @@ int mp3d_backward_recompute_ws(const void *x, const void *y, const void *gy, voi
                                int overlap, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * two-pass index-free backward of mp3d_backward_recompute_ws, same
+ * arguments and same results, with the workspace taken from a static
+ * device array of the library (128 MiB; each GPU the library runs on holds
+ * its own copy until the process ends) instead of from the caller.  No
+ * allocation and no free happen in this call.  A call whose workspace
+ * (mp3d_recompute_workspace_size) exceeds 128 MiB fails with
+ * MP3D_EWORKSPACE before any launch.  Every call on one GPU shares that
+ * GPU's array: calls that may overlap in time on one GPU (several streams,
+ * several host threads) race on it and must be serialised by the caller.
+ * Nothing in the array needs to start at any value: the forward pass
+ * writes all of it that the backward pass reads. */
+int mp3d_backward_recompute_static(const void *x, const void *y, const void *gy, void *gx,
+                                   int dtype, int64_t N, int64_t C, int64_t D, int64_t H,
+                                   int64_t W, int32_t od, int32_t oh, int32_t ow,
+                                   const int32_t *kernel, const int32_t *stride,
+                                   const int32_t *pad, const int32_t *dilation, int overlap,
+                                   void *stream);
+
 /* Output extent into *out.  ceil_mode 0: (X + 2*pad - span)/s + 1, rounded
  * down.  ceil_mode 1: rounded up, less one if that last window would start
  * at or beyond X + pad (so every window starts inside the input or the
