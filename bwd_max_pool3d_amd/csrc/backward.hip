@@ -533,7 +533,7 @@ bwd_gather_kernel(const typename T::raw *__restrict__ gy, const Src src,
         for (int k = 0; k < V; ++k) val[k] = T::narrow(Acc(0) + gv[k]);
         const R zero = T::narrow(Acc(0));
         const int32_t qw = QW ? QW : p.qw;
-        const int32_t w0 = ow0 * qw, nel = nwin * qw;   // the row segment under the windows
+        const int32_t w0 = ow0 * qw;                    // the row segment under the windows
         R *gp = gx + plane * (int64_t)p.g.in_plane;
         for (int32_t dd = 0; dd < p.qd; ++dd) {
             for (int32_t hh = 0; hh < p.qh; ++hh) {
