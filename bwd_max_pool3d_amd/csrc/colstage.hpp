@@ -202,4 +202,46 @@ __device__ __forceinline__ uint32_t col_scan_k(const P &sp, int32_t W, int2 wh, 
     return nk != 0xffffffffu ? nk : bk;
 }
 
+// Stage HW for windows of at most K rows and K columns, reading each
+// partial's value once and its d offset only for the winner: the window's
+// maximum first (every value load issued at once; rows and columns clamped
+// to the span, so a clamped tap repeats an element of the window), then the
+// first tap in (h, w) order equal to it.  When that tap is the only one
+// equal to the maximum, its key is the smallest; a tie (several taps, or
+// -0 and +0) or a NaN maximum takes col_scan, which reads every key.
+template <int K, typename P, typename Acc>
+__device__ __forceinline__ uint32_t col_scan_max(const P &sp, int32_t W, int2 wh, int2 ww, Acc &m)
+{
+    int32_t at[K * K];
+    Acc v[K * K];
+    const int32_t nh = wh.y - wh.x, nw = ww.y - ww.x;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+        for (int c = 0; c < K; ++c)
+            at[j * K + c] = min(wh.x + j, wh.y - 1) * W + min(ww.x + c, ww.y - 1);
+#pragma unroll
+    for (int q = 0; q < K * K; ++q) v[q] = sp.value(at[q]);
+    Acc mx = v[0];
+#pragma unroll
+    for (int q = 1; q < K * K; ++q) mx = __builtin_elementwise_maximum(mx, v[q]);
+    int32_t first = 0, hits = 0;
+#pragma unroll
+    for (int q = K * K - 1; q >= 0; --q) {
+        // clamped taps repeat an element: count each element once
+        const bool own = (q / K) < nh && (q % K) < nw;
+        const bool hit = v[q] == mx;
+        first = hit ? q : first;
+        hits += (hit && own) ? 1 : 0;
+    }
+    if (hits == 1) {
+        // the winner's position from its tap number (no indexing of at[]
+        // by a run-time value, which would put it in scratch memory)
+        const int32_t i = min(wh.x + first / K, wh.y - 1) * W + min(ww.x + first % K, ww.y - 1);
+        m = mx;
+        return (sp.dof(i) << 24) | (uint32_t)i;
+    }
+    return col_scan(sp, W, wh, ww, m);
+}
+
 }  // namespace mp3d

@@ -21,7 +21,8 @@ namespace mp3d {
 
 namespace {
 
-template <typename T, typename IT, int MAXKD, int NT>
+// KHW > 0: every window has at most KHW taps along h and along w.
+template <typename T, typename IT, int MAXKD, int NT, int KHW>
 __global__ void __launch_bounds__(NT)
 fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restrict__ y,
                IT *__restrict__ idx, ColPlan p, uint32_t tile0)
@@ -64,8 +65,12 @@ fwd_col_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restric
         const int32_t oh = (int32_t)(q - odl * (uint32_t)B.O);
         const Acc *sv = pv + odl * HW;
         Acc m;
-        const uint32_t bk = col_scan(PartSplit<T>{pv + odl * HW, pd + odl * HW}, W, tab[oh],
-                                     tab[B.O + ow], m);
+        const PartSplit<T> sp{pv + odl * HW, pd + odl * HW};
+        uint32_t bk;
+        if constexpr (KHW > 0)
+            bk = col_scan_max<KHW>(sp, W, tab[oh], tab[B.O + ow], m);
+        else
+            bk = col_scan(sp, W, tab[oh], tab[B.O + ow], m);
         const int32_t bi = (int32_t)(bk & 0xffffffu);
         const int32_t pos = (A.start(od0 + (int32_t)odl) + (int32_t)(bk >> 24)) * HW + bi;
         const Acc best = sv[bi];          // the element itself: keeps the sign of a zero
@@ -87,13 +92,19 @@ hipError_t launch_col(const void *x, void *y, IT *idx, const ColPlan &p, hipStre
     // a multiple of 8 lets blocks map per XCD (the surplus exits)
     for (int64_t t0 = 0; t0 < (int64_t)p.ntiles; t0 += kMaxTileGrid) {
         const uint32_t grid = tile_grid(p.ntiles, t0);
-        if (p.lds_bytes > kColBigLds)
-            launch_kernel((fwd_col_kernel<T, IT, MAXKD, kColBigThreads>), dim3((uint32_t)grid),
-                          dim3(kColBigThreads), p.lds_bytes, s, (const R *)x, (R *)y, idx, p,
+        auto go = [&](auto kern, int nt) {
+            launch_kernel(kern, dim3(grid), dim3(nt), p.lds_bytes, s, (const R *)x, (R *)y, idx, p,
                           (uint32_t)t0);
-        else
-            launch_kernel((fwd_col_kernel<T, IT, MAXKD, kBlock>), dim3((uint32_t)grid),
-                          dim3(kBlock), p.lds_bytes, s, (const R *)x, (R *)y, idx, p, (uint32_t)t0);
+        };
+        // windows of at most 6 x 6 taps along h, w: one value read per
+        // partial (col_scan_max); larger ones: col_scan
+        if (p.lds_bytes > kColBigLds) {
+            if (p.khw <= 6) go(fwd_col_kernel<T, IT, MAXKD, kColBigThreads, 6>, kColBigThreads);
+            else go(fwd_col_kernel<T, IT, MAXKD, kColBigThreads, 0>, kColBigThreads);
+        } else {
+            if (p.khw <= 6) go(fwd_col_kernel<T, IT, MAXKD, kBlock, 6>, kBlock);
+            else go(fwd_col_kernel<T, IT, MAXKD, kBlock, 0>, kBlock);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -197,6 +197,7 @@ struct ColPlan {
     FastDiv ntd_div, ow_div, oh_div;
     uint32_t ntiles;           // planes * ntd
     int32_t maxkd;             // widest window along D
+    int32_t khw;               // most taps of one window along h or w
     uint32_t tab_bytes, pv_bytes, lds_bytes;
 };
 

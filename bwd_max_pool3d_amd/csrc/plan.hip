@@ -20,6 +20,7 @@ namespace {
 
 constexpr int64_t kLdsCap = 64 * 1024;     // forward LDS per workgroup, all uses
 constexpr int64_t kAccBudget = 40 * 1024;   // backward accumulator per workgroup
+constexpr int32_t kColMaxTod = 2;           // column forward: output slices per tile
 constexpr int64_t kOrdBudget = 40 * 1024;   // the same, ordered slabs
 constexpr int64_t kWantTiles = 1024;        // >= 4 workgroups per CU
 constexpr int64_t kOwnerBudget = 80 * 1024; // owner gather: LDS per workgroup (2 per CU)
@@ -211,7 +212,10 @@ bool plan_col(const Geom &g, int es, const void *x, ColPlan *p)
     if (tod < 1) return false;
     const int64_t per_plane = cdiv(kWantTiles, std::max<int64_t>(g.planes, 1));
     tod = std::min<int32_t>(tod, (int32_t)std::max<int64_t>(1, A.O / per_plane));
-    tod = balance(A.O, tod);
+    // at most two output slices per tile: measured on the adaptive f32
+    // workload (5 output slices of 16), 103 us with tiles of 2, 2, 1 against
+    // 107 with one tile of 5, 107 with 3 + 2 and 110 with 5 tiles of 1
+    tod = balance(A.O, std::min<int32_t>(tod, kColMaxTod));
     const int64_t ntd = cdiv(A.O, tod);
     const int64_t ntiles = g.planes * ntd;
     if (ntiles >= ((int64_t)1 << 31) || (int64_t)tod * B.O * Cw.O >= ((int64_t)1 << 31))
@@ -224,6 +228,7 @@ bool plan_col(const Geom &g, int es, const void *x, ColPlan *p)
     p->oh_div = FastDiv((uint32_t)B.O);
     p->ntiles = (uint32_t)ntiles;
     p->maxkd = (int32_t)maxkd;
+    p->khw = (int32_t)std::min<int64_t>(std::max(max_taps(B), max_taps(Cw)), 1 << 20);
     p->tab_bytes = (uint32_t)tab;
     p->pv_bytes = (uint32_t)(((int64_t)tod * HW * ab + 15) & ~(int64_t)15);
     p->lds_bytes = (uint32_t)(tab + p->pv_bytes + (int64_t)tod * HW);
