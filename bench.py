@@ -490,7 +490,7 @@ def main():
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     collect(sink)
-    step_rows = [op_row(op, "mean") for op in ops]
+    step_rows = [op_row(op, "mean") for op in ops if op.us]
     print("[bench] timed %d steps, kernel times per call" % args.steps, file=sys.stderr, flush=True)
 
     # Pass 3: each workload alone, flushed before every iteration.
@@ -528,19 +528,21 @@ def main():
             "meets_target": (gbs / PEAK_GBS >= TARGET_FRAC) if large else None,
             "per_op": rows})
 
-    dom_op = max(ops, key=lambda o: stats(o.us)["median"])
-    dom = op_row(dom_op, "mean")
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("source_hash") == kernel_source_hash() and dom["op"] in tr.get("ops", {}):
-            traffic = tr["ops"][dom["op"]]["hbm_bytes"]
-    roofline = {"bound": "hbm", "achieved": dom["GB_s"], "peak": PEAK_GBS, "unit": "GB/s",
-                "frac": round(dom["GB_s"] / PEAK_GBS, 4), "traffic": traffic,
-                "kernel": dom["op"], "algorithmic_bytes": dom["bytes"], "avg_us": dom["us"],
-                "timing": "mean kernel time over the per-workload pass (timing hook), "
-                          "launches after an untimed 1 GiB read"}
+    roofline = None
+    if ops:
+        dom_op = max(ops, key=lambda o: stats(o.us)["median"])
+        dom = op_row(dom_op, "mean")
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f)
+            if tr.get("source_hash") == kernel_source_hash() and dom["op"] in tr.get("ops", {}):
+                traffic = tr["ops"][dom["op"]]["hbm_bytes"]
+        roofline = {"bound": "hbm", "achieved": dom["GB_s"], "peak": PEAK_GBS, "unit": "GB/s",
+                    "frac": round(dom["GB_s"] / PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": dom["op"], "algorithmic_bytes": dom["bytes"], "avg_us": dom["us"],
+                    "timing": "mean kernel time over the per-workload pass (timing hook), "
+                              "launches after an untimed 1 GiB read"}
 
     # Small shapes of the PR #308 page's latency table: adaptive backward.
     latency = []
@@ -592,7 +594,7 @@ def main():
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     step_bytes = sum(op.nbytes for op in ops)
-    value = step_bytes / (ms_step * 1e-3) / 1e9
+    value = step_bytes / (ms_step * 1e-3) / 1e9 if ops else 0.0
     vrows = lambda kinds: [op_row(op) for op in var_ops if op.kind in kinds]
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,

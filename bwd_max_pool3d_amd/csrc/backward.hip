@@ -583,6 +583,90 @@ bwd_gather_kernel(const typename T::raw *__restrict__ gy, const Src src,
     }
 }
 
+// The gather again, one 16-byte chunk of gx per thread: when rows are whole
+// chunks (W * element size a multiple of 16, gx on 16 bytes) and a chunk
+// holds whole windows along w (QW divides the chunk's VE elements), chunk c
+// is elements [c*VE, c*VE + VE) of one row, under the NW = VE / QW
+// consecutive windows (d / qd, h / qh, w0 / qw ...).  The lanes of a wave
+// write consecutive chunks, so every store instruction covers whole cache
+// lines of gx (the window-group kernel above writes rows qd*qh apart per
+// instruction, and its streaming stores then leave partial lines); the
+// windows' idx and gy are read by the qd*qh chunks under them, from cache
+// after the first.
+template <typename T, typename Src, int QW>
+__global__ void __launch_bounds__(kBlock)
+bwd_gather_chunk_kernel(const typename T::raw *__restrict__ gy, const Src src,
+                        typename T::raw *__restrict__ gx, GatherPlan p)
+{
+    using R = typename T::raw;
+    using Acc = typename T::acc;
+    constexpr int VE = 16 / (int)sizeof(R);
+    constexpr int NW = VE / QW;
+    static_assert(NW * QW == VE, "whole windows per chunk");
+    const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X, HW = H * W;
+    const int32_t OH = p.g.ax[1].O, OW = p.g.ax[2].O;
+    const int64_t nchunk = p.g.planes * (int64_t)p.g.in_plane / VE;
+    const R zero = T::narrow(Acc(0));
+    for (int64_t c = (int64_t)blockIdx.x * kBlock + threadIdx.x; c < nchunk;
+         c += (int64_t)gridDim.x * kBlock) {
+        const int64_t e0 = c * VE;
+        int64_t plane;
+        if (p.fast_el) plane = p.plane_div.div((uint32_t)e0);
+        else plane = e0 / p.g.in_plane;
+        const int32_t pos0 = (int32_t)(e0 - plane * p.g.in_plane);   // plane position
+        const int32_t d = (int32_t)p.hw_div.div((uint32_t)pos0);
+        const int32_t rem = pos0 - d * HW;
+        const int32_t h = (int32_t)p.w_div.div((uint32_t)rem);
+        const int32_t w0 = rem - h * W;
+        const int32_t od = (int32_t)p.qd_div.div((uint32_t)d), oh = (int32_t)p.qh_div.div((uint32_t)h);
+        const int64_t o0 = plane * (int64_t)p.g.out_plane + ((int64_t)od * OH + oh) * OW + w0 / QW;
+        int32_t ix[NW];
+        R gr[NW];
+        if constexpr (NW == 4) {
+            if (p.vec_in && (o0 & 3) == 0) {
+                // four windows: idx as one 16-byte vector (two for int64),
+                // gy as one 8- or 16-byte vector
+                src.load4(o0, ix);
+                if constexpr (sizeof(R) == 2) {
+                    const u32x2 g2 = *reinterpret_cast<const u32x2 *>(gy + o0);
+                    gr[0] = (R)g2.x; gr[1] = (R)(g2.x >> 16); gr[2] = (R)g2.y; gr[3] = (R)(g2.y >> 16);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < NW; ++k) gr[k] = gy[o0 + k];
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < NW; ++k) {
+                    ix[k] = src(o0 + k);
+                    gr[k] = gy[o0 + k];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NW; ++k) {
+                ix[k] = src(o0 + k);
+                gr[k] = gy[o0 + k];
+            }
+        }
+        R e[VE];
+#pragma unroll
+        for (int q = 0; q < VE; ++q)
+            // 0 + gy: a -0 gradient gives +0, as the accumulate path does
+            e[q] = ix[q / QW] == pos0 + q ? T::narrow(Acc(0) + T::widen(gr[q / QW])) : zero;
+        uint32_t w4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (sizeof(R) == 2)
+                w4[j] = (uint32_t)e[2 * j] | ((uint32_t)e[2 * j + 1] << 16);
+            else if constexpr (sizeof(R) == 4)
+                w4[j] = __builtin_bit_cast(uint32_t, e[j]);
+            else
+                w4[j] = (uint32_t)(__builtin_bit_cast(uint64_t, e[j / 2]) >> (32 * (j % 2)));
+        }
+        st_stream(reinterpret_cast<u32x4 *>(gx + e0), u32x4{w4[0], w4[1], w4[2], w4[3]});
+    }
+}
+
 }  // namespace
 
 template <typename T, typename Src>
@@ -661,6 +745,25 @@ hipError_t launch_backward_gather(const void *gy, const Src &src, void *gx, cons
                                   hipStream_t s)
 {
     using R = typename T::raw;
+    constexpr int VE = 16 / (int)sizeof(R);
+    // one chunk per thread where rows are whole chunks and windows fit
+    // chunks (qw 1 or 2; qw 2 and 8-byte elements: a chunk is one window)
+    const bool rows16 = ((int64_t)p.g.ax[2].X * (int64_t)sizeof(R)) % 16 == 0 &&
+                        (uintptr_t)gx % 16 == 0;
+    if (rows16 && (p.qw == 1 || (p.qw == 2 && VE % 2 == 0))) {
+        const int64_t chunks = p.g.planes * (int64_t)p.g.in_plane / VE;
+        int64_t grid = std::min<int64_t>((chunks + kBlock - 1) / kBlock, kMaxTileGrid);
+        if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
+        GatherPlan q = p;
+        q.vec_in = src.aligned4() && (uintptr_t)gy % 16 == 0;
+        if (p.qw == 1)
+            launch_kernel((bwd_gather_chunk_kernel<T, Src, 1>), dim3((uint32_t)grid), dim3(kBlock),
+                          0, s, (const R *)gy, src, (R *)gx, q);
+        else
+            launch_kernel((bwd_gather_chunk_kernel<T, Src, 2>), dim3((uint32_t)grid), dim3(kBlock),
+                          0, s, (const R *)gy, src, (R *)gx, q);
+        return hipGetLastError();
+    }
     GatherPlan q = p;
     q.vec_in = src.aligned4() && (sizeof(R) != 2 || (uintptr_t)gy % 8 == 0);
     if (q.qw == 1)

@@ -171,6 +171,9 @@ struct GatherPlan {
     FastDiv oh_div, od_div;    // by OH, by OD
     int32_t vec_in;            // idx (and gy) may be read as vectors of 4 windows
     uint32_t grid;             // workgroups (threads are strided over them)
+    // the chunk kernel: element -> (plane, d, h, w), and d, h to windows
+    int32_t fast_el;           // N*C*D*H*W < 2^31: plane_div applies
+    FastDiv plane_div, hw_div, w_div, qd_div, qh_div;
 };
 
 // Forward with compile-time window shape: one thread per V consecutive
