@@ -378,15 +378,23 @@ def cpu_baseline(target_s: float, threads: int = 1):
 
     probe = 1.0 / 512 * threads
     b, t, _ = run(probe)
-    frac = min(1.0, probe * target_s / max(t, 1e-3))
-    b, t, used = run(frac)
+    want = probe * target_s / max(t, 1e-3)
+    frac = min(1.0, want)
+    # when the whole step takes less than the target, it is run again (at
+    # most three times in all)
+    reps = max(1, min(3, int(want))) if want > 1.0 else 1
+    b = t = 0.0
+    for _ in range(reps):
+        b1, t1, used = run(frac)
+        b, t = b + b1, t + t1
     if pool is not None:
         pool.shutdown()
     who = "one thread" if threads == 1 else "%d threads over contiguous plane ranges" % threads
+    times = "" if reps == 1 else ", %d times" % reps
     return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "plain C oracle, %s, forward+backward on %.4f of each "
-                      "workload's planes (%s): %.3g GB of algorithmic bytes in %.1f s"
-                      % (who, frac, ", ".join(used), b / 1e9, t),
+                      "workload's planes (%s)%s: %.3g GB of algorithmic bytes in %.1f s"
+                      % (who, frac, ", ".join(used), times, b / 1e9, t),
             "host_cpu": host_cpu()}
 
 

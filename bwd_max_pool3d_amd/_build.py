@@ -67,5 +67,19 @@ def build(out: str = LIBRARY, verbose: bool = False) -> str:
     return out
 
 
+def build_executable(src: str, out: str, verbose: bool = False) -> str:
+    """Compile a stand-alone HIP program (the HBM ceiling benchmark) with the
+    library's flags."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *[f for f in HIPCC_FLAGS if f != "-fPIC"], "-o", tmp, src]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
