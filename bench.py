@@ -343,6 +343,7 @@ def cpu_baseline(target_s: float, threads: int = 1):
 
     def run(frac):
         total_bytes = 0
+        total_elems = 0
         elapsed = 0.0
         planes_used = []
         for wl in workloads.WORKLOADS:
@@ -365,6 +366,7 @@ def cpu_baseline(target_s: float, threads: int = 1):
             elapsed += time.perf_counter() - t0
             nin, nout = xs.size, sum(y.size for y, _ in fw)
             total_bytes += nin * es + nout * (es + 4)
+            total_elems += nin
             if wl.backward:
                 gy = draw(wl, "gy", (P, 1) + o3)[:np_].contiguous()
                 gys = storage(gy)
@@ -374,27 +376,29 @@ def cpu_baseline(target_s: float, threads: int = 1):
                                                     side=False), jobs)
                 elapsed += time.perf_counter() - t0
                 total_bytes += nout * (es + 4) + nin * es
-        return total_bytes, elapsed, planes_used
+                total_elems += nin
+        return total_bytes, elapsed, planes_used, total_elems
 
     probe = 1.0 / 512 * threads
-    b, t, _ = run(probe)
+    b, t, _, _ = run(probe)
     want = probe * target_s / max(t, 1e-3)
     frac = min(1.0, want)
-    # when the whole step takes less than the target, it is run again (at
-    # most three times in all)
-    reps = max(1, min(3, int(want))) if want > 1.0 else 1
-    b = t = 0.0
-    for _ in range(reps):
-        b1, t1, used = run(frac)
-        b, t = b + b1, t + t1
+    # when the whole step takes well under the target, it is run up to three
+    # times and the median rate is reported
+    reps = min(3, max(1, int(round(want)))) if want > 1.0 else 1
+    runs = [run(frac) for _ in range(reps)]
     if pool is not None:
         pool.shutdown()
+    mid = sorted(runs, key=lambda r: r[0] / r[1])[len(runs) // 2]
+    rate, erate = mid[0] / mid[1], mid[3] / mid[1]
+    b, t, used = runs[0][0], sum(r[1] for r in runs), runs[0][2]
     who = "one thread" if threads == 1 else "%d threads over contiguous plane ranges" % threads
-    times = "" if reps == 1 else ", %d times" % reps
-    return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    times = "" if reps == 1 else ", median of %d runs" % reps
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "elems_per_s": round(erate, 1),
             "sample": "plain C oracle, %s, forward+backward on %.4f of each "
-                      "workload's planes (%s)%s: %.3g GB of algorithmic bytes in %.1f s"
-                      % (who, frac, ", ".join(used), times, b / 1e9, t),
+                      "workload's planes (%s)%s: %.3g GB of algorithmic bytes per run, %.1f s "
+                      "in all" % (who, frac, ", ".join(used), times, b / 1e9, t),
             "host_cpu": host_cpu()}
 
 
@@ -405,6 +409,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-oracle sample size in seconds (0 skips the leg)")
+    ap.add_argument("--small-iters", type=int, default=1000,
+                    help="iterations of the per-workload pass for the workloads under 100 MB "
+                         "(launch-bound; the large ones take --steps)")
     ap.add_argument("--only", default=None,
                     help="time only the ops whose name contains this text (profiling aid; "
                          "the JSON then covers that subset)")
@@ -509,7 +516,9 @@ def main():
         by_wl.setdefault(op.wl.name, []).append(op)
     for name, wops in by_wl.items():
         wops.sort(key=lambda o: 0 if o.kind == "fwd" else 1)
-        for _ in range(args.steps):
+        # the small workloads are launch-bound: many more iterations
+        iters = args.steps if sum(o.nbytes for o in wops) > 100e6 else max(args.steps, args.small_iters)
+        for _ in range(iters):
             sink = []
             flush_buf.sum()
             for op in wops:
