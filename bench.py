@@ -113,9 +113,10 @@ class Hip:
 class Op:
     """One C-ABI call, with its inputs and preallocated outputs."""
 
-    def __init__(self, wl, kind, fn, nbytes, elems, note):
+    def __init__(self, wl, kind, fn, nbytes, elems, note, out_elems=None):
         self.wl, self.kind, self.fn, self.nbytes, self.elems, self.note = (
             wl, kind, fn, nbytes, elems, note)
+        self.out_elems = out_elems     # pooled outputs (y / gy elements) per call
         self.us = []           # kernel times, microseconds
 
     @property
@@ -138,6 +139,8 @@ def op_row(op, key="median"):
             "us_mean": round(st["mean"], 3), "n": st["n"], "bytes": op.nbytes,
             "GB_s": round(op.nbytes / (t * 1e-6) / 1e9, 1),
             "elems_per_s": round(op.elems / (t * 1e-6), 1),
+            "out_elems_per_s": (round(op.out_elems / (t * 1e-6), 1)
+                                if op.out_elems is not None else None),
             "frac_of_peak": round(op.nbytes / (t * 1e-6) / 1e9 / PEAK_GBS, 4),
             "note": op.note}
 
@@ -163,7 +166,7 @@ def build_ops(torch, mp, workloads, variants=True):
             f = (lambda x=x, o3=o3, y=y, idx=idx: mp.amp3d_forward(x, o3, out=(y, idx)))
         else:
             f = (lambda x=x, wl=wl, y=y, idx=idx: mp.mp3d_forward(x, wl.kernel, wl.stride, out=(y, idx)))
-        fwd_ops.append(Op(wl, "fwd", f, fbytes, nin, "forward"))
+        fwd_ops.append(Op(wl, "fwd", f, fbytes, nin, "forward", out_elems=nout))
         if wl.adaptive:
             v = (lambda x=x, o3=o3, y=y: mp.amp3d_forward(x, o3, out=y, indices=False))
         else:
@@ -176,7 +179,7 @@ def build_ops(torch, mp, workloads, variants=True):
             bbytes = nout * es + nout * 4 + nin * es
             b = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
                 gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, out=gx))
-            bwd_ops.append(Op(wl, "bwd", b, bbytes, nin, "backward"))
+            bwd_ops.append(Op(wl, "bwd", b, bbytes, nin, "backward", out_elems=nout))
             o = (lambda gy=gy, idx=idx, wl=wl, gx=gx: mp.mp3d_backward(
                 gy, idx, wl.shape, kernel=wl.kernel, stride=wl.stride, overlap=2, out=gx))
             ord_ops.append(Op(wl, "bwd_ordered", o, bbytes, nin, "ordered backward"))

@@ -1,4 +1,4 @@
-// backward_mark.hip -- the overlapping-window backward as an owner gather:
+// backward_owner.hip -- the overlapping-window backward as an owner gather:
 // each element's contributions are summed by one window, out of LDS, with
 // no atomics.
 //
