@@ -21,6 +21,12 @@ PyTorch fallback: if the library is missing every call raises ImportError.
 
 x, y, gy and gx are float32, float16, bfloat16 or float64; idx is int32 (int64 on
 request: index_dtype=torch.int64), flat within each D*H*W plane.
+
+The names of the three-call sketch are kept as aliases:
+  max_pool3d(x, kernel, stride) = mp3d_forward,
+  adaptive_max_pool3d(x, out_size) = amp3d_forward,
+  max_pool3d_backward(gy, idx, in_shape, ..., overlap=None) = mp3d_backward
+      (overlap None: the library picks; False: the gather; True: accumulate).
 """
 from __future__ import annotations
 
@@ -34,7 +40,8 @@ from ._lib import Mp3dError  # noqa: F401
 __all__ = ["mp3d_forward", "amp3d_forward", "mp3d_backward", "mp3d_out_size",
            "mp3d_forward_ex", "mp3d_backward_ex", "mp3d_out_size_ex",
            "mp3d_backward_recompute", "recompute_workspace_size",
-           "mp3d_backward_workspace_bytes", "mp3d_time_next_call", "Mp3dError"]
+           "mp3d_backward_workspace_bytes", "mp3d_time_next_call", "Mp3dError",
+           "max_pool3d", "adaptive_max_pool3d", "max_pool3d_backward"]
 
 _IDX = {torch.int32: _lib.MP3D_IDX_I32, torch.int64: _lib.MP3D_IDX_I64}
 
@@ -332,3 +339,27 @@ def mp3d_backward_recompute(x: torch.Tensor, y: torch.Tensor, gy: torch.Tensor, 
                                               int(overlap), workspace.data_ptr(),
                                               workspace.numel(), _stream(gy)))
     return out
+
+
+def overlap_code(overlap) -> int:
+    """The C ABI's overlap argument for the sketch's ``overlap``: None lets
+    the library choose (-1), False asks for the gather (0), True for the
+    accumulate path (1); an int is passed through (2: ordered)."""
+    return -1 if overlap is None else int(overlap)
+
+
+def max_pool3d(x: torch.Tensor, kernel, stride=None, out=None, indices: bool = True):
+    """Alias of mp3d_forward under the sketch's name."""
+    return mp3d_forward(x, kernel, stride, out=out, indices=indices)
+
+
+def adaptive_max_pool3d(x: torch.Tensor, out_size, out=None, indices: bool = True):
+    """Alias of amp3d_forward under the sketch's name."""
+    return amp3d_forward(x, out_size, out=out, indices=indices)
+
+
+def max_pool3d_backward(gy: torch.Tensor, idx: torch.Tensor, in_shape, kernel=None, stride=None,
+                        overlap=None, out: torch.Tensor | None = None):
+    """Alias of mp3d_backward under the sketch's name; ``overlap`` None,
+    False or True (or the C ABI's integer codes)."""
+    return mp3d_backward(gy, idx, in_shape, kernel, stride, overlap=overlap_code(overlap), out=out)
