@@ -187,6 +187,42 @@ def test_misaligned_pointers(orc, dtype):
         _gpu.check_backward(orc, gy0, idx.cpu(), shape, gxd, exact=False, what="misaligned bwd")
 
 
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+def test_misaligned_pointers_general_kernels(orc, dtype, monkeypatch):
+    """Tensors one element past a 16-byte boundary on the kernels that use
+    16-byte vectors when they can (row-vector and column forwards, chunk
+    gather, slab backward): with the small-tensor kernels off, each must
+    notice the misalignment and still give the oracle's result, a divisible
+    geometry (the gather) bit for bit."""
+    monkeypatch.setenv("MP3D_SMALL", "0")
+    code = _gpu.CODE[dtype]
+    shape = (2, 2, 8, 8, 16)
+    n = int(np.prod(shape))
+    x0 = _pins.from_storage(_pins.draw(shape, code, "ties", 13), code)
+    buf = torch.empty(n + 1, dtype=dtype, device="cuda")
+    xd = buf[1:].view(shape)
+    xd.copy_(x0.cuda())
+    assert xd.data_ptr() % 16 != 0
+    for out, k, s in [((4, 4, 8), None, None), (None, (2, 2, 2), (2, 2, 2)),
+                      ((3, 5, 6), None, None), (None, (3, 3, 3), (2, 2, 2))]:
+        y, idx = _gpu.gpu_forward(xd, out, k, s)
+        yo, io = _gpu.oracle_forward(orc, x0, out, k, s)
+        _gpu.assert_forward_match(y, idx, yo, io, "misaligned fwd %s %s" % (out, k))
+        gy0 = _pins.from_storage(_pins.draw(tuple(y.shape), code, "ties", 14), code)
+        gbuf = torch.empty(gy0.numel() + 1, dtype=dtype, device="cuda")
+        gyd = gbuf[1:].view(gy0.shape)
+        gyd.copy_(gy0.cuda())
+        ibuf = torch.empty(idx.numel() + 1, dtype=idx.dtype, device="cuda")
+        idd = ibuf[1:].view(idx.shape)
+        idd.copy_(idx)
+        xbuf = torch.full((n + 1,), float("nan"), dtype=dtype, device="cuda")
+        gxd = xbuf[1:].view(shape)
+        mp.mp3d_backward(gyd, idd, shape, kernel=k, stride=s, out=gxd)
+        tiles = k is None and all(X % O == 0 for X, O in zip(shape[2:], out)) or k == (2, 2, 2)
+        _gpu.check_backward(orc, gy0, idx.cpu(), shape, gxd, exact=tiles,
+                            what="misaligned bwd %s %s" % (out, k))
+
+
 def test_many_small_planes(orc):
     shape = (256, 256, 2, 2, 2)
     x = _pins.from_storage(_pins.draw(shape, 1, "ties", 5), 1)
