@@ -583,16 +583,18 @@ bwd_gather_kernel(const typename T::raw *__restrict__ gy, const Src src,
     }
 }
 
-// The gather again, one 16-byte chunk of gx per thread: when rows are whole
-// chunks (W * element size a multiple of 16, gx on 16 bytes) and a chunk
-// holds whole windows along w (QW divides the chunk's VE elements), chunk c
-// is elements [c*VE, c*VE + VE) of one row, under the NW = VE / QW
-// consecutive windows (d / qd, h / qh, w0 / qw ...).  The lanes of a wave
-// write consecutive chunks, so every store instruction covers whole cache
-// lines of gx (the window-group kernel above writes rows qd*qh apart per
-// instruction, and its streaming stores then leave partial lines); the
-// windows' idx and gy are read by the qd*qh chunks under them, from cache
-// after the first.
+// The gather again, by 16-byte chunk columns: when rows are whole chunks
+// (W * element size a multiple of 16, gx on 16 bytes) and a chunk holds
+// whole windows along w (QW divides the chunk's VE elements), thread u is
+// chunk c of a slice (elements [c*VE, c*VE + VE) of the H*W slice, c < nc =
+// H*W / VE) under output slice od of one plane.  It reads the idx and gy of
+// the NW = VE / QW windows above that chunk once and stores the chunk in
+// each of the qd input slices od*qd .. od*qd + qd - 1.  The lanes of a wave
+// store consecutive chunks of one slice, so every store instruction covers
+// whole cache lines of gx (the window-group kernel above writes rows qd*qh
+// apart per instruction, and its streaming stores then leave partial
+// lines); a window's idx and gy are read by the qh rows of chunks under
+// it, which sit in the same or the next wave.
 template <typename T, typename Src, int QW>
 __global__ void __launch_bounds__(kBlock)
 bwd_gather_chunk_kernel(const typename T::raw *__restrict__ gy, const Src src,
@@ -603,22 +605,27 @@ bwd_gather_chunk_kernel(const typename T::raw *__restrict__ gy, const Src src,
     constexpr int VE = 16 / (int)sizeof(R);
     constexpr int NW = VE / QW;
     static_assert(NW * QW == VE, "whole windows per chunk");
-    const int32_t H = p.g.ax[1].X, W = p.g.ax[2].X, HW = H * W;
-    const int32_t OH = p.g.ax[1].O, OW = p.g.ax[2].O;
-    const int64_t nchunk = p.g.planes * (int64_t)p.g.in_plane / VE;
+    const int32_t W = p.g.ax[2].X, HW = p.g.ax[1].X * W;
+    const int32_t OD = p.g.ax[0].O, OH = p.g.ax[1].O, OW = p.g.ax[2].O;
+    const int32_t nc = p.nc;
+    const int64_t total = p.g.planes * (int64_t)OD * nc;
     const R zero = T::narrow(Acc(0));
-    for (int64_t c = (int64_t)blockIdx.x * kBlock + threadIdx.x; c < nchunk;
-         c += (int64_t)gridDim.x * kBlock) {
-        const int64_t e0 = c * VE;
-        int64_t plane;
-        if (p.fast_el) plane = p.plane_div.div((uint32_t)e0);
-        else plane = e0 / p.g.in_plane;
-        const int32_t pos0 = (int32_t)(e0 - plane * p.g.in_plane);   // plane position
-        const int32_t d = (int32_t)p.hw_div.div((uint32_t)pos0);
-        const int32_t rem = pos0 - d * HW;
-        const int32_t h = (int32_t)p.w_div.div((uint32_t)rem);
-        const int32_t w0 = rem - h * W;
-        const int32_t od = (int32_t)p.qd_div.div((uint32_t)d), oh = (int32_t)p.qh_div.div((uint32_t)h);
+    for (int64_t u = (int64_t)blockIdx.x * kBlock + threadIdx.x; u < total;
+         u += (int64_t)gridDim.x * kBlock) {
+        int64_t op, plane;                                 // op = plane * OD + od
+        if (p.fast_col) {
+            op = p.nc_div.div((uint32_t)u);
+            plane = p.od_div.div((uint32_t)op);
+        } else {
+            op = u / nc;
+            plane = op / OD;
+        }
+        const int32_t c = (int32_t)(u - op * nc);
+        const int32_t od = (int32_t)(op - plane * OD);
+        const int32_t e = c * VE;                          // element in the slice
+        const int32_t h = (int32_t)p.w_div.div((uint32_t)e);
+        const int32_t w0 = e - h * W;
+        const int32_t oh = (int32_t)p.qh_div.div((uint32_t)h);
         const int64_t o0 = plane * (int64_t)p.g.out_plane + ((int64_t)od * OH + oh) * OW + w0 / QW;
         int32_t ix[NW];
         R gr[NW];
@@ -648,22 +655,33 @@ bwd_gather_chunk_kernel(const typename T::raw *__restrict__ gy, const Src src,
                 gr[k] = gy[o0 + k];
             }
         }
-        R e[VE];
+        // 0 + gy: a -0 gradient gives +0, as the accumulate path does
+        R g0[NW];
 #pragma unroll
-        for (int q = 0; q < VE; ++q)
-            // 0 + gy: a -0 gradient gives +0, as the accumulate path does
-            e[q] = ix[q / QW] == pos0 + q ? T::narrow(Acc(0) + T::widen(gr[q / QW])) : zero;
-        uint32_t w4[4];
+        for (int k = 0; k < NW; ++k) g0[k] = T::narrow(Acc(0) + T::widen(gr[k]));
+        const int32_t d0 = od * p.qd;
+        R *col = gx + plane * (int64_t)p.g.in_plane + (int64_t)d0 * HW + e;
+        for (int32_t dd = 0; dd < p.qd; ++dd) {
+            const int32_t pos0 = (d0 + dd) * HW + e;       // plane position of the chunk
+            uint32_t w4[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (sizeof(R) == 2)
-                w4[j] = (uint32_t)e[2 * j] | ((uint32_t)e[2 * j + 1] << 16);
-            else if constexpr (sizeof(R) == 4)
-                w4[j] = __builtin_bit_cast(uint32_t, e[j]);
-            else
-                w4[j] = (uint32_t)(__builtin_bit_cast(uint64_t, e[j / 2]) >> (32 * (j % 2)));
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (sizeof(R) == 2) {
+                    const int q = 2 * j;
+                    const R lo = ix[q / QW] == pos0 + q ? g0[q / QW] : zero;
+                    const R hi = ix[(q + 1) / QW] == pos0 + q + 1 ? g0[(q + 1) / QW] : zero;
+                    w4[j] = (uint32_t)lo | ((uint32_t)hi << 16);
+                } else if constexpr (sizeof(R) == 4) {
+                    w4[j] = __builtin_bit_cast(uint32_t, ix[j / QW] == pos0 + j ? g0[j / QW] : zero);
+                } else {
+                    const int q = j / 2;
+                    const R v = ix[q / QW] == pos0 + q ? g0[q / QW] : zero;
+                    w4[j] = (uint32_t)(__builtin_bit_cast(uint64_t, v) >> (32 * (j % 2)));
+                }
+            }
+            st_stream(reinterpret_cast<u32x4 *>(col + (int64_t)dd * HW),
+                      u32x4{w4[0], w4[1], w4[2], w4[3]});
         }
-        st_stream(reinterpret_cast<u32x4 *>(gx + e0), u32x4{w4[0], w4[1], w4[2], w4[3]});
     }
 }
 
@@ -751,10 +769,14 @@ hipError_t launch_backward_gather(const void *gy, const Src &src, void *gx, cons
     const bool rows16 = ((int64_t)p.g.ax[2].X * (int64_t)sizeof(R)) % 16 == 0 &&
                         (uintptr_t)gx % 16 == 0;
     if (rows16 && (p.qw == 1 || (p.qw == 2 && VE % 2 == 0))) {
-        const int64_t chunks = p.g.planes * (int64_t)p.g.in_plane / VE;
-        int64_t grid = std::min<int64_t>((chunks + kBlock - 1) / kBlock, kMaxTileGrid);
-        if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
+        // one thread per chunk column: planes * OD * (H*W / VE) threads
         GatherPlan q = p;
+        q.nc = p.g.ax[1].X * p.g.ax[2].X / VE;
+        q.nc_div = FastDiv((uint32_t)q.nc);
+        const int64_t cols = p.g.planes * (int64_t)p.g.ax[0].O * q.nc;
+        q.fast_col = cols < ((int64_t)1 << 31);
+        int64_t grid = std::min<int64_t>((cols + kBlock - 1) / kBlock, kMaxTileGrid);
+        if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
         q.vec_in = src.aligned4() && (uintptr_t)gy % 16 == 0;
         if (p.qw == 1)
             launch_kernel((bwd_gather_chunk_kernel<T, Src, 1>), dim3((uint32_t)grid), dim3(kBlock),

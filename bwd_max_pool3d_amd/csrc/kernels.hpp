@@ -171,9 +171,10 @@ struct GatherPlan {
     FastDiv oh_div, od_div;    // by OH, by OD
     int32_t vec_in;            // idx (and gy) may be read as vectors of 4 windows
     uint32_t grid;             // workgroups (threads are strided over them)
-    // the chunk kernel: element -> (plane, d, h, w), and d, h to windows
-    int32_t fast_el;           // N*C*D*H*W < 2^31: plane_div applies
-    FastDiv plane_div, hw_div, w_div, qd_div, qh_div;
+    // the chunk kernel: thread -> (plane, od, chunk c of a slice), c -> (h, w)
+    int32_t nc;                // 16-byte chunks per H*W slice (set by the launcher)
+    int32_t fast_col;          // N*C*OD*nc < 2^31: nc_div and od_div apply
+    FastDiv nc_div, w_div, qh_div;
 };
 
 // Forward with compile-time window shape: one thread per V consecutive

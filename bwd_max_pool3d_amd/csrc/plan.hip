@@ -531,11 +531,9 @@ void plan_gather(const Geom &g, GatherPlan *p)
     p->oh_div = FastDiv((uint32_t)g.ax[1].O);
     p->od_div = FastDiv((uint32_t)g.ax[0].O);
     p->vec_in = 0;                             // set by the launcher (pointer alignment)
-    p->fast_el = g.planes * (int64_t)g.in_plane < ((int64_t)1 << 31);
-    p->plane_div = FastDiv((uint32_t)g.in_plane);
-    p->hw_div = FastDiv((uint32_t)(g.ax[1].X * g.ax[2].X));
+    p->nc = 0;                                 // set by the chunk kernel's launcher
+    p->fast_col = 0;
     p->w_div = FastDiv((uint32_t)g.ax[2].X);
-    p->qd_div = FastDiv((uint32_t)p->qd);
     p->qh_div = FastDiv((uint32_t)p->qh);
     int64_t grid = std::min<int64_t>(cdiv(threads, kBlock), kMaxGrid);
     if (grid >= 64) grid = (grid + 7) & ~(int64_t)7;
