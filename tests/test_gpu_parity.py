@@ -56,6 +56,9 @@ CASES = [
     ((2, 1, 3, 5000, 1), (2, 777, 1), None, None),
     ((1, 2, 9, 10, 11), None, (5, 5, 5), (1, 1, 1)),      # five windows per element and axis
     ((2, 2, 12, 20, 24), None, (3, 3, 3), (2, 2, 2)),     # several slabs per plane
+    ((1, 2, 16, 8, 16), (2, 4, 8), None, None),           # gather: 8 slices per output slice
+    ((2, 1, 12, 6, 16), (3, 3, 16), None, None),          # gather: windows one wide along w
+    ((1, 1, 32, 4, 32), None, (16, 2, 2), (16, 2, 2)),    # gather: 16 slices per output slice
 ]
 
 
