@@ -42,7 +42,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // computing nothing, when a window holds a NaN.
 template <int KD, int KH, int KW, int SW, int SPAN, int V, int NQ, typename Pos>
 __device__ __forceinline__ bool f16_first_max(const uint32_t (&q)[KD][KH][NQ], Pos pos,
-                                              const uint16_t *__restrict__ xp, bool active,
+                                              const uint16_t *__restrict__ xp, int32_t nvalid,
                                               int32_t (&io)[V], uint16_t (&yo)[V])
 {
     static_assert(KD <= 4 && KH <= 4 && KW <= 4, "window code fields are 2 bits");
@@ -92,8 +92,9 @@ __device__ __forceinline__ bool f16_first_max(const uint32_t (&q)[KD][KH][NQ], P
         io[o] = pos(o, c4[o] >> 4, (c4[o] >> 2) & 3, c4[o] & 3);
         yo[o] = __builtin_bit_cast(uint16_t, mx[o]);
         // -0 and +0 compare equal, so c4 names the first zero; its sign comes
-        // from the element itself (an L1/L2 hit)
-        if (mx[o] == (_Float16)0 && active) yo[o] = xp[io[o]];
+        // from the element itself (an L1/L2 hit).  Only outputs that exist
+        // read it: a window past the row end can name a column past it.
+        if (mx[o] == (_Float16)0 && o < nvalid) yo[o] = xp[io[o]];
     }
     return true;
 }
@@ -334,14 +335,16 @@ fwd_fixed_kernel(const typename T::raw *__restrict__ x, typename T::raw *__restr
     R yo[V];
     int32_t io[V];
     bool done = false;
-    if constexpr (T::code == F16::code) done = f16_first_max<KD, KH, KW, SW, SPAN, V, NQ>(q, pos, xp, active, io, yo);
+    // outputs of this group that exist (none on an idle lane)
+    const int32_t nvalid = active ? OW - ow0 : 0;
+    if constexpr (T::code == F16::code) done = f16_first_max<KD, KH, KW, SW, SPAN, V, NQ>(q, pos, xp, nvalid, io, yo);
     if (!done) {
 #pragma unroll
         for (int o = 0; o < V; ++o) {
             int code;
             const float best = scan_window<T, KD, KH, KW, SW>(el, o, code);
             io[o] = pos(o, code / (KH * KW), (code / KW) % KH, code % KW);
-            if (T::exact_nan || best == best || !active)
+            if (T::exact_nan || best == best || o >= nvalid)
                 yo[o] = T::back(best);
             else
                 yo[o] = xp[io[o]];            // NaN: copy the element's own bits

@@ -256,6 +256,28 @@ def test_subnormal_gradients(orc, dtype):
     _gpu.check_backward(orc, g, idx.cpu(), shape, gx, exact=False, what="subnormal")
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32],
+                         ids=lambda d: DT_ID[d])
+def test_all_negative_last_row_and_slice(orc, dtype, monkeypatch):
+    """3x3x3 windows of stride 2 whose last windows end on the last row and
+    slice (H = 2*OH + 1, D = 2*OD + 1), output rows that end inside a
+    thread's group of four (OW = 6), and inputs that are all negative, with
+    zeros of both signs in the first planes, through the row-vector kernel
+    (small-tensor kernels off): outputs past the row end are never written
+    and every written one matches the oracle."""
+    monkeypatch.setenv("MP3D_SMALL", "0")
+    shape = (2, 3, 7, 9, 14)
+    code = _gpu.CODE[dtype]
+    g = torch.Generator().manual_seed(31)
+    x = -(torch.rand(shape, generator=g, dtype=torch.float64) + 0.25)
+    x[0, 0, :, :, ::5] = 0.0
+    x[0, 1, :, ::3, :] = -0.0
+    x = x.to(dtype)
+    y, idx = _gpu.gpu_forward(x, k=(3, 3, 3), s=(2, 2, 2))
+    yo, io = _gpu.oracle_forward(orc, x, k=(3, 3, 3), s=(2, 2, 2))
+    _gpu.assert_forward_match(y, idx, yo, io, "all negative %s" % dtype)
+
+
 def test_out_of_range_idx_ignored(orc):
     shape = (1, 2, 6, 6, 6)
     g = torch.Generator().manual_seed(3)
